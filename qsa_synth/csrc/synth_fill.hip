@@ -1,0 +1,181 @@
+// synth_fill.hip -- GPU side of the seeded input generator (inputs only).
+//
+// Implements the same counter-based SplitMix64 streams, Irwin-Hall normals,
+// bfloat16 / e4m3 encoders and per-token index-key quantisation as the numpy
+// generator in qsa_synth/__init__.py, so every byte written here can be
+// regenerated on the host. Compiled with -ffp-contract=off and explicit
+// round-to-nearest intrinsics so that float results match numpy's IEEE
+// float32 operations exactly.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__host__ __device__ inline uint64_t mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ inline uint64_t stream_out(uint64_t key, uint64_t c) { return mix64(key + (c + 1) * kGamma); }
+
+__device__ inline float normal_at(uint64_t key, uint64_t n)
+{
+    int64_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+        uint64_t o = stream_out(key, 3 * n + j);
+        acc += (int64_t)(o & 0xFFFF) + (int64_t)((o >> 16) & 0xFFFF) + (int64_t)((o >> 32) & 0xFFFF) +
+               (int64_t)(o >> 48);
+    }
+    return (float)(int)(acc - 393210) * (1.0f / 65536.0f);
+}
+
+__device__ inline uint16_t bf16_rne(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline uint8_t e4m3_rne_sat(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 31) << 7;
+    uint32_t a = u & 0x7FFFFFFFu;
+    float af = __uint_as_float(a);
+    int code;
+    if (af >= 448.0f) {
+        code = 0x7E;
+    } else if ((int)(a >> 23) - 127 >= -6) {
+        code = (int)((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120 << 3);
+        if (code > 0x7E)
+            code = 0x7E;
+    } else {
+        code = (int)rintf(af * 512.0f);
+    }
+    return (uint8_t)((uint32_t)code | sign);
+}
+
+// One thread per token: 64 normals (planted tokens: u + 0.1 * noise), then
+// per-token quantisation sigma = fp16(amax / 448), code = e4m3(x / sigma).
+__global__ void fill_index_kernel(uint8_t *__restrict__ keys, uint16_t *__restrict__ scales, int64_t L,
+                                  uint64_t b, uint64_t key_main, uint64_t key_noise,
+                                  const int32_t *__restrict__ planted, int n_planted,
+                                  const float *__restrict__ u, int block_tokens)
+{
+    int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= L)
+        return;
+    int32_t blk = (int32_t)(t / block_tokens);
+    bool hit = false;
+    int lo = 0, hi = n_planted;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (planted[mid] < blk)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    if (lo < n_planted && planted[lo] == blk)
+        hit = true;
+
+    uint64_t base = ((b << 28) + (uint64_t)t) * 64u;
+    float x[64];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; i++) {
+        float v;
+        if (hit)
+            v = __fadd_rn(u[i], __fmul_rn(0.1f, normal_at(key_noise, base + i)));
+        else
+            v = normal_at(key_main, base + i);
+        x[i] = v;
+        amax = fmaxf(amax, fabsf(v));
+    }
+    __half s16 = __float2half_rn(__fdiv_rn(amax, 448.0f));
+    float s32 = __half2float(s16);
+    uint8_t *dst = keys + t * 64;
+    uint32_t packed[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            uint32_t c = (s32 > 0.0f) ? e4m3_rne_sat(__fdiv_rn(x[4 * i + k], s32)) : 0u;
+            w |= c << (8 * k);
+        }
+        packed[i] = w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        reinterpret_cast<uint4 *>(dst)[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2],
+                                                       packed[4 * i + 3]);
+    scales[t] = __half_as_ushort(s16);
+}
+
+// bf16 normals for rows [slot0, slot0 + n_slots) of a KV pool; 8 values per thread.
+__global__ void fill_kv_kernel(uint16_t *__restrict__ rows, int64_t slot0, int64_t n_vals, int64_t row_elems,
+                               uint64_t key)
+{
+    int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
+    for (int64_t v = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; v < n_vals; v += stride) {
+        uint64_t n0 = (uint64_t)(slot0 * row_elems + v);
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            uint32_t lo = bf16_rne(normal_at(key, n0 + 2 * k));
+            uint32_t hi = bf16_rne(normal_at(key, n0 + 2 * k + 1));
+            w[k] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(rows + v) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+uint64_t stream_key(uint64_t seed, uint64_t tensor, uint64_t layer)
+{
+    return mix64((seed << 32) ^ (tensor << 16) ^ layer);
+}
+
+} // namespace
+
+extern "C" {
+
+// Index keys of tokens [0, L) of sequence b in one layer, written at keys[t*64]
+// and scales[t]. planted: sorted device int32 block list; u: device float[64].
+int synth_fill_index(uint8_t *keys, uint16_t *scales, int64_t L, int b, int layer, uint64_t seed,
+                     const int32_t *planted, int n_planted, const float *u, int block_tokens, void *stream)
+{
+    if (L <= 0)
+        return 0;
+    uint64_t km = stream_key(seed, 4, (uint64_t)layer);
+    uint64_t kn = stream_key(seed, 5, (uint64_t)layer);
+    dim3 grid((unsigned)((L + 255) / 256));
+    hipLaunchKernelGGL(fill_index_kernel, grid, dim3(256), 0, (hipStream_t)stream, keys, scales, L,
+                       (uint64_t)b, km, kn, planted, n_planted, u, block_tokens);
+    return (int)hipGetLastError();
+}
+
+// KV rows [slot0, slot0 + n_slots) of one layer's pool; dst points at row slot0.
+int synth_fill_kv(uint16_t *dst, int64_t slot0, int64_t n_slots, int64_t row_elems, int layer, uint64_t seed,
+                  void *stream)
+{
+    if (n_slots <= 0)
+        return 0;
+    if (row_elems % 8 != 0)
+        return 1;
+    uint64_t key = stream_key(seed, 6, (uint64_t)layer);
+    int64_t n_vals = n_slots * row_elems;
+    int64_t threads = (n_vals + 7) / 8;
+    int64_t blocks = (threads + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;
+    hipLaunchKernelGGL(fill_kv_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, dst, slot0,
+                       n_vals, row_elems, key);
+    return (int)hipGetLastError();
+}
+
+} // extern "C"
