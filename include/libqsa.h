@@ -1,0 +1,191 @@
+/*
+ * libqsa.h -- C ABI of libqsa, the QSA sparse-attention decode step for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (sources: the article "双卡RTX4090跑通Qwen3-Next：8并发满血长上下文实测",
+ * intro and memory-ledger section; the digest "Оффлоадинг KV-кэша
+ * Qwen3.8-Flash-Next в RAM через vLLM", lead paragraph and mechanism /
+ * efficiency sections): in every QSA layer of a decode step, each sequence
+ *   1. scores every cached token with a compact GPU-resident index key
+ *      (66 bytes per token per layer: 64 fp8 e4m3 codes + one fp16 scale),
+ *      s_t = sum_h w_h * ReLU(sigma_t * (q_idx_h . k_t));
+ *   2. reduces the scores to C4 blocks of 4 adjacent tokens (block score =
+ *      max over its valid tokens);
+ *   3. keeps at most indexer_budget tokens: the forced blocks (attention sink
+ *      at the start, tail ring at the end) plus the best remaining blocks by
+ *      (score desc, block index asc);
+ *   4. reads only those KV rows (2048 bytes per token per layer) through a
+ *      logical-token -> physical-slot page table, from HBM or from pinned host
+ *      memory over PCIe;
+ *   5. runs GQA softmax attention of the decode query over the gathered rows
+ *      (split over tokens, partial results merged by log-sum-exp).
+ *
+ * Conventions shared by every call
+ *   - All pointers are device pointers unless stated otherwise; "host-pinned"
+ *     pointers are host allocations made with hipHostMalloc (or torch
+ *     pin_memory), read by the GPU directly over PCIe.
+ *   - The caller owns every buffer, including the workspace. The library never
+ *     allocates, frees or synchronises inside these calls; work is enqueued on
+ *     the given stream(s) and runs asynchronously. NULL stream = the default
+ *     stream. Calls are thread-safe when their workspaces differ.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued. Values that live only on the device
+ *     (ctx_len, idx_row0, page-table entries, selections) are the caller's
+ *     contract: ctx_len is clamped to [0, max_ctx] by the kernels, page-table
+ *     entries must lie in [0, n_slots).
+ *   - Launch failures return QSA_ERR_HIP; faults surface at the next sync.
+ *
+ * Data layouts
+ *   - Index keys of one layer: idx_keys u8 [rows][idx_dim] (e4m3 codes, OCP
+ *     E4M3FN: bias 7, max 448, no infinities) and idx_scales u16 [rows] (IEEE
+ *     fp16 bits, sigma_t >= 0), in logical token order; sequence b occupies
+ *     rows [idx_row0[b], idx_row0[b] + ctx_len[b]). 66 bytes per token.
+ *   - KV pool of one layer: [n_slots][row_bytes], row_bytes = 2 * n_kv_heads *
+ *     head_dim * 2 = 2048; a row holds K of KV head 0..n_kv-1, then V of KV
+ *     head 0..n_kv-1, each head_dim bf16 values.
+ *   - Page table: i32 [batch][pt_stride]; entry [b][t] is the physical slot of
+ *     logical token t of sequence b.
+ *   - Block selections: i32 [batch][K], K = budget_tokens / block_tokens,
+ *     ascending block indices, padded with -1 after n_sel[b] entries.
+ *   - Staged rows: [batch][budget_tokens][row_bytes]; row p of sequence b is
+ *     the p-th selected token in ascending logical order.
+ *   - Queries: q_idx bf16 [batch][idx_heads][idx_dim], w_idx f32
+ *     [batch][idx_heads], q bf16 [batch][n_q_heads][head_dim]; outputs f32
+ *     [batch][n_q_heads][head_dim]. Query head h reads KV head
+ *     h / (n_q_heads / n_kv_heads).
+ *
+ * Compiled geometry: n_q_heads 16, n_kv_heads 2, head_dim 256, idx_heads 4,
+ * idx_dim 64, block_tokens 4. Other values give QSA_ERR_UNSUPPORTED.
+ */
+#ifndef LIBQSA_H
+#define LIBQSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *qsa_stream_t; /* a hipStream_t */
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment */
+    QSA_ERR_UNSUPPORTED = 2,        /* geometry other than the compiled one */
+    QSA_ERR_WORKSPACE_TOO_SMALL = 3,
+    QSA_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
+} qsa_status_t;
+
+typedef enum {
+    QSA_KV_DEVICE = 0,       /* KV pools in device memory (HBM) */
+    QSA_KV_HOST_PINNED = 1   /* KV pools in pinned host memory, read over PCIe */
+} qsa_kv_location_t;
+
+typedef struct {
+    int32_t n_q_heads;     /* 16 */
+    int32_t n_kv_heads;    /* 2 */
+    int32_t head_dim;      /* 256 */
+    int32_t idx_heads;     /* 4 indexer heads */
+    int32_t idx_dim;       /* 64 (index key = idx_dim e4m3 codes + a fp16 scale) */
+    int32_t block_tokens;  /* 4: C4 blocks */
+    int32_t budget_tokens; /* indexer_budget, a multiple of block_tokens, <= 8192 */
+    int32_t sink_blocks;   /* leading blocks always selected (>= 0) */
+    int32_t tail_tokens;   /* blocks holding the last tail_tokens tokens are always selected */
+    float sm_scale;        /* softmax scale, normally 1/sqrt(head_dim) */
+} qsa_config_t;
+
+typedef struct {
+    int32_t batch;             /* B >= 1 (host) */
+    int32_t max_ctx;           /* host-side upper bound of ctx_len[b], <= 2^21 */
+    const int32_t *ctx_len;    /* device [B] tokens cached per sequence (current one included) */
+    const int64_t *idx_row0;   /* device [B] first index row of each sequence */
+    const int32_t *page_table; /* device [B][pt_stride] logical token -> slot */
+    int64_t pt_stride;         /* >= max_ctx */
+    int64_t n_slots;           /* rows in each layer's KV pool */
+} qsa_batch_t;
+
+/* Step 1 + 2 (indexer scoring and C4 reduce).
+ *   idx_keys     u8  [rows][idx_dim], 16-byte aligned
+ *   idx_scales   u16 [rows] fp16 bits
+ *   q_idx        bf16 bits [B][idx_heads][idx_dim];  w_idx f32 [B][idx_heads]
+ *   token_scores f32 [rows] (same row index as the keys) or NULL
+ *   block_scores f32 [B][bs_stride], bs_stride >= ceil(max_ctx / block_tokens);
+ *                entries past ceil(ctx_len[b] / block_tokens) are not written. */
+qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, const uint8_t *idx_keys,
+                             const uint16_t *idx_scales, const uint16_t *q_idx, const float *w_idx,
+                             float *token_scores, float *block_scores, int64_t bs_stride, qsa_stream_t stream);
+
+/* Step 3 (budgeted block selection), on the given block scores.
+ *   sel_blocks i32 [B][K] ascending, -1 padded;  n_sel i32 [B];
+ *   n_tok      i32 [B] tokens covered by the selection, or NULL.
+ * Exact: the same selection as a full sort by (score desc, index asc); -0.0
+ * and +0.0 compare equal. Needs qsa_workspace_size(cfg, B, max_ctx, 1, QSA_KV_DEVICE)
+ * bytes of workspace (any content; 256-byte aligned). QSA_ERR_INVALID_ARGUMENT
+ * if the forced blocks could exceed the budget. */
+qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, const float *block_scores,
+                             int64_t bs_stride, int32_t *sel_blocks, int32_t *n_sel, int32_t *n_tok,
+                             void *workspace, size_t workspace_bytes, qsa_stream_t stream);
+
+/* Step 4 (page-table translate + row gather). Copies the rows of the selected
+ * tokens, in ascending logical order, from kv_pool ([n_slots][row_bytes];
+ * device memory, or host-pinned memory for QSA_KV_HOST_PINNED) to kv_out
+ * ([B][budget_tokens][row_bytes], device). Writes n_tok[b]. Bit-exact copy. */
+qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, const int32_t *sel_blocks,
+                           const int32_t *n_sel, const void *kv_pool, qsa_kv_location_t kv_location,
+                           void *kv_out, int32_t *n_tok, qsa_stream_t stream);
+
+/* Step 5 (split-K GQA decode attention + log-sum-exp merge) over staged rows.
+ *   q   bf16 bits [B][n_q_heads][head_dim];  kv [B][budget_tokens][row_bytes]
+ *   n_tok i32 [B] rows used per sequence (0 gives a zero output)
+ *   out f32 [B][n_q_heads][head_dim]
+ * Workspace: qsa_workspace_size(cfg, B, 0, 1, QSA_KV_DEVICE) bytes. */
+qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uint16_t *q, const void *kv,
+                               const int32_t *n_tok, float *out, void *workspace, size_t workspace_bytes,
+                               qsa_stream_t stream);
+
+/* One QSA layer's inputs and outputs for qsa_decode_step. */
+typedef struct {
+    const uint8_t *idx_keys;    /* [rows][idx_dim] */
+    const uint16_t *idx_scales; /* [rows] */
+    const uint16_t *q_idx;      /* [B][idx_heads][idx_dim] */
+    const float *w_idx;         /* [B][idx_heads] */
+    const uint16_t *q;          /* [B][n_q_heads][head_dim] */
+    const void *kv_pool;        /* [n_slots][row_bytes], device or host-pinned */
+    const int32_t *page_table;  /* this layer's table, or NULL for batch->page_table */
+    float *out;                 /* [B][n_q_heads][head_dim] */
+    int32_t *sel_blocks;        /* optional [B][K] copy of the selection, or NULL */
+    int32_t *n_sel;             /* optional [B], or NULL */
+    void *score_events[2];      /* optional pair of timing-enabled hipEvent_t, recorded on the
+                                   compute stream just before and just after this layer's
+                                   index-scoring kernel; NULL to skip */
+} qsa_layer_t;
+
+/* The whole decode step over n_layers independent QSA layers: for each layer,
+ * score -> select -> gather/attend -> merge. With KV in HBM the gather is
+ * fused into attention (rows are read through the page table in place). With
+ * QSA_KV_HOST_PINNED the selected rows are copied over PCIe into a
+ * double-buffered staging area on the copy stream while the compute stream
+ * scores the next layer; copy = NULL serialises everything on compute.
+ * Workspace: qsa_workspace_size(cfg, B, max_ctx, n_layers, kv_location). */
+qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
+                             int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
+                             size_t workspace_bytes, qsa_stream_t compute, qsa_stream_t copy);
+
+/* Workspace bytes needed by qsa_decode_step (n_layers >= 1); the same call
+ * with n_layers = 1 covers qsa_topk_blocks and qsa_sparse_decode. */
+size_t qsa_workspace_size(const qsa_config_t *cfg, int32_t batch, int32_t max_ctx, int32_t n_layers,
+                          qsa_kv_location_t kv_location);
+
+/* Algorithmic bytes of one layer for one sequence: idx_bytes = ctx * 66
+ * (index scan), kv_bytes = n_tok * row_bytes (gathered rows). */
+void qsa_layer_bytes(const qsa_config_t *cfg, int64_t ctx, int64_t n_tok, int64_t *idx_bytes, int64_t *kv_bytes);
+
+/* Static description of a status code. */
+const char *qsa_status_string(qsa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBQSA_H */

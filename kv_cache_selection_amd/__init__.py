@@ -1,0 +1,163 @@
+"""Python binding of libqsa (the QSA sparse-attention decode step on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libqsa.so``. Functions keep the C names (``qsa_index_score`` ...), take
+torch tensors (device memory, or pinned host memory for the KV pool of the
+offload path) or raw integer addresses, and raise ``QsaError`` on a status
+other than QSA_OK. Importing fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+try:  # load torch's HIP runtime first so that one runtime serves both
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover
+    torch = None
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE_TOO_SMALL, QSA_ERR_HIP = range(5)
+QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1
+
+# Every symbol include/libqsa.h declares.
+EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
+           "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
+
+
+class QsaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
+                ("budget_tokens", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
+                ("tail_tokens", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("ctx_len", ctypes.c_void_p),
+                ("idx_row0", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("pt_stride", ctypes.c_int64),
+                ("n_slots", ctypes.c_int64)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("idx_keys", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p), ("q_idx", ctypes.c_void_p),
+                ("w_idx", ctypes.c_void_p), ("q", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("out", ctypes.c_void_p), ("sel_blocks", ctypes.c_void_p),
+                ("n_sel", ctypes.c_void_p), ("score_events", ctypes.c_void_p * 2)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqsa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    CP, BP = ctypes.POINTER(Config), ctypes.POINTER(Batch)
+    lib.qsa_index_score.argtypes = [CP, BP, P, P, P, P, P, P, i64, P]
+    lib.qsa_topk_blocks.argtypes = [CP, BP, P, i64, P, P, P, P, sz, P]
+    lib.qsa_gather_kv.argtypes = [CP, BP, P, P, P, i32, P, P, P]
+    lib.qsa_sparse_decode.argtypes = [CP, i32, P, P, P, P, P, sz, P]
+    lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P, P]
+    for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step"):
+        getattr(lib, f).restype = i32
+    lib.qsa_workspace_size.argtypes = [CP, i32, i32, i32, i32]
+    lib.qsa_workspace_size.restype = sz
+    lib.qsa_layer_bytes.argtypes = [CP, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.qsa_layer_bytes.restype = None
+    lib.qsa_status_string.argtypes = [i32]
+    lib.qsa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _p(x):
+    """Address of a tensor (data_ptr), an int, or None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn, st):
+    if st != QSA_OK:
+        raise QsaError(fn, st)
+
+
+def status_string(st: int) -> str:
+    return lib.qsa_status_string(st).decode()
+
+
+def make_config(budget_tokens, sink_blocks=0, tail_tokens=0, sm_scale=1.0 / 16.0, n_q_heads=16, n_kv_heads=2,
+                head_dim=256, idx_heads=4, idx_dim=64, block_tokens=4) -> Config:
+    return Config(n_q_heads, n_kv_heads, head_dim, idx_heads, idx_dim, block_tokens, budget_tokens, sink_blocks,
+                  tail_tokens, sm_scale)
+
+
+def make_batch(batch, max_ctx, ctx_len, idx_row0=None, page_table=None, pt_stride=0, n_slots=0) -> Batch:
+    return Batch(batch, max_ctx, _p(ctx_len), _p(idx_row0), _p(page_table), pt_stride, n_slots)
+
+
+def qsa_workspace_size(cfg: Config, batch: int, max_ctx: int, n_layers: int = 1,
+                       kv_location: int = QSA_KV_DEVICE) -> int:
+    return lib.qsa_workspace_size(ctypes.byref(cfg), batch, max_ctx, n_layers, kv_location)
+
+
+def qsa_layer_bytes(cfg: Config, ctx: int, n_tok: int):
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    lib.qsa_layer_bytes(ctypes.byref(cfg), ctx, n_tok, ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def qsa_index_score(cfg, batch, idx_keys, idx_scales, q_idx, w_idx, token_scores, block_scores, bs_stride,
+                    stream=None):
+    _check("qsa_index_score", lib.qsa_index_score(ctypes.byref(cfg), ctypes.byref(batch), _p(idx_keys),
+                                                  _p(idx_scales), _p(q_idx), _p(w_idx), _p(token_scores),
+                                                  _p(block_scores), bs_stride, _stream(stream)))
+
+
+def qsa_topk_blocks(cfg, batch, block_scores, bs_stride, sel_blocks, n_sel, n_tok, workspace, workspace_bytes,
+                    stream=None):
+    _check("qsa_topk_blocks", lib.qsa_topk_blocks(ctypes.byref(cfg), ctypes.byref(batch), _p(block_scores),
+                                                  bs_stride, _p(sel_blocks), _p(n_sel), _p(n_tok), _p(workspace),
+                                                  workspace_bytes, _stream(stream)))
+
+
+def qsa_gather_kv(cfg, batch, sel_blocks, n_sel, kv_pool, kv_location, kv_out, n_tok, stream=None):
+    _check("qsa_gather_kv", lib.qsa_gather_kv(ctypes.byref(cfg), ctypes.byref(batch), _p(sel_blocks), _p(n_sel),
+                                              _p(kv_pool), kv_location, _p(kv_out), _p(n_tok), _stream(stream)))
+
+
+def qsa_sparse_decode(cfg, batch_size, q, kv, n_tok, out, workspace, workspace_bytes, stream=None):
+    _check("qsa_sparse_decode", lib.qsa_sparse_decode(ctypes.byref(cfg), batch_size, _p(q), _p(kv), _p(n_tok),
+                                                      _p(out), _p(workspace), workspace_bytes, _stream(stream)))
+
+
+def make_layer(idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, out, page_table=None, sel_blocks=None,
+               n_sel=None, score_events=None) -> Layer:
+    ev = (ctypes.c_void_p * 2)(*(score_events or (None, None)))
+    return Layer(_p(idx_keys), _p(idx_scales), _p(q_idx), _p(w_idx), _p(q), _p(kv_pool), _p(page_table), _p(out),
+                 _p(sel_blocks), _p(n_sel), ev)
+
+
+def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, copy=None):
+    arr = (Layer * len(layers))(*layers)
+    _check("qsa_decode_step", lib.qsa_decode_step(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
+                                                  kv_location, _p(workspace), workspace_bytes, _stream(compute),
+                                                  _stream(copy)))

@@ -1,0 +1,437 @@
+// api.hip -- the C ABI of libqsa: host-side validation, workspace carving and
+// the per-layer launch sequence of the decode step.
+#include <math.h>
+#include <mutex>
+#include <vector>
+
+#include "../../include/libqsa.h"
+#include "qsa_internal.h"
+
+using namespace qsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int n_split_of(int budget_tokens) { return (budget_tokens + kTPS - 1) / kTPS; }
+
+// Byte offsets of the workspace pieces. Histograms and counters of every
+// layer come first, contiguous, so one fill kernel clears them all.
+struct WsLayout {
+    int B = 0, K = 0, n_blk_max = 0, n_layers = 0, n_split = 0, budget = 0;
+    size_t hist = 0, ctr = 0, zero_bytes = 0;
+    size_t def = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0;
+    size_t per_hist = 0, per_ctr = 0, per_def = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
+           per_ntok = 0, per_po = 0, per_plse = 0, per_stage = 0;
+    size_t total = 0;
+};
+
+WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_layers, qsa_kv_location_t loc)
+{
+    WsLayout w;
+    w.B = batch;
+    w.K = cfg->budget_tokens / kBT;
+    w.budget = cfg->budget_tokens;
+    w.n_blk_max = (max_ctx + kBT - 1) / kBT;
+    w.n_layers = n_layers;
+    w.n_split = n_split_of(cfg->budget_tokens);
+    const size_t nb = (size_t)(w.n_blk_max > 0 ? w.n_blk_max : 1);
+    w.per_hist = align_up((size_t)batch * kHistBins * 4);
+    w.per_ctr = align_up((size_t)batch * kCounters * 4);
+    w.per_def = align_up((size_t)batch * w.K * 4);
+    w.per_cand = align_up((size_t)batch * nb * 8);
+    w.per_bs = align_up((size_t)batch * nb * 4);
+    w.per_sel = align_up((size_t)batch * w.K * 4);
+    w.per_nsel = align_up((size_t)batch * 4);
+    w.per_ntok = align_up((size_t)batch * 4);
+    w.per_po = align_up((size_t)batch * kHq * w.n_split * kDh * 4);
+    w.per_plse = align_up((size_t)batch * kHq * w.n_split * 4);
+    w.per_stage = (loc == QSA_KV_HOST_PINNED) ? align_up((size_t)batch * w.budget * kRowBytes) : 0;
+    size_t off = 0;
+    w.hist = off;
+    off += w.per_hist * n_layers;
+    w.ctr = off;
+    off += w.per_ctr * n_layers;
+    w.zero_bytes = off;
+    w.def = off;
+    off += w.per_def * n_layers;
+    w.cand = off;
+    off += w.per_cand * n_layers;
+    w.bs = off;
+    off += w.per_bs * n_layers;
+    w.sel = off;
+    off += w.per_sel * n_layers;
+    w.nsel = off;
+    off += w.per_nsel * n_layers;
+    w.ntok = off;
+    off += w.per_ntok * n_layers;
+    w.po = off;
+    off += w.per_po * n_layers;
+    w.plse = off;
+    off += w.per_plse * n_layers;
+    w.stage = off;
+    off += w.per_stage * 2;
+    w.total = off;
+    return w;
+}
+
+template <typename T> T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+SelectWs select_ws(void *ws, const WsLayout &w, int l)
+{
+    SelectWs s;
+    s.hist = at<uint32_t>(ws, w.hist + w.per_hist * l);
+    s.counters = at<uint32_t>(ws, w.ctr + w.per_ctr * l);
+    s.def_list = at<int32_t>(ws, w.def + w.per_def * l);
+    s.cand = at<uint64_t>(ws, w.cand + w.per_cand * l);
+    s.cand_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
+    return s;
+}
+
+AttnWs attn_ws(void *ws, const WsLayout &w, int l)
+{
+    AttnWs a;
+    a.part_o = at<float>(ws, w.po + w.per_po * l);
+    a.part_lse = at<float>(ws, w.plse + w.per_plse * l);
+    a.n_split = w.n_split;
+    return a;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+qsa_status_t check_config(const qsa_config_t *c)
+{
+    if (!c)
+        return QSA_ERR_INVALID_ARGUMENT;
+    if (c->n_q_heads != kHq || c->n_kv_heads != kHkv || c->head_dim != kDh || c->idx_heads != kIdxH ||
+        c->idx_dim != kIdxD || c->block_tokens != kBT)
+        return QSA_ERR_UNSUPPORTED;
+    if (c->budget_tokens <= 0 || c->budget_tokens % kBT != 0 || c->budget_tokens > kMaxBudget)
+        return QSA_ERR_INVALID_ARGUMENT;
+    if (c->sink_blocks < 0 || c->tail_tokens < 0 || !isfinite(c->sm_scale))
+        return QSA_ERR_INVALID_ARGUMENT;
+    // Forced blocks must fit in the budget for every context length.
+    const int64_t K = c->budget_tokens / kBT;
+    const int64_t tail_blocks = c->tail_tokens > 0 ? ((int64_t)c->tail_tokens + kBT - 1) / kBT + 1 : 0;
+    if ((int64_t)c->sink_blocks + tail_blocks > K)
+        return QSA_ERR_INVALID_ARGUMENT;
+    return QSA_OK;
+}
+
+qsa_status_t check_batch(const qsa_batch_t *b, bool need_index, bool need_pt)
+{
+    if (!b || b->batch < 1 || b->max_ctx < 0 || b->max_ctx > kMaxCtx || !b->ctx_len)
+        return QSA_ERR_INVALID_ARGUMENT;
+    if (need_index && !b->idx_row0)
+        return QSA_ERR_INVALID_ARGUMENT;
+    if (need_pt && (!b->page_table || b->pt_stride < b->max_ctx || b->n_slots < 1))
+        return QSA_ERR_INVALID_ARGUMENT;
+    return QSA_OK;
+}
+
+qsa_status_t hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
+
+// Address at which the GPU reads a KV pool, or nullptr when it cannot: a pool
+// in device memory is used as is; a pool in pinned host memory is translated
+// to its device mapping. Pageable or unknown memory is rejected here rather
+// than left to fault on the device.
+const void *pool_device_ptr(const void *p, qsa_kv_location_t loc)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (loc == QSA_KV_DEVICE)
+        return (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) ? p : nullptr;
+    if (a.type != hipMemoryTypeHost || !a.devicePointer)
+        return nullptr;
+    if (a.hostPointer)
+        return static_cast<const char *>(a.devicePointer) +
+               (static_cast<const char *>(p) - static_cast<const char *>(a.hostPointer));
+    return a.devicePointer;
+}
+
+// Events for the two-stream offload schedule, created once per device and
+// kept for the life of the process.
+struct EventPool {
+    std::mutex mu;
+    std::vector<std::vector<hipEvent_t>> per_dev;
+};
+
+EventPool &event_pool()
+{
+    static EventPool p;
+    return p;
+}
+
+qsa_status_t get_events(int n, std::vector<hipEvent_t> &out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return QSA_ERR_HIP;
+    EventPool &p = event_pool();
+    std::lock_guard<std::mutex> g(p.mu);
+    if ((int)p.per_dev.size() <= dev)
+        p.per_dev.resize(dev + 1);
+    std::vector<hipEvent_t> &v = p.per_dev[dev];
+    while ((int)v.size() < n) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            return QSA_ERR_HIP;
+        v.push_back(e);
+    }
+    out.assign(v.begin(), v.begin() + n);
+    return QSA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t qsa_workspace_size(const qsa_config_t *cfg, int32_t batch, int32_t max_ctx, int32_t n_layers,
+                          qsa_kv_location_t kv_location)
+{
+    if (check_config(cfg) != QSA_OK || batch < 1 || max_ctx < 0 || max_ctx > kMaxCtx || n_layers < 1)
+        return 0;
+    return make_layout(cfg, batch, max_ctx, n_layers, kv_location).total;
+}
+
+void qsa_layer_bytes(const qsa_config_t *cfg, int64_t ctx, int64_t n_tok, int64_t *idx_bytes, int64_t *kv_bytes)
+{
+    const int64_t idx_row = cfg ? (int64_t)cfg->idx_dim + 2 : 0;
+    const int64_t kv_row = cfg ? 2LL * cfg->n_kv_heads * cfg->head_dim * 2 : 0;
+    if (idx_bytes)
+        *idx_bytes = ctx * idx_row;
+    if (kv_bytes)
+        *kv_bytes = n_tok * kv_row;
+}
+
+const char *qsa_status_string(qsa_status_t s)
+{
+    switch (s) {
+    case QSA_OK:
+        return "ok";
+    case QSA_ERR_INVALID_ARGUMENT:
+        return "invalid argument";
+    case QSA_ERR_UNSUPPORTED:
+        return "unsupported geometry";
+    case QSA_ERR_WORKSPACE_TOO_SMALL:
+        return "workspace too small";
+    case QSA_ERR_HIP:
+        return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, const uint8_t *idx_keys,
+                             const uint16_t *idx_scales, const uint16_t *q_idx, const float *w_idx,
+                             float *token_scores, float *block_scores, int64_t bs_stride, qsa_stream_t stream)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if ((st = check_batch(batch, true, false)) != QSA_OK)
+        return st;
+    if (!idx_keys || !idx_scales || !q_idx || !w_idx || !block_scores || !aligned(idx_keys, 16) ||
+        !aligned(q_idx, 8) || bs_stride < (batch->max_ctx + kBT - 1) / kBT)
+        return QSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_index_score(idx_keys, idx_scales, q_idx, w_idx, batch->ctx_len, batch->idx_row0,
+                                         batch->batch, batch->max_ctx, token_scores, block_scores, bs_stride,
+                                         nullptr, 0, 0, 0, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, const float *block_scores,
+                             int64_t bs_stride, int32_t *sel_blocks, int32_t *n_sel, int32_t *n_tok,
+                             void *workspace, size_t workspace_bytes, qsa_stream_t stream)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if ((st = check_batch(batch, false, false)) != QSA_OK)
+        return st;
+    if (!block_scores || !sel_blocks || !n_sel || !workspace || !aligned(workspace, kAlign) ||
+        bs_stride < (batch->max_ctx + kBT - 1) / kBT)
+        return QSA_ERR_INVALID_ARGUMENT;
+    const WsLayout w = make_layout(cfg, batch->batch, batch->max_ctx, 1, QSA_KV_DEVICE);
+    if (workspace_bytes < w.total)
+        return QSA_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = (hipStream_t)stream;
+    const SelectWs sw = select_ws(workspace, w, 0);
+    hipError_t e = launch_zero_u32(at<uint32_t>(workspace, 0), (int64_t)(w.zero_bytes / 4), s);
+    if (e == hipSuccess)
+        e = launch_block_hist(block_scores, bs_stride, batch->ctx_len, batch->batch, batch->max_ctx, sw.hist, w.K,
+                              cfg->sink_blocks, cfg->tail_tokens, s);
+    if (e == hipSuccess)
+        e = launch_select(block_scores, bs_stride, batch->ctx_len, batch->batch, batch->max_ctx, sw, w.K,
+                          cfg->sink_blocks, cfg->tail_tokens, sel_blocks, n_sel, n_tok, s);
+    return hip_status(e);
+}
+
+qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, const int32_t *sel_blocks,
+                           const int32_t *n_sel, const void *kv_pool, qsa_kv_location_t kv_location, void *kv_out,
+                           int32_t *n_tok, qsa_stream_t stream)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if ((st = check_batch(batch, false, true)) != QSA_OK)
+        return st;
+    if (!sel_blocks || !n_sel || !kv_pool || !kv_out || !aligned(kv_pool, 16) || !aligned(kv_out, 16) ||
+        (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
+        return QSA_ERR_INVALID_ARGUMENT;
+    const void *pool = pool_device_ptr(kv_pool, kv_location);
+    if (!pool)
+        return QSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_gather(sel_blocks, n_sel, batch->ctx_len, batch->batch, batch->max_ctx,
+                                    batch->page_table, batch->pt_stride, pool, kv_out,
+                                    cfg->budget_tokens / kBT, cfg->budget_tokens, n_tok, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uint16_t *q, const void *kv,
+                               const int32_t *n_tok, float *out, void *workspace, size_t workspace_bytes,
+                               qsa_stream_t stream)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if (batch < 1 || !q || !kv || !n_tok || !out || !workspace || !aligned(kv, 16) ||
+        !aligned(workspace, kAlign))
+        return QSA_ERR_INVALID_ARGUMENT;
+    const WsLayout w = make_layout(cfg, batch, 0, 1, QSA_KV_DEVICE);
+    if (workspace_bytes < w.total)
+        return QSA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_attention_staged(q, kv, n_tok, batch, cfg->budget_tokens, cfg->sm_scale,
+                                              attn_ws(workspace, w, 0), out, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
+                             int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
+                             size_t workspace_bytes, qsa_stream_t compute, qsa_stream_t copy)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if ((st = check_batch(batch, true, true)) != QSA_OK)
+        return st;
+    if (!layers || n_layers < 1 || !workspace || !aligned(workspace, kAlign) ||
+        (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
+        return QSA_ERR_INVALID_ARGUMENT;
+    for (int l = 0; l < n_layers; l++) {
+        const qsa_layer_t &L = layers[l];
+        if (!L.idx_keys || !L.idx_scales || !L.q_idx || !L.w_idx || !L.q || !L.kv_pool || !L.out ||
+            !aligned(L.idx_keys, 16) || !aligned(L.q_idx, 8) || !aligned(L.kv_pool, 16))
+            return QSA_ERR_INVALID_ARGUMENT;
+    }
+    const WsLayout w = make_layout(cfg, batch->batch, batch->max_ctx, n_layers, kv_location);
+    if (workspace_bytes < w.total)
+        return QSA_ERR_WORKSPACE_TOO_SMALL;
+    std::vector<const void *> pools((size_t)n_layers);
+    for (int l = 0; l < n_layers; l++) {
+        pools[l] = pool_device_ptr(layers[l].kv_pool, kv_location);
+        if (!pools[l])
+            return QSA_ERR_INVALID_ARGUMENT;
+    }
+
+    hipStream_t sc = (hipStream_t)compute;
+    hipStream_t sx = (hipStream_t)copy;
+    const bool offload = kv_location == QSA_KV_HOST_PINNED;
+    const bool two_streams = offload && copy != nullptr && copy != compute;
+    std::vector<hipEvent_t> ev;
+    if (two_streams && (st = get_events(3 * n_layers, ev)) != QSA_OK)
+        return st;
+
+    const int B = batch->batch;
+    const int K = w.K;
+    const int64_t bs_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
+    hipError_t e = launch_zero_u32(at<uint32_t>(workspace, 0), (int64_t)(w.zero_bytes / 4), sc);
+
+    for (int l = 0; l < n_layers && e == hipSuccess; l++) {
+        const qsa_layer_t &Ly = layers[l];
+        const int32_t *pt = Ly.page_table ? Ly.page_table : batch->page_table;
+        float *bs = at<float>(workspace, w.bs + w.per_bs * l);
+        int32_t *sel = Ly.sel_blocks ? Ly.sel_blocks : at<int32_t>(workspace, w.sel + w.per_sel * l);
+        int32_t *nsel = Ly.n_sel ? Ly.n_sel : at<int32_t>(workspace, w.nsel + w.per_nsel * l);
+        int32_t *ntok = at<int32_t>(workspace, w.ntok + w.per_ntok * l);
+        const SelectWs sw = select_ws(workspace, w, l);
+        const AttnWs aw = attn_ws(workspace, w, l);
+
+        if (Ly.score_events[0])
+            e = hipEventRecord((hipEvent_t)Ly.score_events[0], sc);
+        if (e == hipSuccess)
+            e = launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
+                                   B, batch->max_ctx, nullptr, bs, bs_stride, sw.hist, K, cfg->sink_blocks,
+                                   cfg->tail_tokens, sc);
+        if (e == hipSuccess && Ly.score_events[1])
+            e = hipEventRecord((hipEvent_t)Ly.score_events[1], sc);
+        if (e == hipSuccess)
+            e = launch_select(bs, bs_stride, batch->ctx_len, B, batch->max_ctx, sw, K, cfg->sink_blocks,
+                              cfg->tail_tokens, sel, nsel, ntok, sc);
+        if (e != hipSuccess)
+            break;
+        if (!offload) {
+            e = launch_attention_paged(Ly.q, pools[l], pt, batch->pt_stride, sel, ntok, batch->ctx_len,
+                                       batch->max_ctx, B, K, cfg->budget_tokens, cfg->sm_scale, aw, Ly.out, sc);
+            continue;
+        }
+        void *stage = at<void>(workspace, w.stage + w.per_stage * (l & 1));
+        if (!two_streams) {
+            e = launch_gather(sel, nsel, batch->ctx_len, B, batch->max_ctx, pt, batch->pt_stride, pools[l], stage,
+                              K, cfg->budget_tokens, ntok, sc);
+            if (e == hipSuccess)
+                e = launch_attention_staged(Ly.q, stage, ntok, B, cfg->budget_tokens, cfg->sm_scale, aw, Ly.out,
+                                            sc);
+            continue;
+        }
+        // Two streams: the copy stream gathers layer l over PCIe once its
+        // selection exists and once attention(l-2) has released the buffer;
+        // the compute stream goes on scoring layer l+1 and attends layer l
+        // when its rows have landed.
+        hipEvent_t e_sel = ev[3 * l], e_gat = ev[3 * l + 1], e_att = ev[3 * l + 2];
+        e = hipEventRecord(e_sel, sc);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(sx, e_sel, 0);
+        if (e == hipSuccess && l >= 2)
+            e = hipStreamWaitEvent(sx, ev[3 * (l - 2) + 2], 0);
+        if (e == hipSuccess)
+            e = launch_gather(sel, nsel, batch->ctx_len, B, batch->max_ctx, pt, batch->pt_stride, pools[l], stage,
+                              K, cfg->budget_tokens, ntok, sx);
+        if (e == hipSuccess)
+            e = hipEventRecord(e_gat, sx);
+        if (e != hipSuccess)
+            break;
+        // Attention of the previous layer goes after this layer's scoring.
+        if (l >= 1) {
+            const qsa_layer_t &Lp = layers[l - 1];
+            void *pstage = at<void>(workspace, w.stage + w.per_stage * ((l - 1) & 1));
+            e = hipStreamWaitEvent(sc, ev[3 * (l - 1) + 1], 0);
+            if (e == hipSuccess)
+                e = launch_attention_staged(Lp.q, pstage, at<int32_t>(workspace, w.ntok + w.per_ntok * (l - 1)), B,
+                                            cfg->budget_tokens, cfg->sm_scale, attn_ws(workspace, w, l - 1), Lp.out,
+                                            sc);
+            if (e == hipSuccess)
+                e = hipEventRecord(ev[3 * (l - 1) + 2], sc);
+        }
+        (void)e_att;
+    }
+    if (e == hipSuccess && two_streams) {
+        const int l = n_layers - 1;
+        const qsa_layer_t &Lp = layers[l];
+        void *pstage = at<void>(workspace, w.stage + w.per_stage * (l & 1));
+        e = hipStreamWaitEvent(sc, ev[3 * l + 1], 0);
+        if (e == hipSuccess)
+            e = launch_attention_staged(Lp.q, pstage, at<int32_t>(workspace, w.ntok + w.per_ntok * l), B,
+                                        cfg->budget_tokens, cfg->sm_scale, attn_ws(workspace, w, l), Lp.out, sc);
+        if (e == hipSuccess)
+            e = hipEventRecord(ev[3 * l + 2], sc);
+        // The copy stream must not run ahead of this call's last attention
+        // into a later call that reuses the staging buffers.
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(sx, ev[3 * l + 2], 0);
+    }
+    return hip_status(e);
+}
+
+} // extern "C"

@@ -1,0 +1,87 @@
+// gather.hip -- page-table translate and row gather.
+//
+// For every selected token t (ascending), slot = page_table[b][t] and the
+// 2048-byte KV row kv_pool[slot] is copied to position p of the staging area
+// (article, memory-ledger section: logical token addresses are kept apart
+// from physical cache slots; digest, mechanism section: only the selected
+// rows are moved, over PCIe when the pool lives in pinned host memory).
+// One workgroup copies the rows of kBlocksPerWg selected C4 blocks; every
+// lane moves 16-byte pieces so a row is one contiguous 2 KB burst, which is
+// what both HBM and PCIe reads want.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kThreads = 256;
+constexpr int kBlocksPerWg = 4;                       // 16 rows, 32 KB per workgroup
+constexpr int kRowsPerWg = kBlocksPerWg * kBT;
+constexpr int kPieces = kRowBytes / 16;               // 128 x 16 B per row
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restrict__ sel,
+                                                          const int32_t *__restrict__ n_sel,
+                                                          const int32_t *__restrict__ ctx_len, int max_ctx,
+                                                          const int32_t *__restrict__ pt, int64_t pt_stride,
+                                                          const u32x4 *__restrict__ pool, u32x4 *__restrict__ out,
+                                                          int K, int budget_tokens, int32_t *__restrict__ n_tok)
+{
+    const int b = blockIdx.y;
+    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    int ns = n_sel[b];
+    ns = ns < 0 ? 0 : (ns > K ? K : ns);
+    const int i0 = blockIdx.x * kBlocksPerWg;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && n_tok) {
+        int nt = 0;
+        if (ns > 0) {
+            const int last = sel[(int64_t)b * K + ns - 1];
+            const int end = min(last * kBT + kBT, L);
+            nt = (ns - 1) * kBT + (end - last * kBT);
+        }
+        n_tok[b] = nt;
+    }
+    if (i0 >= ns)
+        return;
+
+    // 16 rows x 128 pieces = 2048 pieces, 8 per thread; gather all loads first.
+    u32x4 v[kRowsPerWg * kPieces / kThreads];
+    int64_t dst[kRowsPerWg * kPieces / kThreads];
+#pragma unroll
+    for (int k = 0; k < kRowsPerWg * kPieces / kThreads; k++) {
+        const int c = threadIdx.x + k * kThreads;
+        const int r = c / kPieces;            // row within the workgroup
+        const int piece = c % kPieces;
+        const int i = i0 + r / kBT;           // selection entry
+        dst[k] = -1;
+        if (i < ns) {
+            const int j = sel[(int64_t)b * K + i];
+            const int t = j * kBT + (r % kBT);
+            if (t < L) {
+                const int64_t slot = pt[(int64_t)b * pt_stride + t];
+                v[k] = __builtin_nontemporal_load(pool + slot * kPieces + piece);
+                const int p = i * kBT + (r % kBT);
+                dst[k] = ((int64_t)b * budget_tokens + p) * kPieces + piece;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWg * kPieces / kThreads; k++)
+        if (dst[k] >= 0)
+            out[dst[k]] = v[k];
+}
+
+} // namespace
+
+hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
+                         const int32_t *pt, int64_t pt_stride, const void *pool, void *out, int budget_blocks,
+                         int budget_tokens, int32_t *n_tok, hipStream_t s)
+{
+    dim3 grid((unsigned)((budget_blocks + kBlocksPerWg - 1) / kBlocksPerWg), (unsigned)batch);
+    hipLaunchKernelGGL(gather_kernel, grid, dim3(kThreads), 0, s, sel, n_sel, ctx_len, max_ctx, pt, pt_stride,
+                       static_cast<const u32x4 *>(pool), static_cast<u32x4 *>(out), budget_blocks, budget_tokens,
+                       n_tok);
+    return hipGetLastError();
+}
+
+} // namespace qsa

@@ -1,0 +1,263 @@
+// index_score.hip -- indexer scoring and C4 block reduce.
+//
+// For every cached token t of sequence b (digest page, mechanism section: the
+// GPU-resident index of 66-byte keys is scanned every decode step):
+//     s_t = sum_h w_h * ReLU(sigma_t * (q_h . k_t))
+// and for every C4 block j (article intro: 4 adjacent tokens form the unit
+// of selection) B_j = max of s_t over the block's valid tokens.
+//
+// Mapping on gfx950: one token per lane, 64 tokens per wave iteration. The
+// e4m3 codes are widened to bf16 in registers (exact: 4 significant bits fit
+// bf16's 8) and the 4-head x 64-dim dot products run on the matrix cores as
+// 16 accumulating v_mfma_f32_4x4x4_16b_bf16 (16 independent 4x4x4 blocks per
+// instruction: block = 4 lanes = 4 tokens, rows = the 4 indexer heads). The
+// products bf16 x bf16 are exact in fp32; accumulation is fp32. The VALU is
+// left with the decode, the ReLU/weight epilogue and the block max, so the
+// kernel stays bound by HBM, not by fp32 FMA throughput.
+//
+// When the sequence has more blocks than the budget, each workgroup also
+// builds an LDS histogram of the top 12 bits of its blocks' order keys
+// (forced blocks excluded) and adds it to the sequence's global histogram:
+// the first pass of the radix selection, fused here so that the selection
+// never re-reads the scores just to count them.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Four e4m3 codes (one dword, lowest byte first) -> four bf16 (exact).
+__device__ __forceinline__ s16x4 e4m3x4_to_bf16x4(uint32_t w)
+{
+    bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    s16x4 r;
+    r.x = __builtin_bit_cast(short, lo.x);
+    r.y = __builtin_bit_cast(short, lo.y);
+    r.z = __builtin_bit_cast(short, hi.x);
+    r.w = __builtin_bit_cast(short, hi.y);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t pick(const u32x4 &v, int i)
+{
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+constexpr int kThreads = 256;
+constexpr int kWaveTok = 64;                       // tokens per wave iteration
+constexpr int kWgTok = kThreads / 64 * kWaveTok;   // 256 tokens per workgroup iteration
+
+template <bool kTokens, bool kHist>
+__global__ __launch_bounds__(kThreads) void index_score_kernel(
+    const uint8_t *__restrict__ keys, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ q_idx,
+    const float *__restrict__ w_idx, const int32_t *__restrict__ ctx_len, const int64_t *__restrict__ row0,
+    int max_ctx, int chunk_tokens, float *__restrict__ token_scores, float *__restrict__ block_scores,
+    int64_t bs_stride, uint32_t *__restrict__ hist, int budget_blocks, int sink_blocks, int tail_tokens)
+{
+    __shared__ uint32_t lhist[kHist ? kHistBins : 1];
+
+    const int b = blockIdx.y;
+    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    const int t_begin = blockIdx.x * chunk_tokens;
+    if (t_begin >= L)
+        return;
+    const int n_blk = (L + kBT - 1) / kBT;
+    const bool do_hist = kHist && n_blk > budget_blocks;
+    const int tail_first = tail_first_block(L, tail_tokens, n_blk);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    if (do_hist) {
+        for (int i = tid; i < kHistBins; i += kThreads)
+            lhist[i] = 0;
+    }
+
+    // A operand: lane holds q[head = lane & 3][4m .. 4m+3] for m = 0..15.
+    s16x4 qa[16];
+    {
+        const uint2 *qrow = reinterpret_cast<const uint2 *>(q_idx + ((int64_t)b * kIdxH + (lane & 3)) * kIdxD);
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            uint2 v = qrow[m];
+            qa[m] = __builtin_bit_cast(s16x4, v);
+        }
+    }
+    float w[kIdxH];
+#pragma unroll
+    for (int h = 0; h < kIdxH; h++)
+        w[h] = w_idx[b * kIdxH + h];
+
+    const int64_t r0 = row0[b];
+    const u32x4 *kbase = reinterpret_cast<const u32x4 *>(keys + r0 * kIdxD);
+    const uint16_t *sbase = scales + r0;
+    float *bs_row = block_scores + (int64_t)b * bs_stride;
+
+    if (do_hist)
+        __syncthreads();
+
+    const int t_end = min(t_begin + chunk_tokens, L);
+    for (int tw = t_begin + wave * kWaveTok; tw < t_end; tw += kWgTok) {
+        const int t = tw + lane;
+        const bool valid = t < L;
+        u32x4 k[4];
+        uint16_t sc_bits = 0;
+        if (valid) {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                k[i] = __builtin_nontemporal_load(kbase + (int64_t)t * 4 + i);
+            sc_bits = sbase[t];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                k[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            s16x4 kb = e4m3x4_to_bf16x4(pick(k[m >> 2], m & 3));
+            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[m], kb, acc, 0, 0, 0);
+        }
+        // acc[h] = q_h . k_t for this lane's token.
+        const float sigma = (float)__builtin_bit_cast(_Float16, sc_bits);
+        float s = 0.0f;
+        s += w[0] * fmaxf(sigma * acc[0], 0.0f);
+        s += w[1] * fmaxf(sigma * acc[1], 0.0f);
+        s += w[2] * fmaxf(sigma * acc[2], 0.0f);
+        s += w[3] * fmaxf(sigma * acc[3], 0.0f);
+        if (!valid)
+            s = -INFINITY;
+        if (kTokens && valid)
+            token_scores[r0 + t] = s;
+
+        // C4 block = 4 consecutive lanes (t is a multiple of 64 at lane 0).
+        s = fmaxf(s, __shfl_xor(s, 1));
+        s = fmaxf(s, __shfl_xor(s, 2));
+        const int blk = t >> 2;
+        if ((lane & 3) == 0 && blk < n_blk) {
+            bs_row[blk] = s;
+            if (do_hist && blk >= sink_blocks && blk < tail_first)
+                atomicAdd(&lhist[order_key(s) >> kHistShift], 1u);
+        }
+    }
+
+    if (do_hist) {
+        __syncthreads();
+        uint32_t *gh = hist + (int64_t)b * kHistBins;
+        for (int i = tid; i < kHistBins; i += kThreads) {
+            uint32_t c = lhist[i];
+            if (c)
+                atomicAdd(gh + i, c);
+        }
+    }
+}
+
+// Histogram of existing block scores (standalone selection call).
+__global__ __launch_bounds__(kThreads) void block_hist_kernel(const float *__restrict__ block_scores,
+                                                              int64_t bs_stride, const int32_t *__restrict__ ctx_len,
+                                                              int max_ctx, int chunk_blocks, uint32_t *__restrict__ hist,
+                                                              int budget_blocks, int sink_blocks, int tail_tokens)
+{
+    __shared__ uint32_t lhist[kHistBins];
+    const int b = blockIdx.y;
+    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    const int n_blk = (L + kBT - 1) / kBT;
+    const int j0 = blockIdx.x * chunk_blocks;
+    if (n_blk <= budget_blocks || j0 >= n_blk)
+        return;
+    const int tail_first = tail_first_block(L, tail_tokens, n_blk);
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+        lhist[i] = 0;
+    __syncthreads();
+    const float *row = block_scores + (int64_t)b * bs_stride;
+    const int j1 = min(j0 + chunk_blocks, n_blk);
+    for (int j = j0 + threadIdx.x; j < j1; j += kThreads) {
+        if (j >= sink_blocks && j < tail_first)
+            atomicAdd(&lhist[order_key(row[j]) >> kHistShift], 1u);
+    }
+    __syncthreads();
+    uint32_t *gh = hist + (int64_t)b * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
+        uint32_t c = lhist[i];
+        if (c)
+            atomicAdd(gh + i, c);
+    }
+}
+
+__global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n)
+{
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = 0;
+}
+
+} // namespace
+
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 2048)
+        blocks = 2048;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
+                              const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int batch,
+                              int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
+                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s)
+{
+    if (max_ctx <= 0)
+        return hipSuccess;
+    // Tokens per workgroup: a multiple of 256, grown while the grid keeps
+    // at least 1024 workgroups (4 per CU) so every CU streams.
+    int chunk = kWgTok;
+    while (chunk < 4096 && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 1024)
+        chunk *= 2;
+    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)batch);
+    if (token_scores) {
+        if (hist)
+            hipLaunchKernelGGL((index_score_kernel<true, true>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
+                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               budget_blocks, sink_blocks, tail_tokens);
+        else
+            hipLaunchKernelGGL((index_score_kernel<true, false>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
+                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               budget_blocks, sink_blocks, tail_tokens);
+    } else {
+        if (hist)
+            hipLaunchKernelGGL((index_score_kernel<false, true>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
+                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               budget_blocks, sink_blocks, tail_tokens);
+        else
+            hipLaunchKernelGGL((index_score_kernel<false, false>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
+                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               budget_blocks, sink_blocks, tail_tokens);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
+                             int max_ctx, uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
+                             hipStream_t s)
+{
+    const int n_blk_max = (max_ctx + kBT - 1) / kBT;
+    if (n_blk_max <= 0)
+        return hipSuccess;
+    const int chunk = 4096;
+    dim3 grid((unsigned)((n_blk_max + chunk - 1) / chunk), (unsigned)batch);
+    hipLaunchKernelGGL(block_hist_kernel, grid, dim3(kThreads), 0, s, block_scores, bs_stride, ctx_len, max_ctx,
+                       chunk, hist, budget_blocks, sink_blocks, tail_tokens);
+    return hipGetLastError();
+}
+
+} // namespace qsa

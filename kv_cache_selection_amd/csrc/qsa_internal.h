@@ -1,0 +1,111 @@
+// qsa_internal.h -- shared constants, workspace layout and device helpers of
+// libqsa (internal; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Compiled geometry.
+constexpr int kHq = 16;          // query heads
+constexpr int kHkv = 2;          // KV heads
+constexpr int kGroup = kHq / kHkv;
+constexpr int kDh = 256;         // head dim
+constexpr int kIdxH = 4;         // indexer heads
+constexpr int kIdxD = 64;        // indexer dim (e4m3 codes per key)
+constexpr int kBT = 4;           // tokens per C4 block
+constexpr int kRowElems = 2 * kHkv * kDh;      // bf16 values per KV row
+constexpr int kRowBytes = 2 * kRowElems;       // 2048
+constexpr int kMaxBudget = 8192;               // tokens
+constexpr int kMaxCtx = 1 << 21;               // tokens per sequence
+
+// Selection: 12-bit histogram of the order key's top bits.
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
+constexpr int kCounters = 4;                   // per sequence: definite, candidate, ticket, pad
+
+// Attention: tokens per split.
+constexpr int kTPS = 64;
+
+// Monotone map of a float to uint32: a < b  <=>  key(a) < key(b); -0.0 maps
+// to the key of +0.0 so that the two compare equal, as floats do.
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) == 0)
+        u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int clamp_ctx(int32_t L, int max_ctx)
+{
+    return L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+}
+
+// Block j is forced when it is one of the first sink blocks or holds one of
+// the last tail tokens.
+__device__ __forceinline__ int tail_first_block(int L, int tail_tokens, int n_blk)
+{
+    if (tail_tokens <= 0)
+        return n_blk;
+    int first = L - tail_tokens;
+    return (first < 0 ? 0 : first) / kBT;
+}
+
+__device__ __forceinline__ int forced_count(int n_blk, int sink, int tail_first)
+{
+    int s = sink < n_blk ? sink : n_blk;
+    int t0 = tail_first > s ? tail_first : s;
+    return s + (n_blk > t0 ? n_blk - t0 : 0);
+}
+
+// Per-layer pieces of the caller's workspace, carved on the host.
+struct SelectWs {
+    uint32_t *hist;      // [B][kHistBins]
+    uint32_t *counters;  // [B][kCounters]
+    int32_t *def_list;   // [B][K]
+    uint64_t *cand;      // [B][cand_stride]
+    int64_t cand_stride;
+};
+
+struct AttnWs {
+    float *part_o;       // [B][kHq][n_split][kDh]
+    float *part_lse;     // [B][kHq][n_split]
+    int n_split;
+};
+
+// Kernel launchers (one translation unit each).
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
+
+hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
+                              const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int batch,
+                              int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
+                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
+                              hipStream_t s);
+
+hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
+                             int max_ctx, uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
+                             hipStream_t s);
+
+hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
+                         int max_ctx, const SelectWs &ws, int budget_blocks, int sink_blocks, int tail_tokens,
+                         int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s);
+
+hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
+                         const int32_t *pt, int64_t pt_stride, const void *pool, void *out, int budget_blocks,
+                         int budget_tokens, int32_t *n_tok, hipStream_t s);
+
+// Attention over staged rows (kv != nullptr) or through the page table.
+hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int32_t *n_tok, int batch,
+                                   int budget_tokens, float sm_scale, const AttnWs &ws, float *out,
+                                   hipStream_t s);
+
+hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int32_t *pt, int64_t pt_stride,
+                                  const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
+                                  int batch, int budget_blocks, int budget_tokens, float sm_scale,
+                                  const AttnWs &ws, float *out, hipStream_t s);
+
+} // namespace qsa

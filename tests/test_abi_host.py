@@ -1,0 +1,126 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol the header declares, and rejects bad arguments before enqueuing any
+work. Nothing here launches a kernel: every call returns during host-side
+validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libqsa.h")
+
+qsa = pytest.importorskip("kv_cache_selection_amd")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:qsa_status_t|size_t|void|const char \*)\s*\*?\s*(qsa_\w+)\s*\(",
+                                 txt, re.M)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = _declared()
+    for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
+              "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string"):
+        assert f in names
+    assert set(names) == set(qsa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(qsa.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert qsa.status_string(qsa.QSA_OK) == "ok"
+    assert "workspace" in qsa.status_string(qsa.QSA_ERR_WORKSPACE_TOO_SMALL)
+    assert qsa.status_string(99) == "unknown status"
+
+
+def test_layer_bytes_match_the_pages():
+    """66 B per index row and 2048 B per KV row; 2048 rows x 12 layers = 48 MiB."""
+    cfg = qsa.make_config(2048)
+    idx, kv = qsa.qsa_layer_bytes(cfg, 262144, 2048)
+    assert idx == 66 * 262144 and kv == 2048 * 2048
+    assert 12 * kv == 48 * 2**20
+
+
+def test_workspace_size_grows_with_layers_and_offload():
+    cfg = qsa.make_config(2048, sink_blocks=1)
+    one = qsa.qsa_workspace_size(cfg, 8, 262144, 1)
+    twelve = qsa.qsa_workspace_size(cfg, 8, 262144, 12)
+    off = qsa.qsa_workspace_size(cfg, 1, 1 << 20, 12, qsa.QSA_KV_HOST_PINNED)
+    assert one > 0 and twelve > 11 * one // 2 and off > 2 * 2048 * 2048
+    assert qsa.qsa_workspace_size(cfg, 0, 100, 1) == 0
+    assert qsa.qsa_workspace_size(cfg, 1, (1 << 21) + 1, 1) == 0
+    assert qsa.qsa_workspace_size(qsa.make_config(6), 1, 100, 1) == 0     # budget not a multiple of 4
+
+
+FAKE = 1 << 20      # a 256-byte aligned non-null address; never dereferenced on the host
+
+
+def _batch(**kw):
+    args = dict(batch=1, max_ctx=100, ctx_len=FAKE, idx_row0=FAKE, page_table=FAKE, pt_stride=100, n_slots=100)
+    args.update(kw)
+    return qsa.make_batch(**args)
+
+
+@pytest.mark.parametrize("cfg_kw,status", [
+    (dict(head_dim=128), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=32), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(idx_dim=128), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(block_tokens=8), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(budget_tokens=2050), qsa.QSA_ERR_INVALID_ARGUMENT),
+    (dict(budget_tokens=0), qsa.QSA_ERR_INVALID_ARGUMENT),
+    (dict(budget_tokens=16384), qsa.QSA_ERR_INVALID_ARGUMENT),
+    (dict(sink_blocks=-1), qsa.QSA_ERR_INVALID_ARGUMENT),
+    (dict(budget_tokens=64, tail_tokens=64), qsa.QSA_ERR_INVALID_ARGUMENT),   # 17 forced blocks > 16
+    (dict(budget_tokens=64, sink_blocks=17), qsa.QSA_ERR_INVALID_ARGUMENT),
+])
+def test_bad_config_rejected(cfg_kw, status):
+    kw = dict(budget_tokens=2048)
+    kw.update(cfg_kw)
+    cfg = qsa.make_config(**kw)
+    with pytest.raises(qsa.QsaError) as ei:
+        qsa.qsa_index_score(cfg, _batch(), FAKE, FAKE, FAKE, FAKE, None, FAKE, 25)
+    assert ei.value.status == status
+
+
+def test_bad_arguments_rejected_before_launch():
+    cfg = qsa.make_config(256)
+    E = qsa.QSA_ERR_INVALID_ARGUMENT
+    cases = [
+        lambda: qsa.qsa_index_score(cfg, _batch(), None, FAKE, FAKE, FAKE, None, FAKE, 25),
+        lambda: qsa.qsa_index_score(cfg, _batch(), FAKE + 4, FAKE, FAKE, FAKE, None, FAKE, 25),  # misaligned keys
+        lambda: qsa.qsa_index_score(cfg, _batch(), FAKE, FAKE, FAKE, FAKE, None, FAKE, 24),      # bs_stride short
+        lambda: qsa.qsa_index_score(cfg, _batch(batch=0), FAKE, FAKE, FAKE, FAKE, None, FAKE, 25),
+        lambda: qsa.qsa_index_score(cfg, _batch(max_ctx=(1 << 21) + 1), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20),
+        lambda: qsa.qsa_gather_kv(cfg, _batch(pt_stride=99), FAKE, FAKE, FAKE, 0, FAKE, FAKE),
+        lambda: qsa.qsa_gather_kv(cfg, _batch(), FAKE, FAKE, FAKE + 8, 0, FAKE, FAKE),           # misaligned pool
+        lambda: qsa.qsa_gather_kv(cfg, _batch(), FAKE, FAKE, FAKE, 7, FAKE, FAKE),               # bad location
+        lambda: qsa.qsa_sparse_decode(cfg, 1, FAKE, FAKE, FAKE, FAKE, FAKE + 64, 1 << 30),       # misaligned ws
+        lambda: qsa.qsa_sparse_decode(cfg, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30),
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [], 0, FAKE, 1 << 30),
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)],
+                                    0, FAKE, 1 << 30),                                           # no output
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(qsa.QsaError) as ei:
+            c()
+        assert ei.value.status == E, i
+
+
+def test_workspace_too_small_rejected():
+    cfg = qsa.make_config(256)
+    need = qsa.qsa_workspace_size(cfg, 1, 100, 1)
+    with pytest.raises(qsa.QsaError) as ei:
+        qsa.qsa_topk_blocks(cfg, _batch(), FAKE, 25, FAKE, FAKE, None, FAKE, need - 1)
+    assert ei.value.status == qsa.QSA_ERR_WORKSPACE_TOO_SMALL
+    lay = qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = qsa.qsa_workspace_size(cfg, 1, 100, 2)
+    with pytest.raises(qsa.QsaError) as ei:
+        qsa.qsa_decode_step(cfg, _batch(), [lay, lay], 0, FAKE, need - 256)
+    assert ei.value.status == qsa.QSA_ERR_WORKSPACE_TOO_SMALL

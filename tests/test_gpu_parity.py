@@ -1,0 +1,408 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+synthetic inputs, element by element, plus bit-exact invariances."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_synth as S
+from qsa_synth import fill
+from qsa_synth.device import DeviceInputs
+
+from qsa_testlib import (ATTN_ATOL, check_scores, check_selection, oracle_attention_on, oracle_unit,
+                          score_scale, unit_inputs)
+
+pytestmark = pytest.mark.gpu
+
+qsa = pytest.importorskip("kv_cache_selection_amd")
+G = S.GEOM
+
+
+def _cfg(wl):
+    return qsa.make_config(wl.budget, wl.sink_blocks, wl.tail_tokens, G.sm_scale)
+
+
+def _batch(di):
+    return qsa.make_batch(di.batch, di.max_ctx, di.ctx, di.row0, di.pt, di.pt_stride, di.n_slots)
+
+
+def _ws(cfg, B, max_ctx, layers=1, loc=0):
+    n = qsa.qsa_workspace_size(cfg, B, max_ctx, layers, loc)
+    assert n > 0
+    return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+
+
+def _u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------- inputs
+
+def test_fill_matches_host_generator(gpu):
+    wl = S.WORKLOADS["tiny-4k"]
+    di = DeviceInputs(wl, gpu)
+    hi = di.hi
+    keys, sig = S.host_index_layer(hi, 0)
+    assert np.array_equal(di.keys[0].cpu().numpy(), keys)
+    assert np.array_equal(_u16(di.scales[0]), sig)
+    slots = np.random.default_rng(0).choice(di.n_slots, 64, replace=False)
+    assert np.array_equal(_u16(di.pool[0][torch.from_numpy(slots).to(gpu)]), S.kv_rows(wl.seed, 0, slots))
+    wl2 = S.WORKLOADS["batch8-short"]
+    di2 = DeviceInputs(wl2, gpu, layers=6)
+    L, k2, s2 = unit_inputs(di2.hi, 5, 3)
+    r0 = int(di2.hi.lay.row0[3])
+    assert np.array_equal(di2.keys[5, r0:r0 + L].cpu().numpy(), k2)
+    assert np.array_equal(_u16(di2.scales[5, r0:r0 + L]), s2)
+
+
+# ---------------------------------------------------------- index scoring
+
+def _score(cfg, B, max_ctx, ctx, row0, keys, scales, q_idx, w, n_rows):
+    ts = torch.full((n_rows,), float("nan"), device="cuda")
+    bs_stride = (max_ctx + 3) // 4
+    bs = torch.full((B, bs_stride), float("nan"), device="cuda")
+    bt = qsa.make_batch(B, max_ctx, ctx, row0)
+    qsa.qsa_index_score(cfg, bt, keys, scales, q_idx, w, ts, bs, bs_stride)
+    torch.cuda.synchronize()
+    return ts.cpu().numpy(), bs.cpu().numpy()
+
+
+def test_e4m3_decode_all_codes_through_scoring(gpu):
+    """Token t carries code c_t in dim 0 and zeros elsewhere; with q = +-e_0,
+    w = e_0 and sigma = 1 the score is ReLU(+-decode(c_t)): every finite code,
+    compared with torch's e4m3fn decoder."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    L = len(codes)
+    keys = np.zeros((L, 64), np.uint8)
+    keys[:, 0] = codes
+    scales = np.full(L, np.float16(1.0)).view(np.uint16)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    for sign in (1.0, -1.0):
+        q_idx = np.zeros((1, 4, 64), np.uint16)
+        q_idx[0, 0, 0] = S.f32_to_bf16_bits(np.float32(sign))
+        w = np.array([[1, 0, 0, 0]], np.float32)
+        ts, _ = _score(qsa.make_config(256), 1, L, torch.tensor([L], dtype=torch.int32, device=gpu),
+                       torch.zeros(1, dtype=torch.int64, device=gpu), torch.from_numpy(keys).to(gpu),
+                       torch.from_numpy(scales.view(np.int16)).to(gpu),
+                       torch.from_numpy(q_idx.view(np.int16)).to(gpu), torch.from_numpy(w).to(gpu), L)
+        assert np.array_equal(ts, np.maximum(0.0, sign * ref).astype(np.float32))
+
+
+@pytest.mark.parametrize("name,layers", [("tiny-4k", 1), ("batch8-short", 2), ("single-38k", 1)])
+def test_index_score_parity(gpu, name, layers):
+    wl = S.WORKLOADS[name]
+    di = DeviceInputs(wl, gpu, layers=layers)
+    cfg = _cfg(wl)
+    for l in range(layers):
+        ts, bs = _score(cfg, di.batch, di.max_ctx, di.ctx, di.row0, di.keys[l], di.scales[l], di.q_idx[l],
+                        di.w_idx[l], di.n_rows)
+        for b in range(di.batch):
+            L, keys, sig = unit_inputs(di.hi, l, b)
+            r0 = int(di.hi.lay.row0[b])
+            ref_ts = oracle.token_scores(keys, sig, di.hi.q_idx[l, b], di.hi.w[l, b])
+            A = score_scale(keys, sig, di.hi.q_idx[l, b], di.hi.w[l, b])
+            check_scores(ts[r0:r0 + L], ref_ts, A, "token scores %s l%d b%d" % (name, l, b))
+            ref_bs = oracle.block_scores(ref_ts)
+            Ab = np.array([A[4 * j:4 * j + 4].max() for j in range(len(ref_bs))])
+            check_scores(bs[b, :len(ref_bs)], ref_bs, Ab, "block scores %s l%d b%d" % (name, l, b))
+            assert np.isnan(bs[b, len(ref_bs):]).all()       # nothing written past the sequence
+
+
+def test_index_score_ragged_and_tiny_lengths(gpu):
+    """Lengths that are not multiples of 4, 64 or the workgroup tile, and zero."""
+    rng = np.random.default_rng(3)
+    lens = np.array([1, 3, 4, 5, 63, 64, 65, 255, 257, 1000, 0, 4097], np.int64)
+    B = len(lens)
+    row0 = np.zeros(B, np.int64)
+    row0[1:] = np.cumsum(lens)[:-1]
+    n = int(lens.sum())
+    keys = rng.integers(0, 256, size=(n, 64)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0x30
+    scales = np.float16(rng.uniform(0.001, 0.02, size=n)).view(np.uint16)
+    q_idx = S.f32_to_bf16_bits(rng.standard_normal((B, 4, 64)).astype(np.float32))
+    w = rng.uniform(0, 1, (B, 4)).astype(np.float32)
+    ts, bs = _score(qsa.make_config(64), B, int(lens.max()),
+                    torch.from_numpy(lens.astype(np.int32)).to(gpu), torch.from_numpy(row0).to(gpu),
+                    torch.from_numpy(keys).to(gpu), torch.from_numpy(scales.view(np.int16)).to(gpu),
+                    torch.from_numpy(q_idx.view(np.int16)).to(gpu), torch.from_numpy(w).to(gpu), n)
+    for b in range(B):
+        L = int(lens[b])
+        r0 = int(row0[b])
+        k, s = keys[r0:r0 + L], scales[r0:r0 + L]
+        ref = oracle.token_scores(k, s, q_idx[b], w[b])
+        A = score_scale(k, s, q_idx[b], w[b])
+        check_scores(ts[r0:r0 + L], ref, A)
+        rb = oracle.block_scores(ref) if L else np.zeros(0, np.float32)
+        Ab = np.array([A[4 * j:4 * j + 4].max() for j in range(len(rb))])
+        check_scores(bs[b, :len(rb)], rb, Ab)
+
+
+def test_index_score_integer_exact(gpu):
+    """Integer keys/queries, power-of-two scales and weights: all partial sums
+    are exact, so the GPU must equal the oracle bit for bit."""
+    rng = np.random.default_rng(4)
+    L = 3000
+    ints = rng.integers(-4, 5, size=(L, 64)).astype(np.float32)
+    keys = S.f32_to_e4m3_codes(ints)
+    q = rng.integers(-3, 4, size=(1, 4, 64)).astype(np.float32)
+    q_idx = S.f32_to_bf16_bits(q)
+    scales = np.float16(2.0 ** rng.integers(-6, 2, size=L)).view(np.uint16)
+    w = np.array([[0.5, 1.0, 2.0, 0.25]], np.float32)
+    ts, bs = _score(qsa.make_config(64), 1, L, torch.tensor([L], dtype=torch.int32, device=gpu),
+                    torch.zeros(1, dtype=torch.int64, device=gpu), torch.from_numpy(keys).to(gpu),
+                    torch.from_numpy(scales.view(np.int16)).to(gpu), torch.from_numpy(q_idx.view(np.int16)).to(gpu),
+                    torch.from_numpy(w).to(gpu), L)
+    ref = oracle.token_scores(keys, scales, q_idx[0], w[0])
+    assert np.array_equal(ts, ref)
+    assert np.array_equal(bs[0], oracle.block_scores(ref))
+
+
+# --------------------------------------------------------------- selection
+
+def _topk(cfg, bs_rows, lens, K):
+    B = len(lens)
+    max_ctx = int(max(lens)) if len(lens) else 0
+    bs_stride = max(bs_rows.shape[1], 1)
+    ctx = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    bt = qsa.make_batch(B, max_ctx, ctx)
+    ws, nws = _ws(cfg, B, max_ctx)
+    ws.fill_(0xAB)                                  # arbitrary workspace content
+    sel = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+    ns = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    nt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    qsa.qsa_topk_blocks(cfg, bt, torch.from_numpy(np.ascontiguousarray(bs_rows, np.float32)).cuda(), bs_stride,
+                        sel, ns, nt, ws, nws)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), ns.cpu().numpy(), nt.cpu().numpy()
+
+
+def _check_topk_exact(bs_rows, lens, budget, sink=0, tail=0):
+    cfg = qsa.make_config(budget, sink, tail)
+    K = budget // 4
+    sel, ns, nt = _topk(cfg, bs_rows, lens, K)
+    for b, L in enumerate(lens):
+        n = (L + 3) // 4
+        fm = oracle.forced_mask(L, 4, sink, tail)
+        ref = oracle.select_blocks(bs_rows[b, :n], K, fm).blocks
+        assert ns[b] == len(ref), (b, ns[b], len(ref))
+        assert np.array_equal(sel[b, :ns[b]], ref), (b, L)
+        assert np.all(sel[b, ns[b]:] == -1)
+        toks = oracle.tokens_of_blocks(L, ref)
+        assert nt[b] == len(toks)
+
+
+def test_topk_exact_random_and_ties(gpu):
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        lens = rng.integers(1, 40000, size=5)
+        lens[0] = 4 * 512 + 3          # just over the budget, ragged
+        lens[1] = 2048                 # exactly the budget: everything fits
+        n_max = (lens.max() + 3) // 4
+        if trial % 2:
+            bs = rng.integers(0, 50, size=(5, n_max)).astype(np.float32)     # heavy ties
+        else:
+            bs = rng.standard_normal((5, n_max)).astype(np.float32) * 10
+        bs[:, ::7] = -0.0 if trial == 3 else bs[:, ::7]
+        _check_topk_exact(bs, lens, 2048, sink=trial % 3, tail=64 if trial >= 3 else 0)
+
+
+def test_topk_exact_degenerate_constant_scores(gpu):
+    """All scores equal: every block lands in one histogram bin, the candidate
+    list is the whole sequence (radix path), and ties break by index."""
+    lens = [280000, 9000, 4 * 512 + 1]
+    n_max = (max(lens) + 3) // 4
+    bs = np.full((3, n_max), 3.5, np.float32)
+    _check_topk_exact(bs, lens, 2048, sink=1)
+    bs2 = np.full((3, n_max), 3.5, np.float32)
+    bs2[:, 1::2] = np.nextafter(np.float32(3.5), np.float32(10))     # two adjacent values
+    _check_topk_exact(bs2, lens, 2048, tail=64)
+
+
+def test_topk_exact_small_budget_many_candidates(gpu):
+    rng = np.random.default_rng(6)
+    lens = [60000, 123457]
+    n_max = (max(lens) + 3) // 4
+    bs = np.round(rng.standard_normal((2, n_max)).astype(np.float32) * 4) / 4    # coarse values
+    for budget in (4, 64, 8192):
+        _check_topk_exact(bs, lens, budget)
+
+
+# ----------------------------------------------------------------- gather
+
+def test_gather_bit_exact_hbm_and_pinned(gpu):
+    wl = S.WORKLOADS["batch8-short"]
+    di = DeviceInputs(wl, gpu, layers=1)
+    cfg = _cfg(wl)
+    K = wl.budget // 4
+    sel = np.full((di.batch, K), -1, np.int32)
+    ns = np.zeros(di.batch, np.int32)
+    rng = np.random.default_rng(7)
+    toks_ref = []
+    for b in range(di.batch):
+        L = int(di.hi.lay.ctx[b])
+        n = (L + 3) // 4
+        k = int(rng.integers(1, min(K, n) + 1)) if b else min(K, n)
+        s = np.sort(rng.choice(n, k, replace=False)).astype(np.int32)
+        if b == 1 and (n - 1) not in s:
+            s[-1] = n - 1                                    # include the partial last block
+            s = np.unique(s)
+        sel[b, :len(s)] = s
+        ns[b] = len(s)
+        toks_ref.append(oracle.tokens_of_blocks(L, s))
+    out = torch.full((di.batch, wl.budget, G.row_elems), 0x5A5A, dtype=torch.int16, device=gpu)
+    nt = torch.zeros(di.batch, dtype=torch.int32, device=gpu)
+    sel_d, ns_d = torch.from_numpy(sel).to(gpu), torch.from_numpy(ns).to(gpu)
+    qsa.qsa_gather_kv(cfg, _batch(di), sel_d, ns_d, di.pool[0], qsa.QSA_KV_DEVICE, out, nt)
+    torch.cuda.synchronize()
+    got = _u16(out)
+    pool0 = _u16(di.pool[0])
+    for b in range(di.batch):
+        toks = toks_ref[b]
+        assert int(nt[b]) == len(toks)
+        ref = oracle.gather_rows(pool0, di.hi.lay.pt[b], toks)
+        assert np.array_equal(got[b, :len(toks)], ref)
+        assert np.all(got[b, len(toks):] == 0x5A5A)          # untouched past n_tok
+    # the same rows from pinned host memory over PCIe
+    host_pool = torch.empty_like(di.pool[0], device="cpu").pin_memory()
+    host_pool.copy_(di.pool[0])
+    out2 = torch.full_like(out, 0x5A5A)
+    qsa.qsa_gather_kv(cfg, _batch(di), sel_d, ns_d, host_pool, qsa.QSA_KV_HOST_PINNED, out2, nt)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+# --------------------------------------------------------------- attention
+
+def _decode(cfg, q, kv, nt):
+    B = q.shape[0]
+    ws, nws = _ws(cfg, B, 0)
+    out = torch.full((B, 16, 256), float("nan"), device="cuda")
+    qsa.qsa_sparse_decode(cfg, B, q, kv, nt, out, ws, nws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_sparse_decode_parity_and_closed_forms(gpu):
+    rng = np.random.default_rng(8)
+    budget = 2048
+    cfg = qsa.make_config(budget)
+    B = 5
+    ntok = np.array([2048, 1, 0, 1000, 65], np.int32)
+    kv = S.f32_to_bf16_bits(rng.standard_normal((B, budget, G.row_elems)).astype(np.float32))
+    q = S.f32_to_bf16_bits(rng.standard_normal((B, 16, 256)).astype(np.float32))
+    got = _decode(cfg, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(kv.view(np.int16)).cuda(),
+                  torch.from_numpy(ntok).cuda())
+    for b in range(B):
+        ref = oracle.attention(np.arange(ntok[b]), None, kv[b], q[b], 2, G.sm_scale)
+        assert np.abs(got[b] - ref).max() <= ATTN_ATOL, b
+    assert np.all(got[2] == 0)                                      # no tokens -> zeros
+    v1 = S.bf16_bits_to_f32(kv[1, 0, 512:]).reshape(2, 256)         # one token -> its V
+    assert np.array_equal(got[1], np.repeat(v1, 8, axis=0))
+    # constant V -> V exactly
+    kvc = kv.copy()
+    kvc[:, :, 512:] = S.f32_to_bf16_bits(np.float32(-0.75))
+    got = _decode(cfg, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(kvc.view(np.int16)).cuda(),
+                  torch.from_numpy(ntok).cuda())
+    assert np.all(got[ntok > 0] == -0.75)
+
+
+# ------------------------------------------------------------- whole step
+
+def _step(di, loc=None, two_streams=True):
+    wl = di.wl
+    cfg = _cfg(wl)
+    K = wl.budget // 4
+    L = di.n_layers
+    loc = (qsa.QSA_KV_HOST_PINNED if di.kv_host else qsa.QSA_KV_DEVICE) if loc is None else loc
+    sel = torch.full((L, di.batch, K), -7, dtype=torch.int32, device="cuda")
+    ns = torch.zeros((L, di.batch), dtype=torch.int32, device="cuda")
+    layers = [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l], di.out[l],
+                             None, sel[l], ns[l]) for l in range(L)]
+    ws, nws = _ws(cfg, di.batch, di.max_ctx, L, loc)
+    copy = torch.cuda.Stream() if (two_streams and loc == qsa.QSA_KV_HOST_PINNED) else None
+    qsa.qsa_decode_step(cfg, _batch(di), layers, loc, ws, nws, torch.cuda.current_stream(), copy)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), ns.cpu().numpy(), di.out.cpu().numpy()
+
+
+def _check_step_units(di, sel, ns, out, units):
+    excused = 0
+    for (l, b) in units:
+        u = oracle_unit(di.hi, l, b)
+        gsel = sel[l, b, :ns[l, b]]
+        excused += check_selection(gsel, u)
+        toks = u.tokens if np.array_equal(gsel, u.sel) else oracle.tokens_of_blocks(u.L, gsel)
+        ref = oracle_attention_on(di.hi, l, b, toks)
+        err = np.abs(out[l, b] - ref).max()
+        assert err <= ATTN_ATOL, ((l, b), err)
+    return excused
+
+
+@pytest.mark.parametrize("name,layers", [("tiny-4k", 1), ("batch8-short", 3), ("single-38k", 2)])
+def test_decode_step_parity(gpu, name, layers):
+    di = DeviceInputs(S.WORKLOADS[name], gpu, layers=layers)
+    sel, ns, out = _step(di)
+    units = [(l, b) for l in range(layers) for b in range(di.batch)]
+    _check_step_units(di, sel, ns, out, units)
+    # planted blocks are recovered (a sanity property of the synthetic data)
+    for (l, b) in units:
+        planted = di.hi.lay.planted[(l, b)]
+        assert set(planted.tolist()) <= set(sel[l, b, :ns[l, b]].tolist())
+
+
+def test_decode_step_deterministic_and_offload_bit_exact(gpu):
+    """Two runs give the same bits; the offload path (pool in pinned host
+    memory, gather over PCIe on a second stream) gives the same bits as the
+    HBM path, which reads the rows in place through the page table."""
+    wl = S.WORKLOADS["batch8-short"]
+    di = DeviceInputs(wl, gpu, layers=3)
+    sel1, ns1, out1 = _step(di)
+    sel2, ns2, out2 = _step(di)
+    assert np.array_equal(out1, out2) and np.array_equal(sel1, sel2)
+    dh = DeviceInputs(wl, gpu, layers=3, kv_host=True, hi=di.hi)
+    for two in (True, False):
+        sel3, ns3, out3 = _step(dh, two_streams=two)
+        assert np.array_equal(sel1, sel3)
+        assert np.array_equal(out1, out3)
+
+
+def test_decode_step_page_table_permutation_invariant(gpu):
+    """Moving every row to another slot and rewriting the page table the same
+    way leaves the output bit for bit unchanged."""
+    wl = S.WORKLOADS["tiny-4k"]
+    di = DeviceInputs(wl, gpu)
+    _, _, out1 = _step(di)
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(di.n_slots)).to(gpu)
+    pool2 = torch.empty_like(di.pool)
+    pool2[:, perm] = di.pool
+    di.pool = pool2
+    di.pt = torch.where(di.pt >= 0, perm[di.pt.clamp(min=0).long()].int(), di.pt)
+    _, _, out2 = _step(di)
+    assert np.array_equal(out1, out2)
+
+
+def test_decode_step_budget_covers_context_is_dense(gpu):
+    """With the budget above the context every block is selected and the step
+    is dense softmax attention over all tokens."""
+    wl = S.Workload("dense", 2, (1501, 2048), 1, 2048, seed=11)
+    di = DeviceInputs(wl, gpu)
+    sel, ns, out = _step(di)
+    for b in range(2):
+        L = int(di.hi.lay.ctx[b])
+        assert ns[0, b] == (L + 3) // 4
+        ref = oracle_attention_on(di.hi, 0, b, np.arange(L))
+        assert np.abs(out[0, b] - ref).max() <= ATTN_ATOL
+
+
+@pytest.mark.slow
+def test_decode_step_batch8_256k_sampled(gpu):
+    """The full 8 x 262,144 x 12-layer workload in the benchmark's launch
+    configuration; oracle parity on sampled (layer, sequence) units."""
+    di = DeviceInputs(S.WORKLOADS["batch8-256k"], gpu)
+    sel, ns, out = _step(di)
+    assert np.all(ns == 512)
+    _check_step_units(di, sel, ns, out, [(0, 0), (5, 3), (11, 7)])
+    for l in range(12):
+        for b in range(8):
+            assert sel[l, b, 0] == 0                           # the sink block
+            assert set(di.hi.lay.planted[(l, b)].tolist()) <= set(sel[l, b].tolist())
