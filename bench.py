@@ -132,7 +132,7 @@ def main():
 
     loc = qsa.QSA_KV_HOST_PINNED if di.kv_host else qsa.QSA_KV_DEVICE
     cfg = qsa.make_config(wl.budget, wl.sink_blocks, wl.tail_tokens, g.sm_scale)
-    bt = qsa.make_batch(di.batch, di.max_ctx, di.ctx, di.row0, di.pt, di.pt_stride, di.n_slots)
+    bt = qsa.make_batch(di.batch, di.max_ctx, di.ctx, di.row0, di.pt, di.pt_stride, di.n_slots, di.n_rows)
     K = wl.budget // g.block_tokens
     NL = di.n_layers
     sel = torch.zeros((NL, di.batch, K), dtype=torch.int32, device=dev)
@@ -140,7 +140,7 @@ def main():
     nws = qsa.qsa_workspace_size(cfg, di.batch, di.max_ctx, NL, loc)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    copy = torch.cuda.Stream() if loc == qsa.QSA_KV_HOST_PINNED else None
+    copy = torch.cuda.Stream()     # select/attention (HBM) or the PCIe gather (host pools) overlap the scoring
 
     def layers(events=None):
         return [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l], di.out[l],

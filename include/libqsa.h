@@ -31,8 +31,10 @@
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error nothing is enqueued. Values that live only on the device
  *     (ctx_len, idx_row0, page-table entries, selections) are the caller's
- *     contract: ctx_len is clamped to [0, max_ctx] by the kernels, page-table
- *     entries must lie in [0, n_slots).
+ *     contract. The kernels never read outside the buffers described here:
+ *     ctx_len is clamped to [0, max_ctx]; a sequence whose index rows fall
+ *     outside [0, n_idx_rows) is treated as empty; a page-table entry outside
+ *     [0, n_slots) is read as slot 0 (the result is then unspecified).
  *   - Launch failures return QSA_ERR_HIP; faults surface at the next sync.
  *
  * Data layouts
@@ -104,6 +106,8 @@ typedef struct {
     const int32_t *page_table; /* device [B][pt_stride] logical token -> slot */
     int64_t pt_stride;         /* >= max_ctx */
     int64_t n_slots;           /* rows in each layer's KV pool */
+    int64_t n_idx_rows;        /* rows in each layer's index buffers; a sequence whose rows
+                                  [idx_row0, idx_row0 + ctx_len) fall outside is scored as empty */
 } qsa_batch_t;
 
 /* Step 1 + 2 (indexer scoring and C4 reduce).
@@ -166,8 +170,17 @@ typedef struct {
  * score -> select -> gather/attend -> merge. With KV in HBM the gather is
  * fused into attention (rows are read through the page table in place). With
  * QSA_KV_HOST_PINNED the selected rows are copied over PCIe into a
- * double-buffered staging area on the copy stream while the compute stream
- * scores the next layer; copy = NULL serialises everything on compute.
+ * double-buffered staging area.
+ * Streams: with a second stream (`copy`, distinct from `compute`) layers
+ * overlap -- HBM pools: the compute stream scores layer after layer while
+ * `copy` selects and attends layer l under the scoring of layer l+1; host
+ * pools: `copy` gathers layer l over PCIe while `compute` scores layer l+1.
+ * The call leaves `compute` ordered after all of its work, so a sync on
+ * `compute` covers the step. copy = NULL (or == compute) serialises every
+ * kernel on `compute`; results are bit-identical either way. The two-stream
+ * schedule records events owned by the library (one set per device): do not
+ * run two-stream decode steps concurrently from several host threads on one
+ * device.
  * Workspace: qsa_workspace_size(cfg, B, max_ctx, n_layers, kv_location). */
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,

@@ -43,7 +43,7 @@ class Config(ctypes.Structure):
 class Batch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("ctx_len", ctypes.c_void_p),
                 ("idx_row0", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("pt_stride", ctypes.c_int64),
-                ("n_slots", ctypes.c_int64)]
+                ("n_slots", ctypes.c_int64), ("n_idx_rows", ctypes.c_int64)]
 
 
 class Layer(ctypes.Structure):
@@ -110,8 +110,16 @@ def make_config(budget_tokens, sink_blocks=0, tail_tokens=0, sm_scale=1.0 / 16.0
                   tail_tokens, sm_scale)
 
 
-def make_batch(batch, max_ctx, ctx_len, idx_row0=None, page_table=None, pt_stride=0, n_slots=0) -> Batch:
-    return Batch(batch, max_ctx, _p(ctx_len), _p(idx_row0), _p(page_table), pt_stride, n_slots)
+def make_batch(batch, max_ctx, ctx_len, idx_row0=None, page_table=None, pt_stride=0, n_slots=0,
+               n_idx_rows=None) -> Batch:
+    """The structs hold raw addresses only, so every tensor passed here is
+    also kept referenced by the returned struct: it cannot be freed (and its
+    memory reused) while the struct is alive."""
+    if idx_row0 is not None and n_idx_rows is None:
+        raise ValueError("n_idx_rows is required with idx_row0")
+    b = Batch(batch, max_ctx, _p(ctx_len), _p(idx_row0), _p(page_table), pt_stride, n_slots, n_idx_rows or 0)
+    b._keep = (ctx_len, idx_row0, page_table)
+    return b
 
 
 def qsa_workspace_size(cfg: Config, batch: int, max_ctx: int, n_layers: int = 1,
@@ -152,11 +160,14 @@ def qsa_sparse_decode(cfg, batch_size, q, kv, n_tok, out, workspace, workspace_b
 def make_layer(idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, out, page_table=None, sel_blocks=None,
                n_sel=None, score_events=None) -> Layer:
     ev = (ctypes.c_void_p * 2)(*(score_events or (None, None)))
-    return Layer(_p(idx_keys), _p(idx_scales), _p(q_idx), _p(w_idx), _p(q), _p(kv_pool), _p(page_table), _p(out),
-                 _p(sel_blocks), _p(n_sel), ev)
+    lay = Layer(_p(idx_keys), _p(idx_scales), _p(q_idx), _p(w_idx), _p(q), _p(kv_pool), _p(page_table), _p(out),
+                _p(sel_blocks), _p(n_sel), ev)
+    lay._keep = (idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, page_table, out, sel_blocks, n_sel)
+    return lay
 
 
 def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, copy=None):
+    # the array copies the structs; `layers` keeps the tensors they point to alive
     arr = (Layer * len(layers))(*layers)
     _check("qsa_decode_step", lib.qsa_decode_step(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
                                                   kv_location, _p(workspace), workspace_bytes, _stream(compute),

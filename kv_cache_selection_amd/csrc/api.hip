@@ -17,13 +17,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int n_split_of(int budget_tokens) { return (budget_tokens + kTPS - 1) / kTPS; }
 
-// Byte offsets of the workspace pieces. Histograms and counters of every
-// layer come first, contiguous, so one fill kernel clears them all.
+// Byte offsets of the workspace pieces. The histograms of every layer come
+// first, contiguous, so one fill kernel clears them all.
 struct WsLayout {
     int B = 0, K = 0, n_blk_max = 0, n_layers = 0, n_split = 0, budget = 0;
-    size_t hist = 0, ctr = 0, zero_bytes = 0;
-    size_t def = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0;
-    size_t per_hist = 0, per_ctr = 0, per_def = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
+    size_t hist = 0, zero_bytes = 0;
+    size_t cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0;
+    size_t per_hist = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
            per_ntok = 0, per_po = 0, per_plse = 0, per_stage = 0;
     size_t total = 0;
 };
@@ -39,8 +39,6 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.n_split = n_split_of(cfg->budget_tokens);
     const size_t nb = (size_t)(w.n_blk_max > 0 ? w.n_blk_max : 1);
     w.per_hist = align_up((size_t)batch * kHistBins * 4);
-    w.per_ctr = align_up((size_t)batch * kCounters * 4);
-    w.per_def = align_up((size_t)batch * w.K * 4);
     w.per_cand = align_up((size_t)batch * nb * 8);
     w.per_bs = align_up((size_t)batch * nb * 4);
     w.per_sel = align_up((size_t)batch * w.K * 4);
@@ -52,11 +50,7 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     size_t off = 0;
     w.hist = off;
     off += w.per_hist * n_layers;
-    w.ctr = off;
-    off += w.per_ctr * n_layers;
     w.zero_bytes = off;
-    w.def = off;
-    off += w.per_def * n_layers;
     w.cand = off;
     off += w.per_cand * n_layers;
     w.bs = off;
@@ -83,8 +77,6 @@ SelectWs select_ws(void *ws, const WsLayout &w, int l)
 {
     SelectWs s;
     s.hist = at<uint32_t>(ws, w.hist + w.per_hist * l);
-    s.counters = at<uint32_t>(ws, w.ctr + w.per_ctr * l);
-    s.def_list = at<int32_t>(ws, w.def + w.per_def * l);
     s.cand = at<uint64_t>(ws, w.cand + w.per_cand * l);
     s.cand_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
     return s;
@@ -124,7 +116,7 @@ qsa_status_t check_batch(const qsa_batch_t *b, bool need_index, bool need_pt)
 {
     if (!b || b->batch < 1 || b->max_ctx < 0 || b->max_ctx > kMaxCtx || !b->ctx_len)
         return QSA_ERR_INVALID_ARGUMENT;
-    if (need_index && !b->idx_row0)
+    if (need_index && (!b->idx_row0 || b->n_idx_rows < 0))
         return QSA_ERR_INVALID_ARGUMENT;
     if (need_pt && (!b->page_table || b->pt_stride < b->max_ctx || b->n_slots < 1))
         return QSA_ERR_INVALID_ARGUMENT;
@@ -239,7 +231,7 @@ qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         !aligned(q_idx, 8) || bs_stride < (batch->max_ctx + kBT - 1) / kBT)
         return QSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_index_score(idx_keys, idx_scales, q_idx, w_idx, batch->ctx_len, batch->idx_row0,
-                                         batch->batch, batch->max_ctx, token_scores, block_scores, bs_stride,
+                                         batch->n_idx_rows, batch->batch, batch->max_ctx, token_scores, block_scores, bs_stride,
                                          nullptr, 0, 0, 0, (hipStream_t)stream));
 }
 
@@ -286,7 +278,7 @@ qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, co
     if (!pool)
         return QSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_gather(sel_blocks, n_sel, batch->ctx_len, batch->batch, batch->max_ctx,
-                                    batch->page_table, batch->pt_stride, pool, kv_out,
+                                    batch->page_table, batch->pt_stride, batch->n_slots, pool, kv_out,
                                     cfg->budget_tokens / kBT, cfg->budget_tokens, n_tok, (hipStream_t)stream));
 }
 
@@ -338,92 +330,141 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     hipStream_t sc = (hipStream_t)compute;
     hipStream_t sx = (hipStream_t)copy;
     const bool offload = kv_location == QSA_KV_HOST_PINNED;
-    const bool two_streams = offload && copy != nullptr && copy != compute;
+    const bool two_streams = copy != nullptr && copy != compute;
     std::vector<hipEvent_t> ev;
-    if (two_streams && (st = get_events(3 * n_layers, ev)) != QSA_OK)
+    if (two_streams && (st = get_events(3 * n_layers + 1, ev)) != QSA_OK)
         return st;
 
     const int B = batch->batch;
     const int K = w.K;
     const int64_t bs_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
+
+    // Per-layer pieces.
+    struct Lw {
+        const int32_t *pt;
+        float *bs;
+        int32_t *sel, *nsel, *ntok;
+        SelectWs sw;
+        AttnWs aw;
+        void *stage;
+    };
+    std::vector<Lw> lw((size_t)n_layers);
+    for (int l = 0; l < n_layers; l++) {
+        const qsa_layer_t &Ly = layers[l];
+        Lw &x = lw[l];
+        x.pt = Ly.page_table ? Ly.page_table : batch->page_table;
+        x.bs = at<float>(workspace, w.bs + w.per_bs * l);
+        x.sel = Ly.sel_blocks ? Ly.sel_blocks : at<int32_t>(workspace, w.sel + w.per_sel * l);
+        x.nsel = Ly.n_sel ? Ly.n_sel : at<int32_t>(workspace, w.nsel + w.per_nsel * l);
+        x.ntok = at<int32_t>(workspace, w.ntok + w.per_ntok * l);
+        x.sw = select_ws(workspace, w, l);
+        x.aw = attn_ws(workspace, w, l);
+        x.stage = offload ? at<void>(workspace, w.stage + w.per_stage * (l & 1)) : nullptr;
+    }
+    auto score = [&](int l, hipStream_t s) {
+        const qsa_layer_t &Ly = layers[l];
+        hipError_t r = hipSuccess;
+        if (Ly.score_events[0])
+            r = hipEventRecord((hipEvent_t)Ly.score_events[0], s);
+        if (r == hipSuccess)
+            r = launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
+                                   batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.hist,
+                                   K, cfg->sink_blocks, cfg->tail_tokens, s);
+        if (r == hipSuccess && Ly.score_events[1])
+            r = hipEventRecord((hipEvent_t)Ly.score_events[1], s);
+        return r;
+    };
+    auto select = [&](int l, hipStream_t s) {
+        return launch_select(lw[l].bs, bs_stride, batch->ctx_len, B, batch->max_ctx, lw[l].sw, K, cfg->sink_blocks,
+                             cfg->tail_tokens, lw[l].sel, lw[l].nsel, lw[l].ntok, s);
+    };
+    auto attend_paged = [&](int l, hipStream_t s) {
+        return launch_attention_paged(layers[l].q, pools[l], lw[l].pt, batch->pt_stride, batch->n_slots, lw[l].sel,
+                                      lw[l].ntok, batch->ctx_len, batch->max_ctx, B, K, cfg->budget_tokens,
+                                      cfg->sm_scale, lw[l].aw, layers[l].out, s);
+    };
+    auto gather = [&](int l, hipStream_t s) {
+        return launch_gather(lw[l].sel, lw[l].nsel, batch->ctx_len, B, batch->max_ctx, lw[l].pt, batch->pt_stride,
+                             batch->n_slots, pools[l], lw[l].stage, K, cfg->budget_tokens, lw[l].ntok, s);
+    };
+    auto attend_staged = [&](int l, hipStream_t s) {
+        return launch_attention_staged(layers[l].q, lw[l].stage, lw[l].ntok, B, cfg->budget_tokens, cfg->sm_scale,
+                                       lw[l].aw, layers[l].out, s);
+    };
+
     hipError_t e = launch_zero_u32(at<uint32_t>(workspace, 0), (int64_t)(w.zero_bytes / 4), sc);
 
-    for (int l = 0; l < n_layers && e == hipSuccess; l++) {
-        const qsa_layer_t &Ly = layers[l];
-        const int32_t *pt = Ly.page_table ? Ly.page_table : batch->page_table;
-        float *bs = at<float>(workspace, w.bs + w.per_bs * l);
-        int32_t *sel = Ly.sel_blocks ? Ly.sel_blocks : at<int32_t>(workspace, w.sel + w.per_sel * l);
-        int32_t *nsel = Ly.n_sel ? Ly.n_sel : at<int32_t>(workspace, w.nsel + w.per_nsel * l);
-        int32_t *ntok = at<int32_t>(workspace, w.ntok + w.per_ntok * l);
-        const SelectWs sw = select_ws(workspace, w, l);
-        const AttnWs aw = attn_ws(workspace, w, l);
-
-        if (Ly.score_events[0])
-            e = hipEventRecord((hipEvent_t)Ly.score_events[0], sc);
-        if (e == hipSuccess)
-            e = launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
-                                   B, batch->max_ctx, nullptr, bs, bs_stride, sw.hist, K, cfg->sink_blocks,
-                                   cfg->tail_tokens, sc);
-        if (e == hipSuccess && Ly.score_events[1])
-            e = hipEventRecord((hipEvent_t)Ly.score_events[1], sc);
-        if (e == hipSuccess)
-            e = launch_select(bs, bs_stride, batch->ctx_len, B, batch->max_ctx, sw, K, cfg->sink_blocks,
-                              cfg->tail_tokens, sel, nsel, ntok, sc);
-        if (e != hipSuccess)
-            break;
-        if (!offload) {
-            e = launch_attention_paged(Ly.q, pools[l], pt, batch->pt_stride, sel, ntok, batch->ctx_len,
-                                       batch->max_ctx, B, K, cfg->budget_tokens, cfg->sm_scale, aw, Ly.out, sc);
-            continue;
-        }
-        void *stage = at<void>(workspace, w.stage + w.per_stage * (l & 1));
-        if (!two_streams) {
-            e = launch_gather(sel, nsel, batch->ctx_len, B, batch->max_ctx, pt, batch->pt_stride, pools[l], stage,
-                              K, cfg->budget_tokens, ntok, sc);
+    if (!two_streams) {
+        // One stream: every layer's kernels in order.
+        for (int l = 0; l < n_layers && e == hipSuccess; l++) {
+            e = score(l, sc);
             if (e == hipSuccess)
-                e = launch_attention_staged(Ly.q, stage, ntok, B, cfg->budget_tokens, cfg->sm_scale, aw, Ly.out,
-                                            sc);
-            continue;
+                e = select(l, sc);
+            if (e == hipSuccess && !offload)
+                e = attend_paged(l, sc);
+            if (e == hipSuccess && offload)
+                e = gather(l, sc);
+            if (e == hipSuccess && offload)
+                e = attend_staged(l, sc);
         }
-        // Two streams: the copy stream gathers layer l over PCIe once its
-        // selection exists and once attention(l-2) has released the buffer;
-        // the compute stream goes on scoring layer l+1 and attends layer l
-        // when its rows have landed.
-        hipEvent_t e_sel = ev[3 * l], e_gat = ev[3 * l + 1], e_att = ev[3 * l + 2];
-        e = hipEventRecord(e_sel, sc);
+        return hip_status(e);
+    }
+
+    if (!offload) {
+        // Pools in HBM: the compute stream streams the index of layer after
+        // layer; the second stream selects and attends layer l as soon as its
+        // scores exist, under the scoring of layer l+1.
+        for (int l = 0; l < n_layers && e == hipSuccess; l++) {
+            e = score(l, sc);
+            if (e == hipSuccess)
+                e = hipEventRecord(ev[l], sc);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(sx, ev[l], 0);
+            if (e == hipSuccess)
+                e = select(l, sx);
+            if (e == hipSuccess)
+                e = attend_paged(l, sx);
+        }
+        // The caller synchronises on the compute stream: join the second one.
+        if (e == hipSuccess)
+            e = hipEventRecord(ev[3 * n_layers], sx);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(sc, ev[3 * n_layers], 0);
+        return hip_status(e);
+    }
+
+    // Pools in pinned host memory: the copy stream gathers layer l over PCIe
+    // once its selection exists and once attention(l-2) has released the
+    // staging buffer; the compute stream goes on scoring layer l+1 and attends
+    // layer l when its rows have landed.
+    for (int l = 0; l < n_layers && e == hipSuccess; l++) {
+        hipEvent_t e_sel = ev[3 * l], e_gat = ev[3 * l + 1];
+        e = score(l, sc);
+        if (e == hipSuccess)
+            e = select(l, sc);
+        if (e == hipSuccess)
+            e = hipEventRecord(e_sel, sc);
         if (e == hipSuccess)
             e = hipStreamWaitEvent(sx, e_sel, 0);
         if (e == hipSuccess && l >= 2)
             e = hipStreamWaitEvent(sx, ev[3 * (l - 2) + 2], 0);
         if (e == hipSuccess)
-            e = launch_gather(sel, nsel, batch->ctx_len, B, batch->max_ctx, pt, batch->pt_stride, pools[l], stage,
-                              K, cfg->budget_tokens, ntok, sx);
+            e = gather(l, sx);
         if (e == hipSuccess)
             e = hipEventRecord(e_gat, sx);
-        if (e != hipSuccess)
-            break;
-        // Attention of the previous layer goes after this layer's scoring.
-        if (l >= 1) {
-            const qsa_layer_t &Lp = layers[l - 1];
-            void *pstage = at<void>(workspace, w.stage + w.per_stage * ((l - 1) & 1));
+        if (e == hipSuccess && l >= 1) {
             e = hipStreamWaitEvent(sc, ev[3 * (l - 1) + 1], 0);
             if (e == hipSuccess)
-                e = launch_attention_staged(Lp.q, pstage, at<int32_t>(workspace, w.ntok + w.per_ntok * (l - 1)), B,
-                                            cfg->budget_tokens, cfg->sm_scale, attn_ws(workspace, w, l - 1), Lp.out,
-                                            sc);
+                e = attend_staged(l - 1, sc);
             if (e == hipSuccess)
                 e = hipEventRecord(ev[3 * (l - 1) + 2], sc);
         }
-        (void)e_att;
     }
-    if (e == hipSuccess && two_streams) {
+    if (e == hipSuccess) {
         const int l = n_layers - 1;
-        const qsa_layer_t &Lp = layers[l];
-        void *pstage = at<void>(workspace, w.stage + w.per_stage * (l & 1));
         e = hipStreamWaitEvent(sc, ev[3 * l + 1], 0);
         if (e == hipSuccess)
-            e = launch_attention_staged(Lp.q, pstage, at<int32_t>(workspace, w.ntok + w.per_ntok * l), B,
-                                        cfg->budget_tokens, cfg->sm_scale, attn_ws(workspace, w, l), Lp.out, sc);
+            e = attend_staged(l, sc);
         if (e == hipSuccess)
             e = hipEventRecord(ev[3 * l + 2], sc);
         // The copy stream must not run ahead of this call's last attention

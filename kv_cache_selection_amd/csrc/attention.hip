@@ -26,7 +26,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ rows, const int32_t *__restrict__ pt,
-    int64_t pt_stride, const int32_t *__restrict__ sel, const int32_t *__restrict__ n_tok,
+    int64_t pt_stride, int64_t n_slots, const int32_t *__restrict__ sel, const int32_t *__restrict__ n_tok,
     const int32_t *__restrict__ ctx_len, int max_ctx, int budget_blocks, int budget_tokens, float sm_scale,
     float *__restrict__ part_o, float *__restrict__ part_lse, int n_split)
 {
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
             if (kPaged) {
                 const int j = sel[(int64_t)b * budget_blocks + (p >> 2)];
                 const int t = j * kBT + (p & 3);
-                const int64_t slot = pt[(int64_t)b * pt_stride + (t < L ? t : 0)];
+                const int64_t slot = safe_slot(pt[(int64_t)b * pt_stride + ((t >= 0 && t < L) ? t : 0)], n_slots);
                 row = rows + slot * kRowBytes;
             } else {
                 row = rows + ((int64_t)b * budget_tokens + p) * kRowBytes;
@@ -185,7 +185,7 @@ hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int3
 {
     dim3 grid((unsigned)ws.n_split, (unsigned)kHkv, (unsigned)batch);
     hipLaunchKernelGGL((attn_split_kernel<false>), grid, dim3(kThreads), 0, s, q,
-                       static_cast<const uint8_t *>(kv), nullptr, 0, nullptr, n_tok, nullptr, 0, 0, budget_tokens,
+                       static_cast<const uint8_t *>(kv), nullptr, 0, 0, nullptr, n_tok, nullptr, 0, 0, budget_tokens,
                        sm_scale, ws.part_o, ws.part_lse, ws.n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -194,13 +194,13 @@ hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int3
 }
 
 hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int32_t *pt, int64_t pt_stride,
-                                  const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
+                                  int64_t n_slots, const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
                                   int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s)
 {
     dim3 grid((unsigned)ws.n_split, (unsigned)kHkv, (unsigned)batch);
     hipLaunchKernelGGL((attn_split_kernel<true>), grid, dim3(kThreads), 0, s, q,
-                       static_cast<const uint8_t *>(pool), pt, pt_stride, sel, n_tok, ctx_len, max_ctx,
+                       static_cast<const uint8_t *>(pool), pt, pt_stride, n_slots, sel, n_tok, ctx_len, max_ctx,
                        budget_blocks, budget_tokens, sm_scale, ws.part_o, ws.part_lse, ws.n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restr
                                                           const int32_t *__restrict__ n_sel,
                                                           const int32_t *__restrict__ ctx_len, int max_ctx,
                                                           const int32_t *__restrict__ pt, int64_t pt_stride,
-                                                          const u32x4 *__restrict__ pool, u32x4 *__restrict__ out,
+                                                          int64_t n_slots, const u32x4 *__restrict__ pool, u32x4 *__restrict__ out,
                                                           int K, int budget_tokens, int32_t *__restrict__ n_tok)
 {
     const int b = blockIdx.y;
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restr
         if (i < ns) {
             const int j = sel[(int64_t)b * K + i];
             const int t = j * kBT + (r % kBT);
-            if (t < L) {
-                const int64_t slot = pt[(int64_t)b * pt_stride + t];
+            if (j >= 0 && t < L) {
+                const int64_t slot = safe_slot(pt[(int64_t)b * pt_stride + t], n_slots);
                 v[k] = __builtin_nontemporal_load(pool + slot * kPieces + piece);
                 const int p = i * kBT + (r % kBT);
                 dst[k] = ((int64_t)b * budget_tokens + p) * kPieces + piece;
@@ -74,11 +74,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restr
 } // namespace
 
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
-                         const int32_t *pt, int64_t pt_stride, const void *pool, void *out, int budget_blocks,
+                         const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out,
+                         int budget_blocks,
                          int budget_tokens, int32_t *n_tok, hipStream_t s)
 {
     dim3 grid((unsigned)((budget_blocks + kBlocksPerWg - 1) / kBlocksPerWg), (unsigned)batch);
-    hipLaunchKernelGGL(gather_kernel, grid, dim3(kThreads), 0, s, sel, n_sel, ctx_len, max_ctx, pt, pt_stride,
+    hipLaunchKernelGGL(gather_kernel, grid, dim3(kThreads), 0, s, sel, n_sel, ctx_len, max_ctx, pt, pt_stride, n_slots,
                        static_cast<const u32x4 *>(pool), static_cast<u32x4 *>(out), budget_blocks, budget_tokens,
                        n_tok);
     return hipGetLastError();

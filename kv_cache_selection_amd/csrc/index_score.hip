@@ -29,18 +29,17 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-// Four e4m3 codes (one dword, lowest byte first) -> four bf16 (exact).
+// Four e4m3 codes (one dword, lowest byte first) -> four bf16 (exact). The
+// packed results are moved as whole 32-bit words: extracting single __bf16
+// elements of the pair lets the compiler duplicate the low half.
 __device__ __forceinline__ s16x4 e4m3x4_to_bf16x4(uint32_t w)
 {
-    bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    s16x4 r;
-    r.x = __builtin_bit_cast(short, lo.x);
-    r.y = __builtin_bit_cast(short, lo.y);
-    r.z = __builtin_bit_cast(short, hi.x);
-    r.w = __builtin_bit_cast(short, hi.y);
-    return r;
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);   // bytes 0, 1
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);    // bytes 2, 3
+    const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    return __builtin_bit_cast(s16x4, v);
 }
 
 __device__ __forceinline__ uint32_t pick(const u32x4 &v, int i)
@@ -56,13 +55,16 @@ template <bool kTokens, bool kHist>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const uint8_t *__restrict__ keys, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ q_idx,
     const float *__restrict__ w_idx, const int32_t *__restrict__ ctx_len, const int64_t *__restrict__ row0,
-    int max_ctx, int chunk_tokens, float *__restrict__ token_scores, float *__restrict__ block_scores,
+    int64_t n_rows, int max_ctx, int chunk_tokens, float *__restrict__ token_scores, float *__restrict__ block_scores,
     int64_t bs_stride, uint32_t *__restrict__ hist, int budget_blocks, int sink_blocks, int tail_tokens)
 {
     __shared__ uint32_t lhist[kHist ? kHistBins : 1];
 
     const int b = blockIdx.y;
-    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    const int64_t r0 = row0[b];
+    int L = clamp_ctx(ctx_len[b], max_ctx);
+    if (r0 < 0 || r0 + L > n_rows)
+        L = 0;                                    // rows outside the index buffer: empty
     const int t_begin = blockIdx.x * chunk_tokens;
     if (t_begin >= L)
         return;
@@ -94,7 +96,6 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     for (int h = 0; h < kIdxH; h++)
         w[h] = w_idx[b * kIdxH + h];
 
-    const int64_t r0 = row0[b];
     const u32x4 *kbase = reinterpret_cast<const u32x4 *>(keys + r0 * kIdxD);
     const uint16_t *sbase = scales + r0;
     float *bs_row = block_scores + (int64_t)b * bs_stride;
@@ -212,8 +213,8 @@ hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)
 }
 
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
-                              const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int batch,
-                              int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
+                              const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
+                              int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s)
 {
     if (max_ctx <= 0)
@@ -227,20 +228,20 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
     if (token_scores) {
         if (hist)
             hipLaunchKernelGGL((index_score_kernel<true, true>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
                                budget_blocks, sink_blocks, tail_tokens);
         else
             hipLaunchKernelGGL((index_score_kernel<true, false>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
                                budget_blocks, sink_blocks, tail_tokens);
     } else {
         if (hist)
             hipLaunchKernelGGL((index_score_kernel<false, true>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
                                budget_blocks, sink_blocks, tail_tokens);
         else
             hipLaunchKernelGGL((index_score_kernel<false, false>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
+                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
                                budget_blocks, sink_blocks, tail_tokens);
     }
     return hipGetLastError();

@@ -25,7 +25,6 @@ constexpr int kMaxCtx = 1 << 21;               // tokens per sequence
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
-constexpr int kCounters = 4;                   // per sequence: definite, candidate, ticket, pad
 
 // Attention: tokens per split.
 constexpr int kTPS = 64;
@@ -64,10 +63,8 @@ __device__ __forceinline__ int forced_count(int n_blk, int sink, int tail_first)
 
 // Per-layer pieces of the caller's workspace, carved on the host.
 struct SelectWs {
-    uint32_t *hist;      // [B][kHistBins]
-    uint32_t *counters;  // [B][kCounters]
-    int32_t *def_list;   // [B][K]
-    uint64_t *cand;      // [B][cand_stride]
+    uint32_t *hist;      // [B][kHistBins], zeroed before scoring
+    uint64_t *cand;      // [B][cand_stride] candidate spill list
     int64_t cand_stride;
 };
 
@@ -77,12 +74,19 @@ struct AttnWs {
     int n_split;
 };
 
+// A physical slot read from a page table, forced into [0, n_slots) so that a
+// bad entry can never address memory outside the pool.
+__device__ __forceinline__ int64_t safe_slot(int32_t slot, int64_t n_slots)
+{
+    return ((uint64_t)(int64_t)slot < (uint64_t)n_slots) ? (int64_t)slot : 0;
+}
+
 // Kernel launchers (one translation unit each).
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
-                              const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int batch,
-                              int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
+                              const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
+                              int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
                               hipStream_t s);
 
@@ -95,7 +99,7 @@ hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int
                          int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s);
 
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
-                         const int32_t *pt, int64_t pt_stride, const void *pool, void *out, int budget_blocks,
+                         const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out, int budget_blocks,
                          int budget_tokens, int32_t *n_tok, hipStream_t s);
 
 // Attention over staged rows (kv != nullptr) or through the page table.
@@ -104,6 +108,7 @@ hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int3
                                    hipStream_t s);
 
 hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int32_t *pt, int64_t pt_stride,
+                                  int64_t n_slots,
                                   const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
                                   int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s);

@@ -63,7 +63,8 @@ FAKE = 1 << 20      # a 256-byte aligned non-null address; never dereferenced on
 
 
 def _batch(**kw):
-    args = dict(batch=1, max_ctx=100, ctx_len=FAKE, idx_row0=FAKE, page_table=FAKE, pt_stride=100, n_slots=100)
+    args = dict(batch=1, max_ctx=100, ctx_len=FAKE, idx_row0=FAKE, page_table=FAKE, pt_stride=100, n_slots=100,
+                n_idx_rows=100)
     args.update(kw)
     return qsa.make_batch(**args)
 
@@ -124,3 +125,27 @@ def test_workspace_too_small_rejected():
     with pytest.raises(qsa.QsaError) as ei:
         qsa.qsa_decode_step(cfg, _batch(), [lay, lay], 0, FAKE, need - 256)
     assert ei.value.status == qsa.QSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_structs_keep_their_tensors_alive():
+    """The structs hold raw addresses; the binding keeps the tensors behind
+    them referenced so their memory cannot be freed and reused before a call
+    reads it (a freed row-offset tensor once sent the scoring kernel to
+    addresses outside the index buffer)."""
+    import gc
+    import weakref
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4, dtype=torch.int32)
+    r = weakref.ref(t)
+    b = qsa.make_batch(1, 4, t, torch.zeros(1, dtype=torch.int64), n_idx_rows=4)
+    del t
+    gc.collect()
+    assert r() is not None and b._keep[0] is r()
+    k = torch.zeros(16, dtype=torch.uint8)
+    rk = weakref.ref(k)
+    lay = qsa.make_layer(k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    del k
+    gc.collect()
+    assert rk() is not None and lay.idx_keys == rk().data_ptr()
+    with pytest.raises(ValueError):
+        qsa.make_batch(1, 4, FAKE, FAKE)          # index rows without their count
