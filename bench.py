@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="batch8-256k")
     ap.add_argument("--cpu-units", type=int, default=2, help="oracle units in the CPU baseline (0: skip)")
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                    help="2: overlap layers on a second stream (default); 1: every kernel in order on one stream")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the QSA decode step runs on a single MI355X and this build has "
@@ -140,7 +142,8 @@ def main():
     nws = qsa.qsa_workspace_size(cfg, di.batch, di.max_ctx, NL, loc)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    copy = torch.cuda.Stream()     # select/attention (HBM) or the PCIe gather (host pools) overlap the scoring
+    # select/attention (HBM pools) or the PCIe gather (host pools) overlap the scoring on a second stream
+    copy = torch.cuda.Stream() if args.streams == 2 else None
 
     def layers(events=None):
         return [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l], di.out[l],
@@ -199,7 +202,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 generator; planted relevant blocks)",
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(ctx.max()), "layers": NL,
                    "budget_tokens": wl.budget, "sink_blocks": wl.sink_blocks, "tail_tokens": wl.tail_tokens,
-                   "kv": "host-pinned" if di.kv_host else "hbm"},
+                   "kv": "host-pinned" if di.kv_host else "hbm", "streams": args.streams},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "bytes_per_launch": idx_bytes_launch,

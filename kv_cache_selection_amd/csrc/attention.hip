@@ -147,28 +147,45 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     }
 }
 
-__global__ __launch_bounds__(kThreads) void merge_kernel(const float *__restrict__ part_o,
-                                                         const float *__restrict__ part_lse, int n_split,
-                                                         float *__restrict__ out)
+constexpr int kMaxSplit = kMaxBudget / kTPS;
+
+// One workgroup per (sequence, head); thread d owns output dim d. The split
+// weights e^{lse_s - max} are computed once into LDS, then every thread sums
+// its column with independent loads.
+__global__ __launch_bounds__(kDh) void merge_kernel(const float *__restrict__ part_o,
+                                                    const float *__restrict__ part_lse, int n_split,
+                                                    float *__restrict__ out)
 {
+    __shared__ float wgt[kMaxSplit];
+    __shared__ float red[kDh / 64];
     const int bh = blockIdx.x;              // b * kHq + h
+    const int tid = threadIdx.x;
     const float *lse = part_lse + (int64_t)bh * n_split;
-    float m = -INFINITY;
-    for (int s = 0; s < n_split; s++)
-        m = fmaxf(m, lse[s]);
+    float ls = tid < n_split ? lse[tid] : -INFINITY;
+    // block max of the split lse values (n_split <= 256 = threads)
+    float m = ls;
+    for (int o = 32; o >= 1; o >>= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0)
+        red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (tid < n_split)
+        wgt[tid] = (m == -INFINITY || ls == -INFINITY) ? 0.0f : __expf(ls - m);
+    __syncthreads();
     float acc = 0.0f, den = 0.0f;
     if (m != -INFINITY) {
+        const float *col = part_o + (int64_t)bh * n_split * kDh + tid;
+#pragma unroll 8
         for (int s = 0; s < n_split; s++) {
-            const float ls = lse[s];
-            if (ls == -INFINITY)
-                continue;
-            const float wgt = __expf(ls - m);
-            den += wgt;
-            acc = fmaf(wgt, part_o[((int64_t)bh * n_split + s) * kDh + threadIdx.x], acc);
+            const float ws = wgt[s];
+            const float x = col[(int64_t)s * kDh];   // empty splits hold stale data: select, not multiply
+            den += ws;
+            acc = ws != 0.0f ? fmaf(ws, x, acc) : acc;
         }
         acc /= den;
     }
-    out[(int64_t)bh * kDh + threadIdx.x] = acc;
+    out[(int64_t)bh * kDh + tid] = acc;
 }
 
 } // namespace

@@ -6,14 +6,21 @@
 // and for every C4 block j (article intro: 4 adjacent tokens form the unit
 // of selection) B_j = max of s_t over the block's valid tokens.
 //
-// Mapping on gfx950: one token per lane, 64 tokens per wave iteration. The
-// e4m3 codes are widened to bf16 in registers (exact: 4 significant bits fit
-// bf16's 8) and the 4-head x 64-dim dot products run on the matrix cores as
-// 16 accumulating v_mfma_f32_4x4x4_16b_bf16 (16 independent 4x4x4 blocks per
-// instruction: block = 4 lanes = 4 tokens, rows = the 4 indexer heads). The
-// products bf16 x bf16 are exact in fp32; accumulation is fp32. The VALU is
-// left with the decode, the ReLU/weight epilogue and the block max, so the
-// kernel stays bound by HBM, not by fp32 FMA throughput.
+// Mapping on gfx950: a wave scores a tile of 64 tokens as 4 groups of 16.
+// For group g, lane l loads the 16 bytes at offset 16*(l>>4) of token
+// 16g + (l&15), so each of the wave's four 16-byte loads reads one contiguous
+// 1 KB piece of the tile (full cache lines, no lane stride). The e4m3 codes
+// are widened to bf16 in registers (exact: 4 significant bits fit bf16's 8)
+// and the 4-head x 64-dim dot products run on the matrix cores as
+// v_mfma_f32_16x16x32_bf16 (B = 32 dims x 16 tokens): the lane's first 8
+// bytes feed one MFMA and its last 8 the other, and the query operand A
+// follows the same permutation of the 64 dims. For group g the query heads
+// sit in rows 4g..4g+3 of A (zeros elsewhere), so all four groups accumulate
+// into one 16x16 tile whose row 4g+h, column j -- head h of token 16g+j --
+// the MFMA output layout places in lane 16g+j: one token per lane, no
+// shuffles. bf16 x bf16 products are exact in fp32; accumulation is fp32.
+// The VALU only widens codes and runs the ReLU/weight epilogue and the block
+// max, so the kernel stays bound by HBM, not by fp32 FMA throughput.
 //
 // When the sequence has more blocks than the budget, each workgroup also
 // builds an LDS histogram of the top 12 bits of its blocks' order keys
@@ -26,25 +33,21 @@ namespace qsa {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-// Four e4m3 codes (one dword, lowest byte first) -> four bf16 (exact). The
+// Eight e4m3 codes (two dwords, lowest byte first) -> eight bf16 (exact). The
 // packed results are moved as whole 32-bit words: extracting single __bf16
-// elements of the pair lets the compiler duplicate the low half.
-__device__ __forceinline__ s16x4 e4m3x4_to_bf16x4(uint32_t w)
+// elements of a pair lets the compiler duplicate the low half.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1)
 {
-    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);   // bytes 0, 1
-    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);    // bytes 2, 3
-    const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-    return __builtin_bit_cast(s16x4, v);
-}
-
-__device__ __forceinline__ uint32_t pick(const u32x4 &v, int i)
-{
-    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+    const u32x4 v = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 constexpr int kThreads = 256;
@@ -81,14 +84,20 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
             lhist[i] = 0;
     }
 
-    // A operand: lane holds q[head = lane & 3][4m .. 4m+3] for m = 0..15.
-    s16x4 qa[16];
+    // A operands: for group g, lane l (row l&15 of A) holds head (l&3) of the
+    // query when (l&15)>>2 == g, else zeros; dims follow the lane's bytes:
+    // qa[g][0] = dims 16(l>>4) + 0..7, qa[g][1] = dims 16(l>>4) + 8..15.
+    bf16x8 qa[4][2];
     {
-        const uint2 *qrow = reinterpret_cast<const uint2 *>(q_idx + ((int64_t)b * kIdxH + (lane & 3)) * kIdxD);
+        const u32x4 *qrow =
+            reinterpret_cast<const u32x4 *>(q_idx + ((int64_t)b * kIdxH + (lane & 3)) * kIdxD + 16 * (lane >> 4));
+        const u32x4 q0 = qrow[0], q1 = qrow[1];
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
-            uint2 v = qrow[m];
-            qa[m] = __builtin_bit_cast(s16x4, v);
+        for (int g = 0; g < 4; g++) {
+            const bool mine = ((lane & 15) >> 2) == g;
+            qa[g][0] = __builtin_bit_cast(bf16x8, mine ? q0 : z);
+            qa[g][1] = __builtin_bit_cast(bf16x8, mine ? q1 : z);
         }
     }
     float w[kIdxH];
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     for (int h = 0; h < kIdxH; h++)
         w[h] = w_idx[b * kIdxH + h];
 
-    const u32x4 *kbase = reinterpret_cast<const u32x4 *>(keys + r0 * kIdxD);
+    const uint8_t *kbase = keys + r0 * kIdxD;
     const uint16_t *sbase = scales + r0;
     float *bs_row = block_scores + (int64_t)b * bs_stride;
 
@@ -104,29 +113,41 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
         __syncthreads();
 
     const int t_end = min(t_begin + chunk_tokens, L);
-    for (int tw = t_begin + wave * kWaveTok; tw < t_end; tw += kWgTok) {
+    // Two-deep software pipeline: the keys of the wave's next 64 tokens are
+    // requested before the current 64 are widened and multiplied.
+    u32x4 k[4], kn[4];
+    uint16_t sc_bits = 0, sc_next = 0;
+    const int grp_tok = lane & 15;          // token within a group, for the loads
+    const int grp_off = 16 * (lane >> 4);   // byte offset within the token's 64
+    auto load_tile = [&](int tw, u32x4 *dst, uint16_t &sc) {
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int t = tw + 16 * g + grp_tok;
+            dst[g] = t < L ? __builtin_nontemporal_load(
+                                 reinterpret_cast<const u32x4 *>(kbase + (int64_t)t * kIdxD + grp_off))
+                           : u32x4{0u, 0u, 0u, 0u};
+        }
+        sc = (tw + lane < L) ? sbase[tw + lane] : (uint16_t)0;
+    };
+    int tw = t_begin + wave * kWaveTok;
+    if (tw < t_end)
+        load_tile(tw, k, sc_bits);
+    for (; tw < t_end; tw += kWgTok) {
+        const int tn = tw + kWgTok;
+        if (tn < t_end)
+            load_tile(tn, kn, sc_next);
         const int t = tw + lane;
         const bool valid = t < L;
-        u32x4 k[4];
-        uint16_t sc_bits = 0;
-        if (valid) {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                k[i] = __builtin_nontemporal_load(kbase + (int64_t)t * 4 + i);
-            sc_bits = sbase[t];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                k[i] = u32x4{0u, 0u, 0u, 0u};
-        }
 
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // Two independent accumulation chains (first / last 8 bytes of each lane).
+        f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
-            s16x4 kb = e4m3x4_to_bf16x4(pick(k[m >> 2], m & 3));
-            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[m], kb, acc, 0, 0, 0);
+        for (int g = 0; g < 4; g++) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[g][0], e4m3x8_to_bf16x8(k[g].x, k[g].y), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[g][1], e4m3x8_to_bf16x8(k[g].z, k[g].w), acc1, 0, 0, 0);
         }
-        // acc[h] = q_h . k_t for this lane's token.
+        const f32x4 acc = acc0 + acc1;
+        // acc[h] = q_h . k_t for this lane's token t.
         const float sigma = (float)__builtin_bit_cast(_Float16, sc_bits);
         float s = 0.0f;
         s += w[0] * fmaxf(sigma * acc[0], 0.0f);
@@ -147,6 +168,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
             if (do_hist && blk >= sink_blocks && blk < tail_first)
                 atomicAdd(&lhist[order_key(s) >> kHistShift], 1u);
         }
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+            k[g] = kn[g];
+        sc_bits = sc_next;
     }
 
     if (do_hist) {

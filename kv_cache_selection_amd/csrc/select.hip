@@ -30,7 +30,7 @@ namespace qsa {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kPerThread = 8;                      // block scores per thread per pass
+constexpr int kPerThread = 64;                     // block scores per thread per pass (65536 per pass)
 constexpr int kDefCap = kMaxBudget / kBT;          // definite blocks are < K <= 2048
 constexpr int kCandCap = 2048;                     // candidates held in LDS
 constexpr int kSegBlocks = 1 << 18;                // bitmap segment (32 KB of LDS)
@@ -144,6 +144,21 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int tail_first = tail_first_block(L, tail_tokens, n);
     const int r = K - forced_count(n, sink_blocks, tail_first);   // non-forced blocks to take (host: >= 0)
 
+    const float *row = block_scores + (int64_t)b * bs_stride;
+    uint64_t *spill_b = spill + (int64_t)b * spill_stride;
+    // The first pass's scores are requested before anything waits on memory,
+    // so their latency overlaps the histogram walk.
+    float v[kPerThread];
+    auto load_pass = [&](int base) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; k++) {
+            const int j = base + k * kThreads + tid;
+            v[k] = j < n ? row[j] : 0.0f;
+        }
+    };
+    if (r > 0)
+        load_pass(0);
+
     // ---- 1. threshold bin b* from the 12-bit histogram ----------------------
     uint32_t bstar = kHistBins;   // no bin: nothing non-forced is taken
     if (tid == 0) {
@@ -161,16 +176,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
 
     // ---- 2. one pass over the block scores -----------------------------------
-    const float *row = block_scores + (int64_t)b * bs_stride;
-    uint64_t *spill_b = spill + (int64_t)b * spill_stride;
     if (r > 0) {
         for (int base = 0; base < n; base += kThreads * kPerThread) {
-            float v[kPerThread];
-#pragma unroll
-            for (int k = 0; k < kPerThread; k++) {
-                const int j = base + k * kThreads + tid;
-                v[k] = j < n ? row[j] : 0.0f;
-            }
+            if (base > 0)
+                load_pass(base);
 #pragma unroll
             for (int k = 0; k < kPerThread; k++) {
                 const int j = base + k * kThreads + tid;
