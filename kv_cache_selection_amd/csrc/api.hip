@@ -20,10 +20,10 @@ int n_split_of(int budget_tokens) { return (budget_tokens + kTPS - 1) / kTPS; }
 // Byte offsets of the workspace pieces. The histograms of every layer come
 // first, contiguous, so one fill kernel clears them all.
 struct WsLayout {
-    int B = 0, K = 0, n_blk_max = 0, n_layers = 0, n_split = 0, budget = 0;
+    int B = 0, K = 0, n_blk_max = 0, n_slices = 0, n_layers = 0, n_split = 0, budget = 0;
     size_t hist = 0, zero_bytes = 0;
-    size_t cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0;
-    size_t per_hist = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
+    size_t cnt = 0, sdef = 0, scand = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0;
+    size_t per_hist = 0, per_cnt = 0, per_sdef = 0, per_scand = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
            per_ntok = 0, per_po = 0, per_plse = 0, per_stage = 0;
     size_t total = 0;
 };
@@ -35,10 +35,14 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.K = cfg->budget_tokens / kBT;
     w.budget = cfg->budget_tokens;
     w.n_blk_max = (max_ctx + kBT - 1) / kBT;
+    w.n_slices = w.n_blk_max > 0 ? (w.n_blk_max + kSliceBlocks - 1) / kSliceBlocks : 1;
     w.n_layers = n_layers;
     w.n_split = n_split_of(cfg->budget_tokens);
     const size_t nb = (size_t)(w.n_blk_max > 0 ? w.n_blk_max : 1);
     w.per_hist = align_up((size_t)batch * kHistBins * 4);
+    w.per_cnt = align_up((size_t)batch * w.n_slices * 2 * 4);
+    w.per_sdef = align_up((size_t)batch * w.n_slices * kSliceBlocks * 4);
+    w.per_scand = align_up((size_t)batch * w.n_slices * kSliceBlocks * 8);
     w.per_cand = align_up((size_t)batch * nb * 8);
     w.per_bs = align_up((size_t)batch * nb * 4);
     w.per_sel = align_up((size_t)batch * w.K * 4);
@@ -51,6 +55,12 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.hist = off;
     off += w.per_hist * n_layers;
     w.zero_bytes = off;
+    w.cnt = off;
+    off += w.per_cnt * n_layers;
+    w.sdef = off;
+    off += w.per_sdef * n_layers;
+    w.scand = off;
+    off += w.per_scand * n_layers;
     w.cand = off;
     off += w.per_cand * n_layers;
     w.bs = off;
@@ -77,8 +87,11 @@ SelectWs select_ws(void *ws, const WsLayout &w, int l)
 {
     SelectWs s;
     s.hist = at<uint32_t>(ws, w.hist + w.per_hist * l);
-    s.cand = at<uint64_t>(ws, w.cand + w.per_cand * l);
-    s.cand_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
+    s.slot_count = at<uint32_t>(ws, w.cnt + w.per_cnt * l);
+    s.slot_def = at<int32_t>(ws, w.sdef + w.per_sdef * l);
+    s.slot_cand = at<uint64_t>(ws, w.scand + w.per_scand * l);
+    s.spill = at<uint64_t>(ws, w.cand + w.per_cand * l);
+    s.spill_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
     return s;
 }
 

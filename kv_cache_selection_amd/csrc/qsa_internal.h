@@ -62,10 +62,15 @@ __device__ __forceinline__ int forced_count(int n_blk, int sink, int tail_first)
 }
 
 // Per-layer pieces of the caller's workspace, carved on the host.
+constexpr int kSliceBlocks = 2048;             // blocks per selection slice (one collect workgroup)
+
 struct SelectWs {
-    uint32_t *hist;      // [B][kHistBins], zeroed before scoring
-    uint64_t *cand;      // [B][cand_stride] candidate spill list
-    int64_t cand_stride;
+    uint32_t *hist;        // [B][kHistBins], zeroed before scoring
+    uint32_t *slot_count;  // [B][n_slices][2] per-slice list lengths (definite, candidates)
+    int32_t *slot_def;     // [B][n_slices][kSliceBlocks] blocks above the threshold bin
+    uint64_t *slot_cand;   // [B][n_slices][kSliceBlocks] blocks inside the threshold bin
+    uint64_t *spill;       // [B][spill_stride] candidates past the finish kernel's LDS
+    int64_t spill_stride;
 };
 
 struct AttnWs {

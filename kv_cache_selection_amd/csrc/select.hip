@@ -7,39 +7,47 @@
 // ascending block order. The result is exact -- the same set a full sort
 // would give -- for any input, ties included.
 //
-// Radix selection over a monotone 32-bit key of the score:
+// Radix selection over a monotone 32-bit key of the score, in three kernels:
 //  1. (fused into scoring, or block_hist_kernel) a per-sequence histogram of
-//     the key's top 12 bits over the non-forced blocks, built by many
-//     workgroups with global atomics;
-//  2. here, one workgroup per sequence finds the threshold bin b* from that
-//     histogram and scans the sequence's block scores once, keeping the
-//     blocks above b* ("definite") and the blocks inside b* ("candidates", as
-//     64-bit composites key << 32 | ~index: unique, and ordered like
-//     (score desc, index asc)) in LDS;
-//  3. it picks the best need = K - |F| - |definite| candidates exactly -- by
-//     rank counting when they fit in LDS, by a radix select over the
-//     remaining 52 bits otherwise (candidates past the LDS capacity spill to
-//     a global list only this workgroup touches) -- and writes the union in
-//     ascending order through an LDS bitmap, so the output needs no sort.
-// One workgroup owns a sequence from start to end, so no step needs a
-// device-scope fence: on gfx950 such a fence writes back and invalidates the
-// XCD's L2, which costs far more than this whole selection.
+//     the key's top 12 bits over the non-forced blocks;
+//  2. collect_kernel: one workgroup per slice of 2048 blocks finds the
+//     threshold bin b* from the histogram and compacts, in LDS, the slice's
+//     blocks above b* ("definite") and inside b* ("candidates", as 64-bit
+//     composites key << 32 | ~index: unique, and ordered like (score desc,
+//     index asc)); it writes them with their counts to the slice's own slot;
+//  3. finish_kernel: one workgroup per sequence gathers the slots through
+//     prefix offsets, picks the best need = K - |F| - |definite| candidates
+//     exactly with a radix select over the composites' remaining 52 bits
+//     (11-bit digits, finishing by direct ranking once few are left), and
+//     writes the union in ascending order through an LDS bitmap, so the
+//     output needs no sort.
+// Nothing is shared between workgroups inside a kernel: no global atomics on
+// a few hot addresses (they serialise at the memory side) and no
+// device-scope fences (on gfx950 one writes back and invalidates the XCD's
+// L2). The kernel boundary orders the slots, and the scan of the scores is
+// spread over many CUs.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kPerThread = 64;                     // block scores per thread per pass (65536 per pass)
-constexpr int kDefCap = kMaxBudget / kBT;          // definite blocks are < K <= 2048
-constexpr int kCandCap = 2048;                     // candidates held in LDS
+constexpr int kThreads = 1024;                     // finish_kernel
+constexpr int kCollectThreads = 256;
+constexpr int kCollectPer = 8;                     // block scores per thread in collect_kernel
+constexpr int kCandCap = 2048;                     // candidates held in LDS by finish_kernel
 constexpr int kSegBlocks = 1 << 18;                // bitmap segment (32 KB of LDS)
 constexpr int kSegWords = kSegBlocks / 32;
-constexpr int kRadixBits = 13;
-constexpr int kRadixBins = 1 << kRadixBits;        // 8192 bins = 32 KB
-constexpr int kWorkWords = kSegWords > kRadixBins ? kSegWords : kRadixBins;
+constexpr int kDigitBits = 11;                     // radix digit of the candidate selection
+constexpr int kDigitBins = 1 << kDigitBits;        // 2048 bins, 2 per thread
+constexpr int kWorkWords = kSegWords;              // bitmap; also digit histogram + short list
+constexpr int kDefCap = kMaxBudget / kBT;          // definite blocks are < K <= 2048
+constexpr int kMaxSlices = (kMaxCtx / kBT) / kSliceBlocks;   // 256
+static_assert(kSliceBlocks == kCollectThreads * kCollectPer, "slice size");
+static_assert(kMaxSlices <= kThreads, "one finish thread per slice");
+static_assert(kDigitBins + 2 * kThreads <= kWorkWords, "digit histogram and short list fit the work area");
 
-// LDS layout (dynamic): candidates | definite list | work area (histograms, bitmap)
+// finish_kernel LDS layout (dynamic): candidates | definite list | work area
+// (digit histogram and short list, then the output bitmap)
 constexpr size_t kSmemBytes = (size_t)kCandCap * 8 + (size_t)kDefCap * 4 + (size_t)kWorkWords * 4;
 
 // Position of this lane's item in an LDS list: one LDS atomic per wave.
@@ -59,7 +67,8 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t *counter)
 }
 
 // Block-wide inclusive prefix sum of one uint32 per thread.
-__device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [16] */, uint32_t *total)
+template <int NT>
+__device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [NT / 64] */, uint32_t *total)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -74,7 +83,7 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [16] */, ui
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; w++) {
+    for (int w = 0; w < NT / 64; w++) {
         const uint32_t x = sh[w];
         off += (w < wave) ? x : 0u;
         tot += x;
@@ -84,13 +93,13 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [16] */, ui
     return v + off;
 }
 
-// Walk a histogram of kThreads * W bins from the top: the bin where the
-// running count first reaches `want`, and the count strictly above it.
-template <int W>
+// Walk a histogram of NT * W bins from the top: the bin where the running
+// count first reaches `want`, and the count strictly above it.
+template <int W, int NT>
 __device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
                               uint32_t *above_out)
 {
-    const int tr = kThreads - 1 - threadIdx.x;         // thread 0 owns the top bins
+    const int tr = NT - 1 - threadIdx.x;               // thread 0 owns the top bins
     uint32_t hv[W], local = 0;
 #pragma unroll
     for (int i = 0; i < W; i++) {
@@ -98,7 +107,7 @@ __device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_sca
         local += hv[i];
     }
     uint32_t total;
-    uint32_t above = block_inclusive_scan(local, sh_scan, &total) - local;
+    uint32_t above = block_inclusive_scan<NT>(local, sh_scan, &total) - local;
 #pragma unroll
     for (int i = W - 1; i >= 0; i--) {
         if (above < want && above + hv[i] >= want) {
@@ -110,26 +119,123 @@ __device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_sca
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void select_kernel(
+// Number of non-forced blocks to take, or -1 when every block fits.
+__device__ __forceinline__ int rest_to_take(int L, int n, int K, int sink_blocks, int tail_tokens, int *tail_first)
+{
+    if (n <= K)
+        return -1;
+    *tail_first = tail_first_block(L, tail_tokens, n);
+    return K - forced_count(n, sink_blocks, *tail_first);   // host guarantees >= 0
+}
+
+__global__ __launch_bounds__(kCollectThreads) void collect_kernel(
     const float *__restrict__ block_scores, int64_t bs_stride, const int32_t *__restrict__ ctx_len, int max_ctx,
-    const uint32_t *__restrict__ hist, uint64_t *__restrict__ spill, int64_t spill_stride, int K, int sink_blocks,
-    int tail_tokens, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel, int32_t *__restrict__ n_tok)
+    const uint32_t *__restrict__ hist, uint32_t *__restrict__ slot_count, int32_t *__restrict__ slot_def,
+    uint64_t *__restrict__ slot_cand, int n_slices, int K, int sink_blocks, int tail_tokens)
+{
+    __shared__ int32_t ldef[kSliceBlocks];          // 8 KB
+    __shared__ uint64_t lcand[kSliceBlocks];        // 16 KB
+    __shared__ uint32_t sh_scan[kCollectThreads / 64];
+    __shared__ uint32_t sh_u[4];                    // 0,1: crossing bin / count above; 2,3: list lengths
+
+    const int b = blockIdx.y;
+    const int slice = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    const int n = (L + kBT - 1) / kBT;
+    const int j0 = slice * kSliceBlocks;
+    int tail_first = n;
+    const int r = rest_to_take(L, n, K, sink_blocks, tail_tokens, &tail_first);
+    if (r <= 0 || j0 >= n)
+        return;
+
+    // The slice's scores are requested first; their latency overlaps the
+    // histogram walk.
+    const float *row = block_scores + (int64_t)b * bs_stride;
+    float v[kCollectPer];
+#pragma unroll
+    for (int k = 0; k < kCollectPer; k++) {
+        const int j = j0 + k * kCollectThreads + tid;
+        v[k] = j < n ? row[j] : 0.0f;
+    }
+    if (tid == 0) {
+        sh_u[0] = kHistBins;
+        sh_u[2] = 0;
+        sh_u[3] = 0;
+    }
+    __syncthreads();
+    find_crossing<kHistBins / kCollectThreads, kCollectThreads>(hist + (int64_t)b * kHistBins, (uint32_t)r, sh_scan,
+                                                                &sh_u[0], &sh_u[1]);
+    const uint32_t bstar = sh_u[0];
+
+#pragma unroll
+    for (int k = 0; k < kCollectPer; k++) {
+        const int j = j0 + k * kCollectThreads + tid;
+        bool is_def = false, is_cand = false;
+        uint32_t key = 0;
+        if (j < n && j >= sink_blocks && j < tail_first) {
+            key = order_key(v[k]);
+            const uint32_t bin = key >> kHistShift;
+            is_def = bin > bstar;
+            is_cand = bin == bstar;
+        }
+        const uint32_t pd = wave_append(is_def, &sh_u[2]);
+        const uint32_t pc = wave_append(is_cand, &sh_u[3]);
+        if (is_def)
+            ldef[pd] = j;                           // at most kSliceBlocks items per slice
+        if (is_cand)
+            lcand[pc] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+    }
+    __syncthreads();
+    const uint32_t nd = sh_u[2], nc = sh_u[3];
+    const int64_t slot = (int64_t)b * n_slices + slice;
+    if (tid == 0) {
+        slot_count[2 * slot] = nd;
+        slot_count[2 * slot + 1] = nc;
+    }
+    for (uint32_t i = tid; i < nd; i += kCollectThreads)
+        slot_def[slot * kSliceBlocks + i] = ldef[i];
+    for (uint32_t i = tid; i < nc; i += kCollectThreads)
+        slot_cand[slot * kSliceBlocks + i] = lcand[i];
+}
+
+// Index of the slot whose [off[s], off[s+1]) range holds p (off ascending, off[0] = 0).
+__device__ __forceinline__ int slot_of(const uint32_t *off, int ns, uint32_t p)
+{
+    int lo = 0, hi = ns - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= p)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kThreads) void finish_kernel(
+    const int32_t *__restrict__ ctx_len, int max_ctx, const uint32_t *__restrict__ slot_count,
+    const int32_t *__restrict__ slot_def, const uint64_t *__restrict__ slot_cand, int n_slices,
+    uint64_t *__restrict__ spill, int64_t spill_stride, int K, int sink_blocks, int tail_tokens,
+    int32_t *__restrict__ sel, int32_t *__restrict__ n_sel, int32_t *__restrict__ n_tok)
 {
     extern __shared__ uint64_t smem64[];
     uint64_t *cand = smem64;                                            // [kCandCap]
     int32_t *defl = reinterpret_cast<int32_t *>(smem64 + kCandCap);     // [kDefCap]
     uint32_t *work = reinterpret_cast<uint32_t *>(defl + kDefCap);      // [kWorkWords]
-    __shared__ uint32_t sh_scan[16];
-    __shared__ uint32_t sh_u[8];   // 0,1: crossing bin / count above; 2: #definite; 3: #candidates;
-                                   // 4,5: T64; 6: partial last block taken
+    __shared__ uint32_t off_d[kMaxSlices + 1], off_c[kMaxSlices + 1];
+    __shared__ uint32_t sh_scan[kThreads / 64];
+    __shared__ uint32_t sh_u[8];   // 0,1: crossing digit / count above; 4,5: T64; 6: partial last block taken
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int L = clamp_ctx(ctx_len[b], max_ctx);
     const int n = (L + kBT - 1) / kBT;
     int32_t *sel_b = sel + (int64_t)b * K;
+    int tail_first = n;
+    const int r = rest_to_take(L, n, K, sink_blocks, tail_tokens, &tail_first);
 
-    if (n <= K) {
+    if (r < 0) {
         // Every block fits in the budget.
         for (int j = tid; j < K; j += kThreads)
             sel_b[j] = j < n ? j : -1;
@@ -140,125 +246,123 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         }
         return;
     }
-
-    const int tail_first = tail_first_block(L, tail_tokens, n);
-    const int r = K - forced_count(n, sink_blocks, tail_first);   // non-forced blocks to take (host: >= 0)
-
-    const float *row = block_scores + (int64_t)b * bs_stride;
-    uint64_t *spill_b = spill + (int64_t)b * spill_stride;
-    // The first pass's scores are requested before anything waits on memory,
-    // so their latency overlaps the histogram walk.
-    float v[kPerThread];
-    auto load_pass = [&](int base) {
-#pragma unroll
-        for (int k = 0; k < kPerThread; k++) {
-            const int j = base + k * kThreads + tid;
-            v[k] = j < n ? row[j] : 0.0f;
-        }
-    };
-    if (r > 0)
-        load_pass(0);
-
-    // ---- 1. threshold bin b* from the 12-bit histogram ----------------------
-    uint32_t bstar = kHistBins;   // no bin: nothing non-forced is taken
-    if (tid == 0) {
-        sh_u[0] = kHistBins;
-        sh_u[1] = 0;
-        sh_u[2] = 0;
-        sh_u[3] = 0;
+    if (tid == 0)
         sh_u[6] = 0;
-    }
-    __syncthreads();
-    if (r > 0) {
-        find_crossing<kHistBins / kThreads>(hist + (int64_t)b * kHistBins, (uint32_t)r, sh_scan, &sh_u[0],
-                                            &sh_u[1]);
-        bstar = sh_u[0];
-    }
 
-    // ---- 2. one pass over the block scores -----------------------------------
-    if (r > 0) {
-        for (int base = 0; base < n; base += kThreads * kPerThread) {
-            if (base > 0)
-                load_pass(base);
-#pragma unroll
-            for (int k = 0; k < kPerThread; k++) {
-                const int j = base + k * kThreads + tid;
-                bool is_def = false, is_cand = false;
-                uint32_t key = 0;
-                if (j < n && j >= sink_blocks && j < tail_first) {
-                    key = order_key(v[k]);
-                    const uint32_t bin = key >> kHistShift;
-                    is_def = bin > bstar;
-                    is_cand = bin == bstar;
-                }
-                const uint32_t pd = wave_append(is_def, &sh_u[2]);
-                const uint32_t pc = wave_append(is_cand, &sh_u[3]);
-                if (is_def && pd < (uint32_t)kDefCap)
-                    defl[pd] = j;
-                if (is_cand) {
-                    const uint64_t comp = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-                    if (pc < (uint32_t)kCandCap)
-                        cand[pc] = comp;
-                    else if ((int64_t)pc < spill_stride)
-                        spill_b[pc] = comp;
-                }
-            }
-        }
+    // ---- gather the slots: prefix offsets, then one entry per thread ---------
+    const int ns = r > 0 ? (n + kSliceBlocks - 1) / kSliceBlocks : 0;
+    uint32_t cd = 0, cc = 0;
+    if (tid < ns) {
+        const int64_t slot = (int64_t)b * n_slices + tid;
+        cd = slot_count[2 * slot];
+        cc = slot_count[2 * slot + 1];
+    }
+    uint32_t tot_d, tot_c;
+    const uint32_t incl_d = block_inclusive_scan<kThreads>(cd, sh_scan, &tot_d);
+    const uint32_t incl_c = block_inclusive_scan<kThreads>(cc, sh_scan, &tot_c);
+    if (tid < ns) {
+        off_d[tid] = incl_d - cd;
+        off_c[tid] = incl_c - cc;
     }
     __syncthreads();
-    // The histogram describes these same scores, so D < r <= D + C; the clamps
-    // only keep every index in bounds.
-    const uint32_t D = r > 0 ? min(sh_u[2], (uint32_t)r) : 0u;
-    const uint32_t C =
-        r > 0 ? (uint32_t)min((int64_t)sh_u[3], spill_stride > kCandCap ? spill_stride : (int64_t)kCandCap) : 0u;
+    // Lists built from the same scores as the histogram give D < r <= D + C;
+    // the clamps only keep every index in bounds.
+    const uint32_t D = min(tot_d, (uint32_t)r);
+    const uint32_t C = (uint32_t)min((int64_t)tot_c, spill_stride);
     const uint32_t need = min((uint32_t)r - D, C);
+    uint64_t *spill_b = spill + (int64_t)b * spill_stride;
+    for (uint32_t p = tid; p < D; p += kThreads) {
+        const int s = slot_of(off_d, ns, p);
+        defl[p] = slot_def[((int64_t)b * n_slices + s) * kSliceBlocks + (p - off_d[s])];
+    }
+    for (uint32_t p = tid; p < C; p += kThreads) {
+        const int s = slot_of(off_c, ns, p);
+        const uint64_t c = slot_cand[((int64_t)b * n_slices + s) * kSliceBlocks + (p - off_c[s])];
+        if (p < (uint32_t)kCandCap)
+            cand[p] = c;
+        else
+            spill_b[p] = c;          // read back below by this workgroup only
+    }
+    __syncthreads();
 
-    // ---- 3a. threshold composite T64: chosen(i) <=> comp_i >= T64 -----------
+    // ---- choose: threshold composite T64, chosen(i) <=> comp_i >= T64 -------
+    // Radix select over the composites below the shared 12-bit bin, 11 bits
+    // at a time: each pass histograms the next digit of the candidates that
+    // still match the prefix and keeps the bin where the count of larger ones
+    // crosses `want`. A pass usually isolates the answer (a 12-bit bin spreads
+    // its few hundred candidates over the next 11 bits); once the crossing bin
+    // holds exactly the items still wanted, or few enough, it finishes at once.
     uint64_t T64 = ~0ull;
     if (need > 0 && need == C) {
         T64 = 0;
-    } else if (need > 0 && C <= (uint32_t)kCandCap) {
-        for (uint32_t i = tid; i < C; i += kThreads) {
-            const uint64_t ci = cand[i];
-            uint32_t rank = 0;
-            for (uint32_t j = 0; j < C; j++)
-                rank += cand[j] > ci ? 1u : 0u;
-            if (rank == need - 1) {     // the need-th largest composite
-                sh_u[4] = (uint32_t)(ci >> 32);
-                sh_u[5] = (uint32_t)ci;
-            }
-        }
-        __syncthreads();
-        T64 = ((uint64_t)sh_u[4] << 32) | sh_u[5];
     } else if (need > 0) {
-        // Radix select over bits [51:0] in 4 passes of 13 bits (the top 12
-        // bits are b* for every candidate).
-        uint64_t prefix = (uint64_t)bstar << 52;
+        auto cand_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandCap ? cand[i] : spill_b[i]; };
         uint64_t pmask = 0xFFFull << 52;
+        uint64_t prefix = cand[0] & pmask;
         uint32_t want = need;
-        for (int shift = 52 - kRadixBits; shift >= 0; shift -= kRadixBits) {
-            for (int i = tid; i < kRadixBins; i += kThreads)
-                work[i] = 0;
+        int shift = 52;
+        uint32_t *h = work;                         // 2048-bin histogram
+        bool done = false;
+        while (!done) {
+            const int bits = shift >= kDigitBits ? kDigitBits : shift;
+            shift -= bits;
+            const uint32_t dmask = (1u << bits) - 1u;
+            for (int i = tid; i < kDigitBins; i += kThreads)
+                h[i] = 0;
             __syncthreads();
             for (uint32_t i = tid; i < C; i += kThreads) {
-                const uint64_t c = i < (uint32_t)kCandCap ? cand[i] : spill_b[i];
+                const uint64_t c = cand_at(i);
                 if ((c & pmask) == prefix)
-                    atomicAdd(&work[(c >> shift) & (kRadixBins - 1)], 1u);
+                    atomicAdd(&h[(c >> shift) & dmask], 1u);
             }
             __syncthreads();
-            find_crossing<kRadixBins / kThreads>(work, want, sh_scan, &sh_u[0], &sh_u[1]);
-            const uint64_t digit = sh_u[0];
+            find_crossing<kDigitBins / kThreads, kThreads>(h, want, sh_scan, &sh_u[0], &sh_u[1]);
+            const uint32_t digit = sh_u[0];
+            const uint32_t in_bin = h[digit];
             want -= sh_u[1];
-            prefix |= digit << shift;
-            pmask |= (uint64_t)(kRadixBins - 1) << shift;
+            prefix |= (uint64_t)digit << shift;
+            pmask |= (uint64_t)dmask << shift;
+            if (in_bin == want || shift == 0) {
+                // every remaining match is chosen (or the prefix is complete)
+                T64 = prefix;
+                done = true;
+            } else if (in_bin <= (uint32_t)kThreads) {
+                // few left: rank them directly, one thread each
+                uint32_t *lst_n = &sh_u[2];
+                uint64_t *lst = reinterpret_cast<uint64_t *>(work + kDigitBins);   // [kThreads]
+                if (tid == 0)
+                    *lst_n = 0;
+                __syncthreads();
+                for (uint32_t i = tid; i < C; i += kThreads) {
+                    const uint64_t c = cand_at(i);
+                    if ((c & pmask) == prefix)
+                        lst[atomicAdd(lst_n, 1u)] = c;
+                }
+                __syncthreads();
+                const uint32_t m = *lst_n;
+                if (tid < m) {
+                    const uint64_t ci = lst[tid];
+                    uint32_t rank = 0;
+                    for (uint32_t j = 0; j < m; j++)
+                        rank += lst[j] > ci ? 1u : 0u;
+                    if (rank == want - 1) {         // the want-th largest of the bin
+                        sh_u[4] = (uint32_t)(ci >> 32);
+                        sh_u[5] = (uint32_t)ci;
+                    }
+                }
+                __syncthreads();
+                T64 = ((uint64_t)sh_u[4] << 32) | sh_u[5];
+                done = true;
+            }
             __syncthreads();
         }
-        T64 = prefix;
     }
 
-    // ---- 3b. ascending output through a bitmap, segment by segment ----------
+    // ---- ascending output through a bitmap, segment by segment -------------
     uint32_t *bm = work;
     uint32_t written = 0;
+    const int s_end = min(sink_blocks, n);
+    const int t_begin = max(tail_first, s_end);
     for (int seg0 = 0; seg0 < n; seg0 += kSegBlocks) {
         const int seg1 = min(seg0 + kSegBlocks, n);
         const int nw = (seg1 - seg0 + 31) / 32;
@@ -266,10 +370,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         for (int i = tid; i < nw; i += kThreads)
             bm[i] = 0;
         __syncthreads();
-        const int s_end = min(sink_blocks, n);
-        for (int j = seg0 + tid; j < seg1; j += kThreads)
-            if (j < s_end || j >= tail_first)
-                atomicOr(&bm[(j - seg0) >> 5], 1u << ((j - seg0) & 31));
+        // forced blocks: [0, s_end) and [t_begin, n)
+        for (int j = seg0 + tid; j < min(seg1, s_end); j += kThreads)
+            atomicOr(&bm[(j - seg0) >> 5], 1u << ((j - seg0) & 31));
+        for (int j = max(seg0, t_begin) + tid; j < seg1; j += kThreads)
+            atomicOr(&bm[(j - seg0) >> 5], 1u << ((j - seg0) & 31));
         for (uint32_t i = tid; i < D; i += kThreads) {
             const int j = defl[i];
             if (j >= seg0 && j < seg1)
@@ -296,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         for (int i = w0; i < w1; i++)
             cnt += __popc(bm[i]);
         uint32_t total;
-        uint32_t pos = written + block_inclusive_scan(cnt, sh_scan, &total) - cnt;
+        uint32_t pos = written + block_inclusive_scan<kThreads>(cnt, sh_scan, &total) - cnt;
         for (int i = w0; i < w1; i++) {
             uint32_t m = bm[i];
             while (m) {
@@ -312,10 +417,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     for (int p = (int)written + tid; p < K; p += kThreads)
         sel_b[p] = -1;
     if (tid == 0) {
-        const int ns = (int)min(written, (uint32_t)K);
-        n_sel[b] = ns;
+        const int nsel = (int)min(written, (uint32_t)K);
+        n_sel[b] = nsel;
         if (n_tok) {
-            int nt = ns * kBT;
+            int nt = nsel * kBT;
             const int last_len = L - (n - 1) * kBT;
             if (last_len < kBT && sh_u[6])
                 nt -= kBT - last_len;     // the partial last block is selected
@@ -330,9 +435,20 @@ hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int
                          int max_ctx, const SelectWs &ws, int budget_blocks, int sink_blocks, int tail_tokens,
                          int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s)
 {
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)batch), dim3(kThreads), kSmemBytes, s, block_scores, bs_stride,
-                       ctx_len, max_ctx, ws.hist, ws.cand, ws.cand_stride, budget_blocks, sink_blocks, tail_tokens,
-                       sel, n_sel, n_tok);
+    const int n_blk_max = (max_ctx + kBT - 1) / kBT;
+    const int n_slices = n_blk_max > 0 ? (n_blk_max + kSliceBlocks - 1) / kSliceBlocks : 1;
+    if (n_blk_max > budget_blocks) {
+        dim3 grid((unsigned)n_slices, (unsigned)batch);
+        hipLaunchKernelGGL(collect_kernel, grid, dim3(kCollectThreads), 0, s, block_scores, bs_stride, ctx_len,
+                           max_ctx, ws.hist, ws.slot_count, ws.slot_def, ws.slot_cand, n_slices, budget_blocks,
+                           sink_blocks, tail_tokens);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)batch), dim3(kThreads), kSmemBytes, s, ctx_len, max_ctx,
+                       ws.slot_count, ws.slot_def, ws.slot_cand, n_slices, ws.spill, ws.spill_stride, budget_blocks,
+                       sink_blocks, tail_tokens, sel, n_sel, n_tok);
     return hipGetLastError();
 }
 
