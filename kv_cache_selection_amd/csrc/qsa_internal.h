@@ -27,7 +27,7 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 
 // Attention: tokens per split.
-constexpr int kTPS = 64;
+constexpr int kTPS = 128;
 
 // Monotone map of a float to uint32: a < b  <=>  key(a) < key(b); -0.0 maps
 // to the key of +0.0 so that the two compare equal, as floats do.
