@@ -11,11 +11,26 @@ paged attention -> merge) through the C ABI; the metric is layer-steps/s.
 Prints one JSON line with the driver's fields plus:
   roofline      the dominant kernel (index scoring): algorithmic bytes per
                 launch / its average duration, timed with HIP events recorded
-                on the compute stream around each scoring launch;
+                on the compute stream around each scoring launch, with the
+                steps run on one stream so that each launch has the GPU alone;
+  one_stream    the step time with every kernel in order on one stream;
   step_hbm      the whole step's algorithmic bytes (index scan + gathered
                 rows) over the step time, against the same HBM peak;
   cpu_baseline  the CPU oracle, single-threaded, on a sample of (layer,
                 sequence) units of the same workload, scaled to layer-steps/s.
+
+The roofline's "traffic" comes from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+summarised in profiles/ (see --pmc-summary); it is reported only while the
+scoring kernel's source is the one those counters were taken on.
+
+Helper modes for the profiles (no benchmark run):
+  --copy-calibration      a plain 256 MiB device-to-device copy, three times:
+                          the known-size kernel that calibrates the counters;
+  --stats-summary CSV     a short table of a rocprofv3 kernel_stats.csv;
+  --pmc-summary F W CF CW summarise four rocprofv3 counter_collection.csv
+                          files (bench FETCH_SIZE, bench WRITE_SIZE, copy
+                          FETCH_SIZE, copy WRITE_SIZE) into the text file that
+                          this script reads back.
 """
 from __future__ import annotations
 
@@ -30,6 +45,127 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SCORE_KERNEL = "index_score_kernel"
+SCORE_SOURCES = ("kv_cache_selection_amd/csrc/index_score.hip", "kv_cache_selection_amd/csrc/qsa_internal.h")
+COPY_BYTES = 1 << 28
+
+
+def pmc_file(workload):
+    return os.path.join(ROOT, "profiles", "%s.%s.pmc.txt" % (SCORE_KERNEL, workload))
+
+
+def score_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in SCORE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_counter_csv(path):
+    """{kernel name: [counter values]} from a rocprofv3 counter_collection.csv
+    (one row per dispatch and counter)."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            low = {k.lower(): v for k, v in row.items()}
+            name = low.get("kernel_name") or low.get("kernel-name") or ""
+            out.setdefault(name, []).append(float(low["counter_value"]))
+    return out
+
+
+def pmc_summary(paths, workload):
+    """Text summary of the four counter passes: KiB per dispatch for every
+    kernel, the copy calibration factors and the scoring kernel's HBM bytes."""
+    fetch, write, cfetch, cwrite = (read_counter_csv(p) for p in paths)
+
+    def biggest(d):
+        # the calibration copy is the only large dispatch of its run
+        return max(v for vals in d.values() for v in vals)
+
+    f_fetch = COPY_BYTES / (biggest(cfetch) * 1024.0)
+    f_write = COPY_BYTES / (biggest(cwrite) * 1024.0)
+    lines = ["# HBM traffic per dispatch from rocprofv3 counters, workload %s" % workload,
+             "# four passes, each its own run (cd /tmp && export TMPDIR=/tmp first), C in FETCH_SIZE WRITE_SIZE:",
+             "#   rocprofv3 --pmc C --kernel-trace -f csv -d OUT_C -o run -- python3 bench.py --steps 2 --warmup 1 "
+             "--cpu-seconds 0",
+             "#   rocprofv3 --pmc C --kernel-trace -f csv -d COPY_C -o run -- python3 bench.py --copy-calibration",
+             "# summary: python3 bench.py --pmc-summary OUT_FETCH_SIZE/run_counter_collection.csv "
+             "OUT_WRITE_SIZE/run_counter_collection.csv COPY_FETCH_SIZE/run_counter_collection.csv "
+             "COPY_WRITE_SIZE/run_counter_collection.csv",
+             "# the copy moves %d bytes each way: its FETCH_SIZE and WRITE_SIZE readings give the KiB-to-byte "
+             "factors" % COPY_BYTES,
+             "kernel: %s" % SCORE_KERNEL,
+             "source_sha256: %s" % score_source_hash(),
+             "fetch_factor: %.4f" % f_fetch,
+             "write_factor: %.4f" % f_write]
+    score = None
+    rows = []
+    for name in sorted(set(fetch) | set(write)):
+        fv, wv = fetch.get(name, []), write.get(name, [])
+        fk = sum(fv) / len(fv) if fv else 0.0
+        wk = sum(wv) / len(wv) if wv else 0.0
+        byt = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
+        rows.append((byt, name, len(fv), fk, wk))
+        if SCORE_KERNEL in name:
+            score = byt
+    if score is None:
+        raise SystemExit("no %s dispatch in the counter files" % SCORE_KERNEL)
+    lines.append("traffic_bytes_per_launch: %d" % round(score))
+    lines.append("")
+    lines.append("%14s %8s %14s %14s  %s" % ("bytes/dispatch", "dispatch", "FETCH KiB", "WRITE KiB", "kernel"))
+    for byt, name, n, fk, wk in sorted(rows, reverse=True):
+        lines.append("%14d %8d %14.1f %14.1f  %s" % (byt, n, fk, wk, name[:110]))
+    return "\n".join(lines) + "\n"
+
+
+def stats_summary(path, workload):
+    """Short text table of a rocprofv3 --stats kernel_stats.csv."""
+    import csv
+    lines = ["# rocprofv3 kernel statistics of the default benchmark run, workload %s" % workload,
+             "# command (cd /tmp && export TMPDIR=/tmp first):",
+             "#   rocprofv3 --kernel-trace --stats -f csv -d OUT -o run -- python3 bench.py",
+             "# summary: python3 bench.py --stats-summary OUT/run_kernel_stats.csv",
+             "# averages over every launch of the run (warm-up, the two-stream steps and the two one-stream",
+             "# regions); under the tracer the two streams hardly overlap, so they match the one-stream timing",
+             "",
+             "%8s %12s %10s %10s %10s %7s  %s" % ("calls", "total ms", "avg us", "min us", "max us", "%", "kernel")]
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            lines.append("%8s %12.3f %10.2f %10.2f %10.2f %7.2f  %s" % (
+                r["Calls"], float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"]), r["Name"][:110]))
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(workload):
+    """The scoring kernel's measured HBM bytes per launch, or None when there
+    is no summary for this workload or the kernel changed since."""
+    path = pmc_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != score_source_hash() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
 class HipEvents:
@@ -73,34 +209,41 @@ def tokens_selected(sel, ns, ctx):
     return out
 
 
-def cpu_baseline(wl, hi, units):
-    """Oracle time per (layer, sequence) unit, single thread; input generation
-    excluded. Returns layer-steps/s = 1 / (batch * mean unit time)."""
+def cpu_baseline(wl, hi, seconds):
+    """The oracle, single-threaded, on (layer, sequence) units of the workload
+    taken in order (layer 0's sequences first) until about `seconds` of oracle
+    time have run. Input generation (the host C generator) is excluded.
+    Returns layer-steps/s = 1 / (batch * mean unit time)."""
     import numpy as np
     import oracle
     import qsa_synth as S
+    from qsa_synth import host as SH
     g = S.GEOM
     K = wl.budget // g.block_tokens
-    times = []
-    for (l, b) in units:
-        L = int(hi.lay.ctx[b])
-        keys, sig = S.index_keys(wl.seed, l, b, 0, L, hi.lay.planted[(l, b)], hi.u[l, b])
-        t0 = time.perf_counter()
-        ts = oracle.token_scores(keys, sig, hi.q_idx[l, b], hi.w[l, b])
-        bs = oracle.block_scores(ts, g.block_tokens)
-        sel = oracle.select_blocks(bs, K, oracle.forced_mask(L, g.block_tokens, wl.sink_blocks, wl.tail_tokens))
-        toks = oracle.tokens_of_blocks(L, sel.blocks, g.block_tokens)
-        t1 = time.perf_counter()
-        rows = S.kv_rows(wl.seed, l, hi.lay.pt[b, toks])          # input generation, not timed
-        t2 = time.perf_counter()
-        oracle.attention(np.arange(len(toks)), None, rows, hi.q[l, b], g.n_kv_heads, g.sm_scale)
-        t3 = time.perf_counter()
-        times.append((t1 - t0) + (t3 - t2))
+    times, units = [], []
+    for l in range(wl.layers):
+        for b in range(wl.batch):
+            if sum(times) >= seconds:
+                break
+            L = int(hi.lay.ctx[b])
+            keys, sig = SH.index_keys(wl.seed, l, b, 0, L, hi.lay.planted[(l, b)], hi.u[l, b])
+            t0 = time.perf_counter()
+            ts = oracle.token_scores(keys, sig, hi.q_idx[l, b], hi.w[l, b])
+            bs = oracle.block_scores(ts, g.block_tokens)
+            sel = oracle.select_blocks(bs, K, oracle.forced_mask(L, g.block_tokens, wl.sink_blocks, wl.tail_tokens))
+            toks = oracle.tokens_of_blocks(L, sel.blocks, g.block_tokens)
+            t1 = time.perf_counter()
+            rows = SH.kv_rows(wl.seed, l, hi.lay.pt[b, toks])          # input generation, not timed
+            t2 = time.perf_counter()
+            oracle.attention(np.arange(len(toks)), None, rows, hi.q[l, b], g.n_kv_heads, g.sm_scale)
+            t3 = time.perf_counter()
+            times.append((t1 - t0) + (t3 - t2))
+            units.append((l, b))
     mean = sum(times) / len(times)
     return {"value": 1.0 / (wl.batch * mean), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
-            "sample": "%d (layer, sequence) units of %s (%s), single-threaded C oracle in fp64: "
-                      "%.2f s per unit; a layer-step is %d units; input generation excluded"
-                      % (len(units), wl.name, ", ".join("l%d/b%d" % u for u in units), mean, wl.batch)}
+            "sample": "%d (layer, sequence) units of %s (layers %d-%d, %.1f s of oracle time), single-threaded "
+                      "C oracle in fp64: %.3f s per unit, and a layer-step is %d units; input generation excluded"
+                      % (len(units), wl.name, units[0][0], units[-1][0], sum(times), mean, wl.batch)}
 
 
 def main():
@@ -109,10 +252,23 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="batch8-256k")
-    ap.add_argument("--cpu-units", type=int, default=2, help="oracle units in the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time spent on the CPU baseline (0: skip)")
     ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
                     help="2: overlap layers on a second stream (default); 1: every kernel in order on one stream")
+    ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--pmc-summary", nargs=4, metavar="CSV", help=argparse.SUPPRESS)
+    ap.add_argument("--stats-summary", metavar="CSV", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.stats_summary:
+        sys.stdout.write(stats_summary(args.stats_summary, args.workload))
+        return
+    if args.pmc_summary:
+        sys.stdout.write(pmc_summary(args.pmc_summary, args.workload))
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the QSA decode step runs on a single MI355X and this build has "
               "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -168,13 +324,27 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # Timed region 2: the same steps with HIP events around every scoring launch.
+    # Timed region 2: the same steps with every kernel in order on one stream (each layer's
+    # score -> select -> attention -> merge before the next layer starts).
+    ms_serial = None
+    if copy is not None:
+        e0.record(stream)
+        for _ in range(args.steps):
+            qsa.qsa_decode_step(cfg, bt, plain, loc, ws, nws, stream, None)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_serial = e0.elapsed_time(e1) / args.steps
+
+    # Timed region 3: the same steps on one stream with HIP events around
+    # every scoring launch, so that each launch is timed on its own (as a
+    # kernel-trace profile of this script sees it) rather than sharing the
+    # GPU with the previous layer's selection and attention.
     hev = HipEvents()
     evs = [(hev.create(), hev.create()) for _ in range(NL)]
     timed = layers(evs)
     durs = []
     for _ in range(args.steps):
-        step(timed)
+        qsa.qsa_decode_step(cfg, bt, timed, loc, ws, nws, stream, None)
         torch.cuda.synchronize()
         durs.extend(hev.elapsed_ms(a, b) for (a, b) in evs)
     score_ms = float(np.mean(durs))
@@ -205,14 +375,15 @@ def main():
                    "kv": "host-pinned" if di.kv_host else "hbm", "streams": args.streams},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": idx_bytes_launch,
+                     "traffic": read_traffic(wl.name), "bytes_per_launch": idx_bytes_launch,
                      "avg_launch_us": round(score_ms * 1e3, 2)},
+        "one_stream": {"ms_per_step": round(ms_serial if ms_serial is not None else ms_step, 4),
+                       "value": round(NL / ((ms_serial if ms_serial is not None else ms_step) * 1e-3), 2)},
         "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes},
     }
-    if args.cpu_units > 0:
-        units = [(0, b) for b in range(min(args.cpu_units, wl.batch))]
-        result["cpu_baseline"] = cpu_baseline(wl, di.hi, units)
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, di.hi, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

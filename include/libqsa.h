@@ -161,9 +161,9 @@ typedef struct {
     float *out;                 /* [B][n_q_heads][head_dim] */
     int32_t *sel_blocks;        /* optional [B][K] copy of the selection, or NULL */
     int32_t *n_sel;             /* optional [B], or NULL */
-    void *score_events[2];      /* optional pair of timing-enabled hipEvent_t, recorded on the
-                                   compute stream just before and just after this layer's
-                                   index-scoring kernel; NULL to skip */
+    void *score_events[2];      /* optional pair of timing-enabled hipEvent_t that take the begin
+                                   and end timestamps of this layer's index-scoring kernel (it is
+                                   then launched through hipExtLaunchKernel); NULL to skip */
 } qsa_layer_t;
 
 /* The whole decode step over n_layers independent QSA layers: for each layer,

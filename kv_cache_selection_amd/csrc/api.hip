@@ -376,16 +376,10 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     }
     auto score = [&](int l, hipStream_t s) {
         const qsa_layer_t &Ly = layers[l];
-        hipError_t r = hipSuccess;
-        if (Ly.score_events[0])
-            r = hipEventRecord((hipEvent_t)Ly.score_events[0], s);
-        if (r == hipSuccess)
-            r = launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
-                                   batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.hist,
-                                   K, cfg->sink_blocks, cfg->tail_tokens, s);
-        if (r == hipSuccess && Ly.score_events[1])
-            r = hipEventRecord((hipEvent_t)Ly.score_events[1], s);
-        return r;
+        return launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
+                                  batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.hist, K,
+                                  cfg->sink_blocks, cfg->tail_tokens, s, (hipEvent_t)Ly.score_events[0],
+                                  (hipEvent_t)Ly.score_events[1]);
     };
     auto select = [&](int l, hipStream_t s) {
         return launch_select(lw[l].bs, bs_stride, batch->ctx_len, B, batch->max_ctx, lw[l].sw, K, cfg->sink_blocks,

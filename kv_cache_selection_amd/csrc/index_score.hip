@@ -29,6 +29,8 @@
 // never re-reads the scores just to count them.
 #include "qsa_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace qsa {
 namespace {
 
@@ -237,10 +239,22 @@ hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
+// With a start/stop event pair the launch goes through hipExtLaunchKernel,
+// whose events take the kernel's own begin and end timestamps.
+template <typename Kernel, typename... Args>
+void launch_timed(Kernel k, dim3 grid, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, Args... args)
+{
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, ev0, ev1, 0, args...);
+    else
+        hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, args...);
+}
+
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
-                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s)
+                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s,
+                              hipEvent_t ev0, hipEvent_t ev1)
 {
     if (max_ctx <= 0)
         return hipSuccess;
@@ -250,25 +264,20 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
     while (chunk < 4096 && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 1024)
         chunk *= 2;
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)batch);
+#define QSA_SCORE_ARGS keys, scales, q_idx, w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, \
+                       bs_stride, hist, budget_blocks, sink_blocks, tail_tokens
     if (token_scores) {
         if (hist)
-            hipLaunchKernelGGL((index_score_kernel<true, true>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
-                               budget_blocks, sink_blocks, tail_tokens);
+            launch_timed(index_score_kernel<true, true>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
         else
-            hipLaunchKernelGGL((index_score_kernel<true, false>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
-                               budget_blocks, sink_blocks, tail_tokens);
+            launch_timed(index_score_kernel<true, false>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
     } else {
         if (hist)
-            hipLaunchKernelGGL((index_score_kernel<false, true>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
-                               budget_blocks, sink_blocks, tail_tokens);
+            launch_timed(index_score_kernel<false, true>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
         else
-            hipLaunchKernelGGL((index_score_kernel<false, false>), grid, dim3(kThreads), 0, s, keys, scales, q_idx,
-                               w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, bs_stride, hist,
-                               budget_blocks, sink_blocks, tail_tokens);
+            launch_timed(index_score_kernel<false, false>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
     }
+#undef QSA_SCORE_ARGS
     return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
-                              hipStream_t s);
+                              hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
                              int max_ctx, uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,

@@ -100,3 +100,29 @@ def test_ragged_lengths_in_range():
     wl = S.WORKLOADS["batch8-short"]
     ctx = S.ctx_lengths(wl)
     assert len(ctx) == 8 and ctx.min() >= 3072 and ctx.max() <= 4608 and len(set(ctx.tolist())) > 1
+
+
+def test_host_c_generator_matches_numpy():
+    """The C version of the two large streams gives the numpy generator's bytes:
+    index keys over a stretch that crosses planted blocks and a ragged end, KV
+    rows at scattered slots, and the float32 -> float16 rounding of the scale
+    against numpy's own conversion (normal, subnormal, overflow edges)."""
+    from qsa_synth import host as SH
+    SH.build(force=False)
+    wl = S.WORKLOADS["batch8-256k"]
+    hi = S.host_inputs(wl)
+    for (l, b) in [(0, 0), (7, 3)]:
+        pl = hi.lay.planted[(l, b)]
+        for t0, t1 in [(0, 700), (int(pl[0]) * 4 - 37, int(pl[0]) * 4 + 541), (262144 - 301, 262144)]:
+            c1, s1 = S.index_keys(wl.seed, l, b, t0, t1, pl, hi.u[l, b])
+            c2, s2 = SH.index_keys(wl.seed, l, b, t0, t1, pl, hi.u[l, b])
+            assert np.array_equal(c1, c2) and np.array_equal(s1, s2), (l, b, t0)
+    slots = np.array([0, 1, 4095, 123457, 2**21 - 1])
+    assert np.array_equal(S.kv_rows(wl.seed, 5, slots), SH.kv_rows(wl.seed, 5, slots))
+    x = np.abs(np.random.default_rng(7).standard_normal(20000).astype(np.float32)) * np.float32(0.02)
+    edges = np.float32([0.0, 1e-9, 2.0**-25, 3 * 2.0**-26, 2.0**-14, 2.0**-14 * 0.99, 65504, 65519.99, 65520, 7e4])
+    x = np.concatenate([x, edges])
+    got = np.array([SH.f32_to_f16_bits(float(v)) for v in x], np.uint16)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
