@@ -128,8 +128,8 @@ def stats_summary(path, workload):
              "# command (cd /tmp && export TMPDIR=/tmp first):",
              "#   rocprofv3 --kernel-trace --stats -f csv -d OUT -o run -- python3 bench.py",
              "# summary: python3 bench.py --stats-summary OUT/run_kernel_stats.csv",
-             "# averages over every launch of the run (warm-up, the two-stream steps and the two one-stream",
-             "# regions); under the tracer the two streams hardly overlap, so they match the one-stream timing",
+             "# averages over every launch of the run (warm-up, the overlapped steps and the two one-stream",
+             "# regions); under the tracer the streams hardly overlap, so they match the one-stream timing",
              "",
              "%8s %12s %10s %10s %10s %7s  %s" % ("calls", "total ms", "avg us", "min us", "max us", "%", "kernel")]
     with open(path, newline="") as f:
@@ -254,8 +254,8 @@ def main():
     ap.add_argument("--workload", default="batch8-256k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time spent on the CPU baseline (0: skip)")
-    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
-                    help="2: overlap layers on a second stream (default); 1: every kernel in order on one stream")
+    ap.add_argument("--side-streams", type=int, default=3,
+                    help="side streams of the overlapped schedule (default 3); 0: every kernel in order on one stream")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=4, metavar="CSV", help=argparse.SUPPRESS)
     ap.add_argument("--stats-summary", metavar="CSV", help=argparse.SUPPRESS)
@@ -298,8 +298,8 @@ def main():
     nws = qsa.qsa_workspace_size(cfg, di.batch, di.max_ctx, NL, loc)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    # select/attention (HBM pools) or the PCIe gather (host pools) overlap the scoring on a second stream
-    copy = torch.cuda.Stream() if args.streams == 2 else None
+    # select/attention (HBM pools) or the PCIe gather (host pools) overlap the scoring on side streams
+    side = [torch.cuda.Stream() for _ in range(args.side_streams)]
 
     def layers(events=None):
         return [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l], di.out[l],
@@ -308,7 +308,7 @@ def main():
     plain = layers()
 
     def step(lys):
-        qsa.qsa_decode_step(cfg, bt, lys, loc, ws, nws, stream, copy)
+        qsa.qsa_decode_step(cfg, bt, lys, loc, ws, nws, stream, side)
 
     for _ in range(args.warmup):
         step(plain)
@@ -327,7 +327,7 @@ def main():
     # Timed region 2: the same steps with every kernel in order on one stream (each layer's
     # score -> select -> attention -> merge before the next layer starts).
     ms_serial = None
-    if copy is not None:
+    if side:
         e0.record(stream)
         for _ in range(args.steps):
             qsa.qsa_decode_step(cfg, bt, plain, loc, ws, nws, stream, None)
@@ -372,7 +372,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 generator; planted relevant blocks)",
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(ctx.max()), "layers": NL,
                    "budget_tokens": wl.budget, "sink_blocks": wl.sink_blocks, "tail_tokens": wl.tail_tokens,
-                   "kv": "host-pinned" if di.kv_host else "hbm", "streams": args.streams},
+                   "kv": "host-pinned" if di.kv_host else "hbm", "side_streams": args.side_streams},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(wl.name), "bytes_per_launch": idx_bytes_launch,

@@ -171,20 +171,27 @@ typedef struct {
  * fused into attention (rows are read through the page table in place). With
  * QSA_KV_HOST_PINNED the selected rows are copied over PCIe into a
  * double-buffered staging area.
- * Streams: with a second stream (`copy`, distinct from `compute`) layers
- * overlap -- HBM pools: the compute stream scores layer after layer while
- * `copy` selects and attends layer l under the scoring of layer l+1; host
- * pools: `copy` gathers layer l over PCIe while `compute` scores layer l+1.
+ * Streams: `side` holds n_side extra streams (all distinct from `compute`);
+ * with n_side = 0 (side may then be NULL) every kernel runs in order on
+ * `compute`. With side streams the layers overlap:
+ *   - HBM pools: `compute` scores layer after layer; layer l's selection,
+ *     attention and merge run on side[l % n_side] as soon as its scores exist,
+ *     so they hide under the scoring of the following layers (this treats the
+ *     layers as independent, which they are within one call);
+ *   - host pools: side[0] gathers layer l over PCIe while `compute` scores
+ *     and selects layer l+1 and attends layer l-1 (further side streams are
+ *     not used).
  * The call leaves `compute` ordered after all of its work, so a sync on
- * `compute` covers the step. copy = NULL (or == compute) serialises every
- * kernel on `compute`; results are bit-identical either way. The two-stream
- * schedule records events owned by the library (one set per device): do not
- * run two-stream decode steps concurrently from several host threads on one
- * device.
+ * `compute` covers the step. Results are bit-identical for every schedule.
+ * The overlapped schedules record events owned by the library (one set per
+ * device): do not run them concurrently from several host threads on one
+ * device. n_side is at most QSA_MAX_SIDE_STREAMS.
  * Workspace: qsa_workspace_size(cfg, B, max_ctx, n_layers, kv_location). */
+#define QSA_MAX_SIDE_STREAMS 8
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
-                             size_t workspace_bytes, qsa_stream_t compute, qsa_stream_t copy);
+                             size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
+                             int32_t n_side);
 
 /* Workspace bytes needed by qsa_decode_step (n_layers >= 1); the same call
  * with n_layers = 1 covers qsa_topk_blocks and qsa_sparse_decode. */

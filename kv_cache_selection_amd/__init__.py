@@ -63,7 +63,8 @@ def _load():
     lib.qsa_topk_blocks.argtypes = [CP, BP, P, i64, P, P, P, P, sz, P]
     lib.qsa_gather_kv.argtypes = [CP, BP, P, P, P, i32, P, P, P]
     lib.qsa_sparse_decode.argtypes = [CP, i32, P, P, P, P, P, sz, P]
-    lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P, P]
+    lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P,
+                                    ctypes.POINTER(ctypes.c_void_p), i32]
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step"):
         getattr(lib, f).restype = i32
     lib.qsa_workspace_size.argtypes = [CP, i32, i32, i32, i32]
@@ -166,9 +167,17 @@ def make_layer(idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, out, page_table=N
     return lay
 
 
-def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, copy=None):
+def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, side=None):
+    """`side`: None, one stream, or a sequence of streams (the side streams of
+    the overlapped schedules); None or an empty sequence serialises the step
+    on `compute`."""
     # the array copies the structs; `layers` keeps the tensors they point to alive
     arr = (Layer * len(layers))(*layers)
+    if side is None:
+        side = ()
+    elif not isinstance(side, (list, tuple)):
+        side = (side,)
+    sarr = (ctypes.c_void_p * max(len(side), 1))(*[_stream(x) for x in side])
     _check("qsa_decode_step", lib.qsa_decode_step(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
                                                   kv_location, _p(workspace), workspace_bytes, _stream(compute),
-                                                  _stream(copy)))
+                                                  sarr if side else None, len(side)))

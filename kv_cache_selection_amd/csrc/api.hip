@@ -314,7 +314,8 @@ qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uin
 
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
-                             size_t workspace_bytes, qsa_stream_t compute, qsa_stream_t copy)
+                             size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
+                             int32_t n_side)
 {
     qsa_status_t st = check_config(cfg);
     if (st != QSA_OK)
@@ -330,6 +331,15 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             !aligned(L.idx_keys, 16) || !aligned(L.q_idx, 8) || !aligned(L.kv_pool, 16))
             return QSA_ERR_INVALID_ARGUMENT;
     }
+    if (n_side < 0 || n_side > QSA_MAX_SIDE_STREAMS || (n_side > 0 && !side))
+        return QSA_ERR_INVALID_ARGUMENT;
+    for (int k = 0; k < n_side; k++) {
+        if (side[k] == compute)
+            return QSA_ERR_INVALID_ARGUMENT;
+        for (int k2 = 0; k2 < k; k2++)
+            if (side[k] == side[k2])
+                return QSA_ERR_INVALID_ARGUMENT;
+    }
     const WsLayout w = make_layout(cfg, batch->batch, batch->max_ctx, n_layers, kv_location);
     if (workspace_bytes < w.total)
         return QSA_ERR_WORKSPACE_TOO_SMALL;
@@ -341,11 +351,12 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     }
 
     hipStream_t sc = (hipStream_t)compute;
-    hipStream_t sx = (hipStream_t)copy;
     const bool offload = kv_location == QSA_KV_HOST_PINNED;
-    const bool two_streams = copy != nullptr && copy != compute;
+    const bool two_streams = n_side > 0;
+    const int NS = offload ? (n_side > 0 ? 1 : 0) : n_side;
+    hipStream_t sx = NS > 0 ? (hipStream_t)side[0] : nullptr;
     std::vector<hipEvent_t> ev;
-    if (two_streams && (st = get_events(3 * n_layers + 1, ev)) != QSA_OK)
+    if (two_streams && (st = get_events(3 * n_layers + NS, ev)) != QSA_OK)
         return st;
 
     const int B = batch->batch;
@@ -419,24 +430,28 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
 
     if (!offload) {
         // Pools in HBM: the compute stream streams the index of layer after
-        // layer; the second stream selects and attends layer l as soon as its
-        // scores exist, under the scoring of layer l+1.
+        // layer; layer l's selection and attention run on side stream
+        // l % NS as soon as its scores exist, under the scoring of the next
+        // layers. Several side streams let the latency-bound chains of
+        // consecutive layers overlap one another too.
         for (int l = 0; l < n_layers && e == hipSuccess; l++) {
+            hipStream_t sy = (hipStream_t)side[l % NS];
             e = score(l, sc);
             if (e == hipSuccess)
                 e = hipEventRecord(ev[l], sc);
             if (e == hipSuccess)
-                e = hipStreamWaitEvent(sx, ev[l], 0);
+                e = hipStreamWaitEvent(sy, ev[l], 0);
             if (e == hipSuccess)
-                e = select(l, sx);
+                e = select(l, sy);
             if (e == hipSuccess)
-                e = attend_paged(l, sx);
+                e = attend_paged(l, sy);
         }
-        // The caller synchronises on the compute stream: join the second one.
-        if (e == hipSuccess)
-            e = hipEventRecord(ev[3 * n_layers], sx);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(sc, ev[3 * n_layers], 0);
+        // The caller synchronises on the compute stream: join the side streams.
+        for (int k = 0; k < NS && k < n_layers && e == hipSuccess; k++) {
+            e = hipEventRecord(ev[3 * n_layers + k], (hipStream_t)side[k]);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(sc, ev[3 * n_layers + k], 0);
+        }
         return hip_status(e);
     }
 

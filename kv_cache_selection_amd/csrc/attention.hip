@@ -43,20 +43,6 @@ constexpr int kWaveTok = kTile * kTiles;           // 32
 static_assert(kWaves * kWaveTok == kTPS, "tokens per split");
 constexpr int kKBytes = kDh * 2;                   // 512 bytes of K (or V) per head per row
 
-template <bool kPaged>
-__device__ __forceinline__ const uint8_t *row_of(const uint8_t *rows, const int32_t *pt, int64_t pt_stride,
-                                                 int64_t n_slots, const int32_t *sel, int b, int budget_blocks,
-                                                 int budget_tokens, int L, int p)
-{
-    if (kPaged) {
-        const int j = sel[(int64_t)b * budget_blocks + (p >> 2)];
-        const int t = j * kBT + (p & 3);
-        const int64_t slot = safe_slot(pt[(int64_t)b * pt_stride + ((t >= 0 && t < L) ? t : 0)], n_slots);
-        return rows + slot * kRowBytes;
-    }
-    return rows + ((int64_t)b * budget_tokens + p) * kRowBytes;
-}
-
 __device__ __forceinline__ void wave_lds_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -68,8 +54,8 @@ template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ rows, const int32_t *__restrict__ pt,
     int64_t pt_stride, int64_t n_slots, const int32_t *__restrict__ sel, const int32_t *__restrict__ n_tok,
-    const int32_t *__restrict__ ctx_len, int max_ctx, int budget_blocks, int budget_tokens, float sm_scale,
-    float *__restrict__ part_o, float *__restrict__ part_lse, int n_split)
+    int max_ctx, int budget_blocks, int budget_tokens, float sm_scale, float *__restrict__ part_o,
+    float *__restrict__ part_lse, int n_split)
 {
     __shared__ float ps[kWaves][kGroup][kTile];     // probabilities of the wave's current tile
     __shared__ float salpha[kWaves][kGroup];        // per-head rescale of the wave's running output
@@ -83,22 +69,32 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    int nt = n_tok[b];
-    nt = nt < 0 ? 0 : (nt > budget_tokens ? budget_tokens : nt);
     const int split_p0 = s * kTPS;
-    const int64_t part_base = ((int64_t)b * kHq + g * kGroup) * n_split + s;   // head g*8, split s
-    if (split_p0 >= nt) {
-        if (tid < kGroup)
-            part_lse[part_base + (int64_t)tid * n_split] = -INFINITY;
-        return;
-    }
-    const int L = kPaged ? clamp_ctx(ctx_len[b], max_ctx) : 0;
     const int wave_p0 = split_p0 + wave * kWaveTok;
-
-    // A operand: lane holds row (lane & 15) = query head of group g (rows 8..15
-    // zero), dims 32kk + 8 (lane >> 4) .. +8 for MFMA kk.
     const int arow = lane & 15;
     const int kofs = 8 * (lane >> 4);
+
+    // Everything that does not depend on the token count is requested at
+    // once: the count, the query, and each lane's row for its K token (lane
+    // l holds token l & 15 of each tile). On the paged path the row is the
+    // page-table slot of the selected token; indices are clamped so that
+    // every read stays inside its buffer before the count is known.
+    int nt = n_tok[b];
+    int64_t row_k[kTiles];
+#pragma unroll
+    for (int i = 0; i < kTiles; i++) {
+        int p = wave_p0 + kTile * i + arow;
+        p = p < budget_tokens ? p : budget_tokens - 1;
+        if (kPaged) {
+            int t = sel[(int64_t)b * budget_blocks + (p >> 2)] * kBT + (p & 3);
+            t = t < max_ctx ? t : max_ctx - 1;
+            row_k[i] = t >= 0 ? safe_slot(pt[(int64_t)b * pt_stride + t], n_slots) : 0;
+        } else {
+            row_k[i] = (int64_t)b * budget_tokens + p;
+        }
+    }
+    // A operand: lane holds row (lane & 15) = query head of group g (rows 8..15
+    // zero), dims 32kk + 8 (lane >> 4) .. +8 for MFMA kk.
     bf16x8 qa[kDh / 32];
     {
         const uint16_t *qr = q + ((int64_t)b * kHq + g * kGroup + (arow & 7)) * kDh + kofs;
@@ -109,16 +105,23 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
         }
     }
 
-    // Request every row the wave needs before the first multiply.
+    nt = nt < 0 ? 0 : (nt > budget_tokens ? budget_tokens : nt);
+    const int64_t part_base = ((int64_t)b * kHq + g * kGroup) * n_split + s;   // head g*8, split s
+    if (split_p0 >= nt) {
+        if (tid < kGroup)
+            part_lse[part_base + (int64_t)tid * n_split] = -INFINITY;
+        return;
+    }
+
+    // Request every row the wave needs before the first multiply. The V rows
+    // of a tile's 16 tokens are the K rows held by lanes 0..15.
     u32x4 kd[kTiles][kDh / 32];
     u32x2 vd[kTiles][kTile];
 #pragma unroll
     for (int i = 0; i < kTiles; i++) {
         const int pt0 = wave_p0 + kTile * i;
-        const int pk = pt0 + arow;                  // this lane's token for the K operand
-        if (pk < nt) {
-            const uint8_t *rk = row_of<kPaged>(rows, pt, pt_stride, n_slots, sel, b, budget_blocks, budget_tokens, L,
-                                               pk) + g * kKBytes + 2 * kofs;
+        if (pt0 + arow < nt) {
+            const uint8_t *rk = rows + row_k[i] * kRowBytes + g * kKBytes + 2 * kofs;
 #pragma unroll
             for (int kk = 0; kk < kDh / 32; kk++)
                 kd[i][kk] = *reinterpret_cast<const u32x4 *>(rk + 64 * kk);
@@ -127,14 +130,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
             for (int kk = 0; kk < kDh / 32; kk++)
                 kd[i][kk] = u32x4{0u, 0u, 0u, 0u};
         }
+        const uint32_t rlo = (uint32_t)row_k[i], rhi = (uint32_t)(row_k[i] >> 32);
 #pragma unroll
         for (int t = 0; t < kTile; t++) {
-            const int pv = pt0 + t;                 // uniform across the wave
-            vd[i][t] = pv < nt ? *reinterpret_cast<const u32x2 *>(
-                                     row_of<kPaged>(rows, pt, pt_stride, n_slots, sel, b, budget_blocks,
-                                                    budget_tokens, L, pv) +
-                                     (kHkv + g) * kKBytes + 8 * lane)
-                               : u32x2{0u, 0u};
+            // uniform across the wave: token pt0 + t, whose row lane t holds
+            const int64_t r = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(rhi, t) << 32) |
+                                        __builtin_amdgcn_readlane(rlo, t));
+            vd[i][t] = pt0 + t < nt
+                           ? *reinterpret_cast<const u32x2 *>(rows + r * kRowBytes + (kHkv + g) * kKBytes + 8 * lane)
+                           : u32x2{0u, 0u};
         }
     }
 
@@ -309,8 +313,8 @@ hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int3
 {
     dim3 grid((unsigned)ws.n_split, (unsigned)kHkv, (unsigned)batch);
     hipLaunchKernelGGL((attn_split_kernel<false>), grid, dim3(kThreads), 0, s, q,
-                       static_cast<const uint8_t *>(kv), nullptr, 0, 0, nullptr, n_tok, nullptr, 0, 0, budget_tokens,
-                       sm_scale, ws.part_o, ws.part_lse, ws.n_split);
+                       static_cast<const uint8_t *>(kv), nullptr, 0, 0, nullptr, n_tok, 0, 0, budget_tokens, sm_scale,
+                       ws.part_o, ws.part_lse, ws.n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -324,8 +328,8 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
 {
     dim3 grid((unsigned)ws.n_split, (unsigned)kHkv, (unsigned)batch);
     hipLaunchKernelGGL((attn_split_kernel<true>), grid, dim3(kThreads), 0, s, q,
-                       static_cast<const uint8_t *>(pool), pt, pt_stride, n_slots, sel, n_tok, ctx_len, max_ctx,
-                       budget_blocks, budget_tokens, sm_scale, ws.part_o, ws.part_lse, ws.n_split);
+                       static_cast<const uint8_t *>(pool), pt, pt_stride, n_slots, sel, n_tok, max_ctx, budget_blocks,
+                       budget_tokens, sm_scale, ws.part_o, ws.part_lse, ws.n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -107,6 +107,12 @@ def test_bad_arguments_rejected_before_launch():
         lambda: qsa.qsa_decode_step(cfg, _batch(), [], 0, FAKE, 1 << 30),
         lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)],
                                     0, FAKE, 1 << 30),                                           # no output
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)],
+                                    0, FAKE, 1 << 30, 4096, [4096]),                             # side == compute
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)],
+                                    0, FAKE, 1 << 30, 4096, [8192, 8192]),                       # repeated side
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)],
+                                    0, FAKE, 1 << 30, 4096, list(range(8192, 8192 + 9))),        # too many
     ]
     for i, c in enumerate(cases):
         with pytest.raises(qsa.QsaError) as ei:

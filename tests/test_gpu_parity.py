@@ -331,7 +331,7 @@ def test_sparse_decode_parity_and_closed_forms(gpu):
 
 # ------------------------------------------------------------- whole step
 
-def _step(di, loc=None, two_streams=True):
+def _step(di, loc=None, n_side=2):
     wl = di.wl
     cfg = _cfg(wl)
     K = wl.budget // 4
@@ -342,8 +342,8 @@ def _step(di, loc=None, two_streams=True):
     layers = [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l], di.out[l],
                              None, sel[l], ns[l]) for l in range(L)]
     ws, nws = _ws(cfg, di.batch, di.max_ctx, L, loc)
-    copy = torch.cuda.Stream() if two_streams else None
-    qsa.qsa_decode_step(cfg, _batch(di), layers, loc, ws, nws, torch.cuda.current_stream(), copy)
+    side = [torch.cuda.Stream() for _ in range(n_side)]
+    qsa.qsa_decode_step(cfg, _batch(di), layers, loc, ws, nws, torch.cuda.current_stream(), side)
     torch.cuda.synchronize()
     return sel.cpu().numpy(), ns.cpu().numpy(), di.out.cpu().numpy()
 
@@ -374,19 +374,21 @@ def test_decode_step_parity(gpu, name, layers):
 
 
 def test_decode_step_deterministic_and_offload_bit_exact(gpu):
-    """Two runs give the same bits; the offload path (pool in pinned host
-    memory, gather over PCIe on a second stream) gives the same bits as the
-    HBM path, which reads the rows in place through the page table."""
+    """Every schedule gives the same bits: one stream, one to three side
+    streams, and the offload path (pool in pinned host memory, gather over
+    PCIe on a side stream), which must match the HBM path that reads the rows
+    in place through the page table."""
     wl = S.WORKLOADS["batch8-short"]
-    di = DeviceInputs(wl, gpu, layers=3)
+    di = DeviceInputs(wl, gpu, layers=5)
     sel1, ns1, out1 = _step(di)
-    sel2, ns2, out2 = _step(di, two_streams=False)
-    assert np.array_equal(out1, out2) and np.array_equal(sel1, sel2)
-    dh = DeviceInputs(wl, gpu, layers=3, kv_host=True, hi=di.hi)
-    for two in (True, False):
-        sel3, ns3, out3 = _step(dh, two_streams=two)
-        assert np.array_equal(sel1, sel3)
-        assert np.array_equal(out1, out3)
+    for n_side in (0, 1, 3):
+        sel2, ns2, out2 = _step(di, n_side=n_side)
+        assert np.array_equal(out1, out2) and np.array_equal(sel1, sel2), n_side
+    dh = DeviceInputs(wl, gpu, layers=5, kv_host=True, hi=di.hi)
+    for n_side in (1, 0, 2):
+        sel3, ns3, out3 = _step(dh, n_side=n_side)
+        assert np.array_equal(sel1, sel3), n_side
+        assert np.array_equal(out1, out3), n_side
 
 
 def test_decode_step_page_table_permutation_invariant(gpu):
