@@ -45,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 64.0          # PCIe 5.0 x16, one direction
 SCORE_KERNEL = "index_score_kernel"
 SCORE_SOURCES = ("kv_cache_selection_amd/csrc/index_score.hip", "kv_cache_selection_amd/csrc/qsa_internal.h")
 COPY_BYTES = 1 << 28
@@ -382,6 +383,12 @@ def main():
         "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes},
     }
+    if di.kv_host:
+        # every gathered row crosses PCIe once per step
+        pcie_bytes = int(ntok.sum()) * g.row_bytes
+        pcie_gbs = pcie_bytes / (ms_step * 1e-3) / 1e9
+        result["pcie"] = {"achieved": round(pcie_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "bytes_per_step": pcie_bytes}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, di.hi, args.cpu_seconds)
     print(json.dumps(result), flush=True)

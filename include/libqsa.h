@@ -174,10 +174,12 @@ typedef struct {
  * Streams: `side` holds n_side extra streams (all distinct from `compute`);
  * with n_side = 0 (side may then be NULL) every kernel runs in order on
  * `compute`. With side streams the layers overlap:
- *   - HBM pools: `compute` scores layer after layer; layer l's selection,
- *     attention and merge run on side[l % n_side] as soon as its scores exist,
- *     so they hide under the scoring of the following layers (this treats the
- *     layers as independent, which they are within one call);
+ *   - HBM pools: after `compute` has cleared the step's scratch, layer l's
+ *     whole chain (score, select, attend, merge) runs on stream
+ *     l % (n_side + 1) of {compute, side[0], side[1], ...}, so several layers
+ *     are in flight at once and the latency-bound parts of one hide under the
+ *     index scans of the others; at most two index scans run at a time (this
+ *     treats the layers as independent, which they are within one call);
  *   - host pools: side[0] gathers layer l over PCIe while `compute` scores
  *     and selects layer l+1 and attends layer l-1 (further side streams are
  *     not used).

@@ -39,7 +39,7 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.n_layers = n_layers;
     w.n_split = n_split_of(cfg->budget_tokens);
     const size_t nb = (size_t)(w.n_blk_max > 0 ? w.n_blk_max : 1);
-    w.per_hist = align_up((size_t)batch * kHistBins * 4);
+    w.per_hist = align_up((size_t)batch * kHistReps * kHistBins * 4);
     w.per_cnt = align_up((size_t)batch * w.n_slices * 2 * 4);
     w.per_sdef = align_up((size_t)batch * w.n_slices * kSliceBlocks * 4);
     w.per_scand = align_up((size_t)batch * w.n_slices * kSliceBlocks * 8);
@@ -356,7 +356,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     const int NS = offload ? (n_side > 0 ? 1 : 0) : n_side;
     hipStream_t sx = NS > 0 ? (hipStream_t)side[0] : nullptr;
     std::vector<hipEvent_t> ev;
-    if (two_streams && (st = get_events(3 * n_layers + NS, ev)) != QSA_OK)
+    if (two_streams && (st = get_events(3 * n_layers + NS + 1, ev)) != QSA_OK)
         return st;
 
     const int B = batch->batch;
@@ -429,28 +429,40 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     }
 
     if (!offload) {
-        // Pools in HBM: the compute stream streams the index of layer after
-        // layer; layer l's selection and attention run on side stream
-        // l % NS as soon as its scores exist, under the scoring of the next
-        // layers. Several side streams let the latency-bound chains of
-        // consecutive layers overlap one another too.
+        // Pools in HBM: layer l's whole chain (score, select, attend, merge)
+        // runs on stream l % (NS + 1) of {compute, side...}, after the
+        // compute stream has cleared the histograms. Several chains are in
+        // flight at once, so the latency-bound selection and attention of one
+        // layer, and the ramp and tail of each scan, hide under the index
+        // scans of the others. No more than kScansInFlight scans run at once
+        // (the scan of layer l waits for that of layer l - kScansInFlight):
+        // more concurrent scans only make them fight over HBM.
+        constexpr int kScansInFlight = 2;
+        const int NC = NS + 1;
+        if (e == hipSuccess)
+            e = hipEventRecord(ev[0], sc);
+        for (int k = 0; k < NS && e == hipSuccess; k++)
+            e = hipStreamWaitEvent((hipStream_t)side[k], ev[0], 0);
         for (int l = 0; l < n_layers && e == hipSuccess; l++) {
-            hipStream_t sy = (hipStream_t)side[l % NS];
-            e = score(l, sc);
+            const int c = l % NC;
+            hipStream_t sy = c == 0 ? sc : (hipStream_t)side[c - 1];
+            hipEvent_t scanned = ev[1 + NS + l];
+            if (l >= kScansInFlight)
+                e = hipStreamWaitEvent(sy, ev[1 + NS + l - kScansInFlight], 0);
             if (e == hipSuccess)
-                e = hipEventRecord(ev[l], sc);
+                e = score(l, sy);
             if (e == hipSuccess)
-                e = hipStreamWaitEvent(sy, ev[l], 0);
+                e = hipEventRecord(scanned, sy);
             if (e == hipSuccess)
                 e = select(l, sy);
             if (e == hipSuccess)
                 e = attend_paged(l, sy);
         }
         // The caller synchronises on the compute stream: join the side streams.
-        for (int k = 0; k < NS && k < n_layers && e == hipSuccess; k++) {
-            e = hipEventRecord(ev[3 * n_layers + k], (hipStream_t)side[k]);
+        for (int k = 0; k < NS && e == hipSuccess; k++) {
+            e = hipEventRecord(ev[1 + k], (hipStream_t)side[k]);
             if (e == hipSuccess)
-                e = hipStreamWaitEvent(sc, ev[3 * n_layers + k], 0);
+                e = hipStreamWaitEvent(sc, ev[1 + k], 0);
         }
         return hip_status(e);
     }

@@ -80,6 +80,31 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const uint8_t *kbase = keys + r0 * kIdxD;
+    const uint16_t *sbase = scales + r0;
+    float *bs_row = block_scores + (int64_t)b * bs_stride;
+    const int t_end = min(t_begin + chunk_tokens, L);
+
+    // Two-deep software pipeline: the keys of the wave's next 64 tokens are
+    // requested before the current 64 are widened and multiplied. The first
+    // tile is requested before anything else is set up.
+    u32x4 k[4], kn[4];
+    uint16_t sc_bits = 0, sc_next = 0;
+    const int grp_tok = lane & 15;          // token within a group, for the loads
+    const int grp_off = 16 * (lane >> 4);   // byte offset within the token's 64
+    auto load_tile = [&](int tw, u32x4 *dst, uint16_t &sc) {
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int t = tw + 16 * g + grp_tok;
+            dst[g] = t < L ? __builtin_nontemporal_load(
+                                 reinterpret_cast<const u32x4 *>(kbase + (int64_t)t * kIdxD + grp_off))
+                           : u32x4{0u, 0u, 0u, 0u};
+        }
+        sc = (tw + lane < L) ? sbase[tw + lane] : (uint16_t)0;
+    };
+    int tw = t_begin + wave * kWaveTok;
+    if (tw < t_end)
+        load_tile(tw, k, sc_bits);
 
     if (do_hist) {
         for (int i = tid; i < kHistBins; i += kThreads)
@@ -107,33 +132,9 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
     for (int h = 0; h < kIdxH; h++)
         w[h] = w_idx[b * kIdxH + h];
 
-    const uint8_t *kbase = keys + r0 * kIdxD;
-    const uint16_t *sbase = scales + r0;
-    float *bs_row = block_scores + (int64_t)b * bs_stride;
-
     if (do_hist)
         __syncthreads();
 
-    const int t_end = min(t_begin + chunk_tokens, L);
-    // Two-deep software pipeline: the keys of the wave's next 64 tokens are
-    // requested before the current 64 are widened and multiplied.
-    u32x4 k[4], kn[4];
-    uint16_t sc_bits = 0, sc_next = 0;
-    const int grp_tok = lane & 15;          // token within a group, for the loads
-    const int grp_off = 16 * (lane >> 4);   // byte offset within the token's 64
-    auto load_tile = [&](int tw, u32x4 *dst, uint16_t &sc) {
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int t = tw + 16 * g + grp_tok;
-            dst[g] = t < L ? __builtin_nontemporal_load(
-                                 reinterpret_cast<const u32x4 *>(kbase + (int64_t)t * kIdxD + grp_off))
-                           : u32x4{0u, 0u, 0u, 0u};
-        }
-        sc = (tw + lane < L) ? sbase[tw + lane] : (uint16_t)0;
-    };
-    int tw = t_begin + wave * kWaveTok;
-    if (tw < t_end)
-        load_tile(tw, k, sc_bits);
     for (; tw < t_end; tw += kWgTok) {
         const int tn = tw + kWgTok;
         if (tn < t_end)
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(
 
     if (do_hist) {
         __syncthreads();
-        uint32_t *gh = hist + (int64_t)b * kHistBins;
+        uint32_t *gh = hist + ((int64_t)b * kHistReps + blockIdx.x % kHistReps) * kHistBins;
         for (int i = tid; i < kHistBins; i += kThreads) {
             uint32_t c = lhist[i];
             if (c)
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void block_hist_kernel(const float *__res
             atomicAdd(&lhist[order_key(row[j]) >> kHistShift], 1u);
     }
     __syncthreads();
-    uint32_t *gh = hist + (int64_t)b * kHistBins;
+    uint32_t *gh = hist + ((int64_t)b * kHistReps + blockIdx.x % kHistReps) * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
         uint32_t c = lhist[i];
         if (c)

@@ -25,6 +25,10 @@ constexpr int kMaxCtx = 1 << 21;               // tokens per sequence
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
+// Each sequence's histogram is kept in kHistReps copies; scoring workgroup x
+// adds into copy x % kHistReps, so that no more than 1/kHistReps of a
+// sequence's workgroups queue up on the same counter. Readers sum the copies.
+constexpr int kHistReps = 4;
 
 // Attention: tokens per split.
 constexpr int kTPS = 128;
@@ -65,7 +69,7 @@ __device__ __forceinline__ int forced_count(int n_blk, int sink, int tail_first)
 constexpr int kSliceBlocks = 2048;             // blocks per selection slice (one collect workgroup)
 
 struct SelectWs {
-    uint32_t *hist;        // [B][kHistBins], zeroed before scoring
+    uint32_t *hist;        // [B][kHistReps][kHistBins], zeroed before scoring
     uint32_t *slot_count;  // [B][n_slices][2] per-slice list lengths (definite, candidates)
     int32_t *slot_def;     // [B][n_slices][kSliceBlocks] blocks above the threshold bin
     uint64_t *slot_cand;   // [B][n_slices][kSliceBlocks] blocks inside the threshold bin

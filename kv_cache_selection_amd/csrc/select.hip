@@ -94,18 +94,25 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [NT / 64] *
 }
 
 // Walk a histogram of NT * W bins from the top: the bin where the running
-// count first reaches `want`, and the count strictly above it.
-template <int W, int NT>
+// count first reaches `want`, and the count strictly above it. The histogram
+// is the sum of R copies laid out kHistBins apart.
+template <int W, int NT, int R = 1>
 __device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
                               uint32_t *above_out)
 {
     const int tr = NT - 1 - threadIdx.x;               // thread 0 owns the top bins
     uint32_t hv[W], local = 0;
 #pragma unroll
-    for (int i = 0; i < W; i++) {
+    for (int i = 0; i < W; i++)
         hv[i] = h[W * tr + i];
+#pragma unroll
+    for (int c = 1; c < R; c++)
+#pragma unroll
+        for (int i = 0; i < W; i++)
+            hv[i] += h[c * kHistBins + W * tr + i];
+#pragma unroll
+    for (int i = 0; i < W; i++)
         local += hv[i];
-    }
     uint32_t total;
     uint32_t above = block_inclusive_scan<NT>(local, sh_scan, &total) - local;
 #pragma unroll
@@ -164,8 +171,8 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(
         sh_u[3] = 0;
     }
     __syncthreads();
-    find_crossing<kHistBins / kCollectThreads, kCollectThreads>(hist + (int64_t)b * kHistBins, (uint32_t)r, sh_scan,
-                                                                &sh_u[0], &sh_u[1]);
+    find_crossing<kHistBins / kCollectThreads, kCollectThreads, kHistReps>(hist + (int64_t)b * kHistReps * kHistBins,
+                                                                           (uint32_t)r, sh_scan, &sh_u[0], &sh_u[1]);
     const uint32_t bstar = sh_u[0];
 
 #pragma unroll
