@@ -34,6 +34,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -42,6 +43,25 @@ constexpr int kTiles = 2;                          // tiles per wave
 constexpr int kWaveTok = kTile * kTiles;           // 32
 static_assert(kWaves * kWaveTok == kTPS, "tokens per split");
 constexpr int kKBytes = kDh * 2;                   // 512 bytes of K (or V) per head per row
+// A wave's V tile in LDS: 16 token rows of 512 bytes, 32 bytes of padding
+// between rows so that the transposing reads of 16 rows hit distinct banks.
+constexpr int kVPitch = kKBytes + 32;
+constexpr int kVTileBytes = kWaveTok * kVPitch;    // a wave's 32 rows: 17408
+constexpr int kOBytes = kWaves * kGroup * kDh * 4; // per-wave partial outputs for the merge (32 KB)
+constexpr int kSmemBytes = kWaves * kVTileBytes > kOBytes ? kWaves * kVTileBytes : kOBytes;
+
+// Max / sum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15): swaps
+// within pairs and quads, then the half-row and row mirrors.
+template <bool kMax>
+__device__ __forceinline__ float row16_reduce(float x)
+{
+    auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+    x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+    x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+    x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false))); // row_half_mirror
+    x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false))); // row_mirror
+    return x;
+}
 
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -57,10 +77,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     int max_ctx, int budget_blocks, int budget_tokens, float sm_scale, float *__restrict__ part_o,
     float *__restrict__ part_lse, int n_split)
 {
-    __shared__ float ps[kWaves][kGroup][kTile];     // probabilities of the wave's current tile
-    __shared__ float salpha[kWaves][kGroup];        // per-head rescale of the wave's running output
+    __shared__ __attribute__((aligned(16))) float ps[kWaves][kGroup][kWaveTok];  // the wave's probabilities
     __shared__ float sstat[kWaves][kGroup][2];      // per-wave (max, sum) for the workgroup merge
-    __shared__ float so[kWaves][kGroup][kDh];       // per-wave partial outputs (32 KB)
+    // V tiles during the token loop, then the per-wave partial outputs
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    float(*so)[kGroup][kDh] = reinterpret_cast<float(*)[kGroup][kDh]>(smem);
 
     const int s = blockIdx.x;
     const int g = blockIdx.y;
@@ -142,86 +163,119 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
         }
     }
 
-    // Running softmax state: lanes 0..31 hold heads 4 (lane >> 4) + v.
+    // Softmax state of the wave: lane l holds heads 4 (l >> 4) + v (rows 8..15
+    // of the MFMA tiles are padding, so lanes 32..63 carry no head). The
+    // wave's 32 tokens are normalised together, so no running rescale.
     float m_run[4], l_run[4];
+    // Output accumulators, the C tiles of PV: o[m][v] = head 4 (l >> 4) + v,
+    // dim 16 m + (l & 15).
+    f32x4 o[kDh / 16];
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        m_run[v] = -INFINITY;
-        l_run[v] = 0.0f;
-    }
-    float o[kGroup][4];                             // this lane's 4 dims of every head
-#pragma unroll
-    for (int h = 0; h < kGroup; h++)
-#pragma unroll
-        for (int c = 0; c < 4; c++)
-            o[h][c] = 0.0f;
+    for (int m = 0; m < kDh / 16; m++)
+        o[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    uint8_t *vt = smem + wave * kVTileBytes;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
 
-#pragma unroll
-    for (int i = 0; i < kTiles; i++) {
-        const int pt0 = wave_p0 + kTile * i;
-        if (pt0 >= nt)
-            break;                                  // uniform: no valid token left in this wave
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < kDh / 32; kk++)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8, kd[i][kk]), acc, 0, 0,
-                                                          0);
-        // acc[v] = q_{4 (lane>>4) + v} . K_{token lane & 15}; rows >= 8 are padding.
-        const bool tok_ok = pt0 + (lane & 15) < nt;
+    if (wave_p0 >= nt) {                            // uniform: no valid token in this wave
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const float z = tok_ok ? acc[v] * sm_scale : -INFINITY;
-            float mx = z;
+            m_run[v] = -INFINITY;
+            l_run[v] = 0.0f;
+        }
+    } else {
+        // V rows of both tiles to LDS (row 16 i + t) while QK^T runs.
 #pragma unroll
-            for (int o2 = 8; o2 >= 1; o2 >>= 1)
-                mx = fmaxf(mx, __shfl_xor(mx, o2, 16));
-            const float mn = fmaxf(m_run[v], mx);
-            const float alpha = (mn == -INFINITY) ? 1.0f : __expf(m_run[v] - mn);
-            const float e = (z == -INFINITY) ? 0.0f : __expf(z - mn);
-            float sum = e;
+        for (int i = 0; i < kTiles; i++)
 #pragma unroll
-            for (int o2 = 8; o2 >= 1; o2 >>= 1)
-                sum += __shfl_xor(sum, o2, 16);
-            l_run[v] = l_run[v] * alpha + sum;
-            m_run[v] = mn;
-            if (lane < 32) {
-                const int h = 4 * (lane >> 4) + v;
-                ps[wave][h][lane & 15] = e;
-                if ((lane & 15) == 0)
-                    salpha[wave][h] = alpha;
+            for (int t = 0; t < kTile; t++)
+                *reinterpret_cast<u32x2 *>(vt + (kTile * i + t) * kVPitch + 8 * lane) = vd[i][t];
+        f32x4 acc[kTiles];
+#pragma unroll
+        for (int i = 0; i < kTiles; i++) {
+            acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < kDh / 32; kk++)
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8, kd[i][kk]),
+                                                                 acc[i], 0, 0, 0);
+        }
+        // acc[i][v] = q_{4 (lane>>4) + v} . K_{token 16 i + (lane & 15)}.
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            float z[kTiles], mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < kTiles; i++) {
+                z[i] = wave_p0 + kTile * i + col < nt ? acc[i][v] * sm_scale : -INFINITY;
+                mx = fmaxf(mx, z[i]);
             }
+            mx = row16_reduce<true>(mx);
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kTiles; i++) {
+                float e = (z[i] == -INFINITY) ? 0.0f : __expf(z[i] - mx);
+                // Keep 16 mantissa bits (a bf16 head plus a bf16 remainder),
+                // the precision PV uses, so that numerator and normaliser agree.
+                const uint32_t hb = __float_as_uint(e) & 0xFFFF0000u;
+                const uint32_t lb = __float_as_uint(e - __uint_as_float(hb)) & 0xFFFF0000u;
+                e = __uint_as_float(hb) + __uint_as_float(lb);
+                sum += e;
+                if (lane < 32)
+                    ps[wave][4 * grp + v][kTile * i + col] = e;
+            }
+            l_run[v] = row16_reduce<false>(sum);
+            m_run[v] = mx;
         }
         wave_lds_sync();
 
-        // PV: rescale, then accumulate the tile's 16 rows.
+        // PV on the matrix cores, v_mfma_f32_16x16x32_bf16 per 16 dims:
+        //  A = P (row = head `col`, k = tokens 8 grp .. +7) as its exact split
+        //      into a bf16 high part and a bf16 remainder;
+        //  B = V (k = tokens 8 grp .. +7, column = dim), read transposed from
+        //      the rows in LDS, four tokens per read: in each group of 16
+        //      lanes, lane j supplies the address of token row base + (j >> 2),
+        //      dims 4 (j & 3) .. +3, and lane c receives dim c of the four rows.
+        bf16x8 a_hi, a_lo;
+        {
+            uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+            if (col < kGroup) {
+                const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&ps[wave][col][8 * grp]);
+                const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&ps[wave][col][8 * grp + 4]);
+                const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
-        for (int h = 0; h < kGroup; h++) {
-            const float a = salpha[wave][h];
-#pragma unroll
-            for (int c = 0; c < 4; c++)
-                o[h][c] *= a;
-        }
-#pragma unroll
-        for (int t = 0; t < kTile; t++) {
-            const u32x2 w = vd[i][t];
-            const float v0 = __uint_as_float(w.x << 16), v1 = __uint_as_float(w.x & 0xFFFF0000u);
-            const float v2 = __uint_as_float(w.y << 16), v3 = __uint_as_float(w.y & 0xFFFF0000u);
-#pragma unroll
-            for (int h = 0; h < kGroup; h++) {
-                const float p = ps[wave][h][t];
-                o[h][0] = fmaf(p, v0, o[h][0]);
-                o[h][1] = fmaf(p, v1, o[h][1]);
-                o[h][2] = fmaf(p, v2, o[h][2]);
-                o[h][3] = fmaf(p, v3, o[h][3]);
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t h0 = __float_as_uint(pv[e]) & 0xFFFF0000u;
+                    const uint32_t h1 = __float_as_uint(pv[e + 1]) & 0xFFFF0000u;
+                    const uint32_t l0 = __float_as_uint(pv[e] - __uint_as_float(h0)) >> 16;
+                    const uint32_t l1 = __float_as_uint(pv[e + 1] - __uint_as_float(h1)) & 0xFFFF0000u;
+                    hi[e >> 1] = (h0 >> 16) | h1;
+                    lo[e >> 1] = l0 | l1;
+                }
             }
+            a_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            a_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
         }
-        wave_lds_sync();
+        const uint8_t *vrd = vt + (8 * grp + (col >> 2)) * kVPitch + 8 * (col & 3);
+#pragma unroll
+        for (int m = 0; m < kDh / 16; m++) {
+            const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vrd + 32 * m));
+            const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vrd + 4 * kVPitch + 32 * m));
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bv, o[m], 0, 0, 0);
+            o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bv, o[m], 0, 0, 0);
+        }
     }
 
-    // Workgroup merge of the four waves' states.
+    // Workgroup merge of the four waves' states (the V tiles' LDS is reused).
+    __syncthreads();
+    if (lane < 32) {
 #pragma unroll
-    for (int h = 0; h < kGroup; h++)
-        *reinterpret_cast<f32x4 *>(&so[wave][h][4 * lane]) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+        for (int m = 0; m < kDh / 16; m++)
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                so[wave][4 * grp + v][16 * m + col] = o[m][v];
+    }
     if (lane < 32 && (lane & 15) == 0) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
