@@ -284,73 +284,71 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
         }
     }
     __syncthreads();
+    for (int d = tid; d < kDh; d += kThreads) {
 #pragma unroll
-    for (int h = 0; h < kGroup; h++) {
-        float M = -INFINITY;
+        for (int h = 0; h < kGroup; h++) {
+            float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++)
-            M = fmaxf(M, sstat[w][h][0]);
-        float acc = 0.0f, den = 0.0f;
+            for (int w = 0; w < kWaves; w++)
+                M = fmaxf(M, sstat[w][h][0]);
+            float acc = 0.0f, den = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) {
-            const float mw = sstat[w][h][0];
-            const float f = (mw == -INFINITY) ? 0.0f : __expf(mw - M);
-            den += f * sstat[w][h][1];
-            acc = fmaf(f, so[w][h][tid], acc);
+            for (int w = 0; w < kWaves; w++) {
+                const float mw = sstat[w][h][0];
+                const float f = (mw == -INFINITY) ? 0.0f : __expf(mw - M);
+                den += f * sstat[w][h][1];
+                acc = fmaf(f, so[w][h][d], acc);
+            }
+            part_o[(part_base + (int64_t)h * n_split) * kDh + d] = acc / den;
+            if (d == 0)
+                part_lse[part_base + (int64_t)h * n_split] = M + logf(den);
         }
-        part_o[(part_base + (int64_t)h * n_split) * kDh + tid] = acc / den;
-        if (tid == 0)
-            part_lse[part_base + (int64_t)h * n_split] = M + logf(den);
     }
 }
 
-constexpr int kMaxSplit = kMaxBudget / kTPS;
 constexpr int kMergeUnroll = 16;
 
-// One workgroup per (sequence, head); thread d owns output dim d. The split
-// weights e^{lse_s - max} are computed once into LDS, then every thread sums
-// its column with all loads of a batch of splits in flight.
+// One workgroup per (sequence, head); thread d owns output dim d. Every
+// thread reads the (uniform) split LSEs itself and its column of partial
+// outputs in the same batch, so the whole merge is one round of loads: for
+// each batch of splits, the running max is raised and the sums rescaled.
 __global__ __launch_bounds__(kDh) void merge_kernel(const float *__restrict__ part_o,
                                                     const float *__restrict__ part_lse, int n_split,
                                                     float *__restrict__ out)
 {
-    __shared__ float wgt[kMaxSplit];
-    __shared__ float red[kDh / 64];
     const int bh = blockIdx.x;              // b * kHq + h
     const int tid = threadIdx.x;
     const float *lse = part_lse + (int64_t)bh * n_split;
-    const float ls = tid < n_split ? lse[tid] : -INFINITY;
-    float m = ls;
-    for (int o = 32; o >= 1; o >>= 1)
-        m = fmaxf(m, __shfl_xor(m, o));
-    if ((tid & 63) == 0)
-        red[tid >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (tid < n_split)
-        wgt[tid] = (m == -INFINITY || ls == -INFINITY) ? 0.0f : __expf(ls - m);
-    __syncthreads();
-    float acc = 0.0f, den = 0.0f;
-    if (m != -INFINITY) {
-        const float *col = part_o + (int64_t)bh * n_split * kDh + tid;
-        for (int s0 = 0; s0 < n_split; s0 += kMergeUnroll) {
-            float x[kMergeUnroll];
+    const float *col = part_o + (int64_t)bh * n_split * kDh + tid;
+    float M = -INFINITY, acc = 0.0f, den = 0.0f;
+    for (int s0 = 0; s0 < n_split; s0 += kMergeUnroll) {
+        float ls[kMergeUnroll], x[kMergeUnroll];
 #pragma unroll
-            for (int u = 0; u < kMergeUnroll; u++)
-                x[u] = s0 + u < n_split ? col[(int64_t)(s0 + u) * kDh] : 0.0f;
-#pragma unroll
-            for (int u = 0; u < kMergeUnroll; u++) {
-                if (s0 + u < n_split) {
-                    const float ws = wgt[s0 + u];
-                    den += ws;
-                    // empty splits hold stale data: select, not multiply
-                    acc = ws != 0.0f ? fmaf(ws, x[u], acc) : acc;
-                }
-            }
+        for (int u = 0; u < kMergeUnroll; u++) {
+            const bool in = s0 + u < n_split;
+            ls[u] = in ? lse[s0 + u] : -INFINITY;
+            x[u] = in ? col[(int64_t)(s0 + u) * kDh] : 0.0f;
         }
-        acc /= den;
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; u++)
+            mb = fmaxf(mb, ls[u]);
+        if (mb == -INFINITY)
+            continue;                       // uniform: every split of the batch is empty
+        const float Mn = fmaxf(M, mb);
+        const float r = __expf(M - Mn);     // 0 while M is still -inf
+        acc *= r;
+        den *= r;
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; u++) {
+            const float ws = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
+            den += ws;
+            // empty splits hold stale data: select, not multiply
+            acc = ws != 0.0f ? fmaf(ws, x[u], acc) : acc;
+        }
+        M = Mn;
     }
-    out[(int64_t)bh * kDh + tid] = acc;
+    out[(int64_t)bh * kDh + tid] = den > 0.0f ? acc / den : 0.0f;
 }
 
 } // namespace
