@@ -53,6 +53,12 @@ def _load():
     lib.qo_decode_f16.restype = f64
     lib.qo_decode_bf16.argtypes = [ctypes.c_uint16]
     lib.qo_decode_bf16.restype = f64
+    lib.qo_encode_f16.argtypes = [f64]
+    lib.qo_encode_f16.restype = ctypes.c_uint16
+    lib.qo_encode_e4m3.argtypes = [f64]
+    lib.qo_encode_e4m3.restype = ctypes.c_uint8
+    lib.qo_quantise_key.argtypes = [i32, P, P, P]
+    lib.qo_quantise_key.restype = None
     lib.qo_token_scores.argtypes = [i64, i32, i32, P, P, P, P, P]
     lib.qo_token_scores.restype = None
     lib.qo_block_scores.argtypes = [i64, i32, P, P]
@@ -235,3 +241,48 @@ def decode_layer(keys, scales, q_idx, w, q, pt, pool, *, n_kv_heads: int, budget
     sel = sel[:n_sel].copy()
     return LayerResult(ts[:L].copy(), bs[:n_blk].copy(), sel, float(kth[0]),
                        tokens_of_blocks(L, sel, bt), out)
+
+
+# ------------------------------------------------------------ append step
+
+def encode_f16(x: float) -> int:
+    """Nearest binary16 (ties to even) of a non-negative value, as bits."""
+    return int(_load().qo_encode_f16(float(x)))
+
+
+def encode_e4m3(y: float) -> int:
+    """Nearest e4m3 code (ties to even, |y| >= 448 saturates to 448)."""
+    return int(_load().qo_encode_e4m3(float(y)))
+
+
+def quantise_key(x):
+    """One index key, float32 [idx_dim] -> (codes u8 [idx_dim], scale bits u16).
+
+    The append step of the memory-ledger section of "双卡RTX4090跑通Qwen3-Next"
+    (index, scales and page layout kept together): sigma = fp16(amax / 448),
+    code_i = e4m3(x_i / sigma), divisions in binary32."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    codes = np.zeros(x.size, np.uint8)
+    s = np.zeros(1, np.uint16)
+    _load().qo_quantise_key(x.size, _ptr(x), _ptr(codes), _ptr(s))
+    return codes, int(s[0])
+
+
+def append_token(ctx, row0, pt, slot, keys_layers, scales_layers, pools, new_keys, new_rows):
+    """Reference append over host arrays (modified in place).
+
+    For each sequence b with t = ctx[b]: every layer l gets the quantised
+    new_keys[l][b] at index row row0[b] + t and new_rows[l][b] at pool slot
+    slot[b]; the page table maps t -> slot[b]; the length becomes t + 1.
+    Returns the new lengths."""
+    out = np.array(ctx, dtype=np.int64).copy()
+    for b in range(len(ctx)):
+        t = int(ctx[b])
+        for l in range(len(keys_layers)):
+            c, s = quantise_key(new_keys[l][b])
+            keys_layers[l][row0[b] + t] = c
+            scales_layers[l][row0[b] + t] = s
+            pools[l][slot[b]] = new_rows[l][b]
+        pt[b, t] = slot[b]
+        out[b] = t + 1
+    return out

@@ -341,3 +341,84 @@ int64_t qo_decode_layer(int64_t L, int idx_heads, int idx_dim, int bt, int64_t b
     free(ts);
     return n_sel;
 }
+
+/* ------------------------------------------------------------ append step */
+
+/* The new token of a decode step gets an index row and a KV row. Sources:
+ * "双卡RTX4090跑通Qwen3-Next" (kongchang.com), memory-ledger section: the
+ * index, its quantisation scales and the page layout are kept together, and
+ * a new token's logical address maps to a physical cache slot; the workload
+ * definition fixes fp8 e4m3 keys with one fp16 scale per token. Reading taken
+ * where the pages are silent: the scale is the key's largest magnitude over
+ * 448 (the largest e4m3 value), rounded to fp16, and every element is x / scale
+ * rounded to the nearest e4m3 value; both divisions are done in binary32, the
+ * precision the stored format implies (an fp32 key, an fp16 scale).
+ *
+ * The encoders below search every code for the nearest value instead of
+ * manipulating bits, so they can be checked against the decoders by eye. */
+
+/* Nearest binary16 value to a non-negative double, ties to the even code;
+ * values of 65520 and above round to +infinity. Returns the bits. */
+uint16_t qo_encode_f16(double x)
+{
+    if (!(x >= 0.0))
+        return 0x7E00;                  /* NaN; negative inputs are not used */
+    if (x >= 65520.0)
+        return 0x7C00;
+    uint16_t best = 0;
+    double best_d = INFINITY;
+    for (uint32_t c = 0; c < 0x7C00; c++) {
+        double d = fabs(qo_decode_f16((uint16_t)c) - x);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = (uint16_t)c;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+/* Nearest e4m3 value to y, ties to the even code, magnitudes beyond 448
+ * clamped to 448 (saturation); the sign follows y. */
+uint8_t qo_encode_e4m3(double y)
+{
+    double a = fabs(y);
+    uint8_t best = 0;
+    if (a >= 448.0) {
+        best = 0x7E;
+    } else {
+        double best_d = INFINITY;
+        for (uint32_t c = 0; c <= 0x7E; c++) {
+            double d = fabs(qo_decode_e4m3((uint8_t)c) - a);
+            if (d < best_d || (d == best_d && (c & 1) == 0)) {
+                best = (uint8_t)c;
+                best_d = d;
+            }
+        }
+    }
+    return signbit(y) ? (uint8_t)(best | 0x80) : best;
+}
+
+/* Quantise one index key of n elements: scale bits and n e4m3 codes.
+ *   sigma = f16(fl32(amax / 448)), code_i = e4m3(fl32(x_i / sigma)),
+ * with all codes 0 when sigma is 0. */
+void qo_quantise_key(int n, const float *x, uint8_t *codes, uint16_t *scale_bits)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax)
+            amax = a;
+    }
+    float ratio = amax / 448.0f;
+    uint16_t s = qo_encode_f16((double)ratio);
+    float sigma = (float)qo_decode_f16(s);
+    for (int i = 0; i < n; i++) {
+        if (sigma > 0.0f) {
+            float y = x[i] / sigma;
+            codes[i] = qo_encode_e4m3((double)y);
+        } else {
+            codes[i] = 0;
+        }
+    }
+    *scale_bits = s;
+}

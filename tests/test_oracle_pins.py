@@ -383,3 +383,84 @@ def test_page_byte_facts():
     wl = qsa_synth.WORKLOADS["offload-1m"]
     assert wl.budget == facts["indexer_budget"] and wl.layers == facts["qsa_layers"]
     assert wl.budget * g.row_bytes * wl.layers == facts["selected_bytes_per_step"] == 48 * 2**20
+
+
+# --------------------------------------------------------------- append step
+
+def test_f16_encoder_matches_numpy():
+    """Nearest-value search equals numpy's float16 rounding (a library
+    routine): normal, subnormal, exact ties and the overflow edge."""
+    rng = np.random.default_rng(21)
+    xs = np.concatenate([
+        np.abs(rng.standard_normal(300)) * 0.01,
+        np.abs(rng.standard_normal(100)) * 1e-6,                 # subnormal range
+        (np.arange(1, 60) + 0.5) * 2.0 ** -24,                      # ties between subnormals
+        1.0 + (2 * np.arange(40) + 1) * 2.0 ** -11,                 # ties between normals
+        [0.0, 65504.0, 65519.0, 65520.0, 70000.0, 2.0 ** -14],
+    ]).astype(np.float64)
+    for x in xs:
+        with np.errstate(over="ignore"):
+            want = int(np.float16(x).view(np.uint16))
+        assert oracle.encode_f16(x) == want, x
+
+
+def test_e4m3_encoder_matches_torch_and_saturates():
+    """Nearest e4m3 (ties to even) equals torch's float8_e4m3fn rounding
+    inside the finite range, including every midpoint between neighbours;
+    magnitudes from 448 up clamp to 448 with the sign kept."""
+    torch = pytest.importorskip("torch")
+    vals = np.array([oracle.decode_e4m3(c) for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(22)
+    ys = np.concatenate([vals, mids, -mids, rng.uniform(-440, 440, 500), rng.standard_normal(200) * 0.01])
+    want = torch.from_numpy(ys.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.encode_e4m3(y) for y in ys.astype(np.float32)], np.uint8)
+    assert np.array_equal(got, want)
+    for y, code in [(448.0, 0x7E), (449.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE), (464.0, 0x7E)]:
+        assert oracle.encode_e4m3(y) == code
+
+
+def test_quantise_key_properties():
+    """Zero key -> zero scale and codes; a key whose largest magnitude is 448
+    has scale 1.0 and keeps its representable values exactly; in general the
+    largest element lands on +-448 and every element is reconstructed within
+    half an e4m3 step."""
+    z, s = oracle.quantise_key(np.zeros(64, np.float32))
+    assert s == 0 and not z.any()
+    vals = np.array([oracle.decode_e4m3(c) for c in range(0x7F)], np.float32)
+    x = np.random.default_rng(23).choice(vals, 64).astype(np.float32)
+    x[5] = 448.0
+    codes, s = oracle.quantise_key(x)
+    assert s == 0x3C00
+    assert np.array_equal(np.array([oracle.decode_e4m3(c) for c in codes], np.float32), x)
+    rng = np.random.default_rng(24)
+    for _ in range(20):
+        x = (rng.standard_normal(64) * rng.uniform(0.01, 10)).astype(np.float32)
+        codes, s = oracle.quantise_key(x)
+        sigma = oracle.decode_f16(s)
+        assert abs(sigma - np.abs(x).max() / 448) <= 2 ** -11 * sigma
+        dec = np.array([oracle.decode_e4m3(c) for c in codes]) * sigma
+        assert np.abs(codes & 0x7F).max() == 0x7E
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(x) / sigma, 2 ** -6))) - 3), 2 ** -9)
+        assert np.all(np.abs(dec - x) <= 0.5 * step * sigma * (1 + 1e-6) + 2 ** -11 * np.abs(x)), x
+
+
+def test_append_token_reference():
+    """The reference append writes the quantised key at row0 + ctx, the row at
+    the new slot and the page-table entry, and advances the length."""
+    ctx = np.array([3, 0])
+    row0 = np.array([0, 10])
+    pt = np.full((2, 8), -1, np.int32)
+    keys = [np.zeros((20, 64), np.uint8) for _ in range(2)]
+    scales = [np.zeros(20, np.uint16) for _ in range(2)]
+    pools = [np.zeros((6, 1024), np.uint16) for _ in range(2)]
+    rng = np.random.default_rng(25)
+    nk = [rng.standard_normal((2, 64)).astype(np.float32) for _ in range(2)]
+    nr = [rng.integers(0, 2 ** 16, (2, 1024)).astype(np.uint16) for _ in range(2)]
+    out = oracle.append_token(ctx, row0, pt, [4, 1], keys, scales, pools, nk, nr)
+    assert list(out) == [4, 1] and pt[0, 3] == 4 and pt[1, 0] == 1
+    for l in range(2):
+        c, s = oracle.quantise_key(nk[l][0])
+        assert np.array_equal(keys[l][3], c) and scales[l][3] == s
+        assert np.array_equal(pools[l][4], nr[l][0]) and np.array_equal(pools[l][1], nr[l][1])
+        assert not keys[l][4].any() and not pools[l][0].any()
