@@ -122,16 +122,17 @@ def pmc_summary(paths, workload):
     return "\n".join(lines) + "\n"
 
 
-def stats_summary(path, workload):
+def stats_summary(path, workload, op="step", bench_args=""):
     """Short text table of a rocprofv3 --stats kernel_stats.csv."""
     import csv
-    lines = ["# rocprofv3 kernel statistics of the default benchmark run, workload %s" % workload,
+    lines = ["# rocprofv3 kernel statistics of a benchmark run, workload %s" % workload,
              "# command (cd /tmp && export TMPDIR=/tmp first):",
-             "#   rocprofv3 --kernel-trace --stats -f csv -d OUT -o run -- python3 bench.py",
-             "# summary: python3 bench.py --stats-summary OUT/run_kernel_stats.csv",
-             "# averages over every launch of the run (warm-up, the overlapped steps and the two one-stream",
-             "# regions); under the tracer the streams hardly overlap, so they match the one-stream timing",
-             "",
+             "#   rocprofv3 --kernel-trace --stats -f csv -d OUT -o run -- python3 bench.py %s" % bench_args,
+             "# summary: python3 bench.py --stats-summary OUT/run_kernel_stats.csv %s" % bench_args]
+    if op == "step":
+        lines += ["# averages over every launch of the run (warm-up, the overlapped steps and the two one-stream",
+                  "# regions); under the tracer the streams hardly overlap, so they match the one-stream timing"]
+    lines += ["",
              "%8s %12s %10s %10s %10s %7s  %s" % ("calls", "total ms", "avg us", "min us", "max us", "%", "kernel")]
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
@@ -247,6 +248,69 @@ def cpu_baseline(wl, hi, seconds):
                       % (len(units), wl.name, units[0][0], units[-1][0], sum(times), mean, wl.batch)}
 
 
+def bench_append(args):
+    """The append step alone: one token enters every layer of every sequence
+    (quantised index row, KV row, page-table entry). The lengths are not
+    advanced, so every timed call does the same work."""
+    import numpy as np
+    import torch
+    import kv_cache_selection_amd as qsa
+    import qsa_synth as S
+    g = S.GEOM
+    wl = S.WORKLOADS[args.workload]
+    B, NL = wl.batch, wl.layers
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(wl.seed)
+    ctx = (np.array(S.ctx_lengths(wl)) // 2).astype(np.int32)     # the new token lands mid-sequence
+    cap = ctx + 1
+    row0 = np.concatenate([[0], np.cumsum(cap)[:-1]]).astype(np.int64)
+    n_rows, stride = int(cap.sum()), int(cap.max())
+    n_slots = 1 << 16
+    d_ctx = torch.from_numpy(ctx).to(dev)
+    d_row0 = torch.from_numpy(row0).to(dev)
+    d_pt = torch.zeros((B, stride), dtype=torch.int32, device=dev)
+    keys = [torch.zeros((n_rows, g.idx_dim), dtype=torch.uint8, device=dev) for _ in range(NL)]
+    scales = [torch.zeros(n_rows, dtype=torch.int16, device=dev) for _ in range(NL)]
+    pools = [torch.zeros((n_slots, g.row_elems), dtype=torch.int16, device=dev) for _ in range(NL)]
+    new_keys = [torch.from_numpy(rng.standard_normal((B, g.idx_dim)).astype(np.float32)).to(dev) for _ in range(NL)]
+    new_rows = [torch.from_numpy(rng.integers(-2 ** 15, 2 ** 15, (B, g.row_elems)).astype(np.int16)).to(dev)
+                for _ in range(NL)]
+    slots = torch.from_numpy(rng.choice(n_slots, B, replace=False).astype(np.int32)).to(dev)
+    cfg = qsa.make_config(wl.budget, wl.sink_blocks, wl.tail_tokens, g.sm_scale)
+    bt = qsa.make_batch(B, stride, d_ctx, d_row0, d_pt, stride, n_slots, n_rows)
+    lys = [qsa.make_append_layer(new_keys[l], new_rows[l], keys[l], scales[l], pools[l]) for l in range(NL)]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        qsa.qsa_append_token(cfg, bt, lys, qsa.QSA_KV_DEVICE, slots, d_pt, None, stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    # bytes the step must move: read the fp32 key and the bf16 row, write the
+    # 64 codes + 2-byte scale and the 2048-byte row, per sequence and layer
+    per = g.idx_dim * 4 + g.row_bytes + g.idx_dim + 2 + g.row_bytes
+    moved = B * NL * per + B * 4
+    gbs = moved / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "QSA append step: tokens entered into every QSA layer's cache per second",
+        "value": round(B / (us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "us_per_call": round(us, 3), "higher_is_better": True,
+        "dtype": "f32 key -> e4m3+f16 scale; bf16 row copy", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "layers": NL, "op": "append"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 6), "bytes_per_call": moved,
+                     "note": "one wavefront per sequence; the call is launch- and latency-bound"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,18 +321,28 @@ def main():
                     help="oracle time spent on the CPU baseline (0: skip)")
     ap.add_argument("--side-streams", type=int, default=3,
                     help="side streams of the overlapped schedule (default 3); 0: every kernel in order on one stream")
+    ap.add_argument("--op", choices=("step", "append"), default="step",
+                    help="step: the decode step (default); append: the append step alone")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=4, metavar="CSV", help=argparse.SUPPRESS)
     ap.add_argument("--stats-summary", metavar="CSV", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.stats_summary:
-        sys.stdout.write(stats_summary(args.stats_summary, args.workload))
+        extra = [a for a in sys.argv[1:] if a not in ("--stats-summary", args.stats_summary)]
+        sys.stdout.write(stats_summary(args.stats_summary, args.workload, args.op, " ".join(extra)))
         return
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(args.pmc_summary, args.workload))
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the QSA decode step runs on a single MI355X and this build has "
+              "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.op == "append":
+        bench_append(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the QSA decode step runs on a single MI355X and this build has "

@@ -195,6 +195,35 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                              size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
                              int32_t n_side);
 
+/* Step 0 of the next decode step (article, memory-ledger section: the index,
+ * its quantisation scales and the page layout are kept aligned; a token's
+ * logical address is mapped to the physical cache slot it was given): the
+ * token just decoded enters the cache of every QSA layer. For sequence b with
+ * t = batch->ctx_len[b] and s = new_slot[b] (a slot the caller allocated):
+ *   - layer l's index row idx_row0[b] + t receives new_idx_key[b] quantised
+ *     to e4m3 with one fp16 scale: sigma = fp16(amax / 448) and code_i =
+ *     e4m3(x_i / sigma), both divisions in binary32, rounding to nearest even,
+ *     magnitudes clamped to 448, all codes 0 when sigma is 0;
+ *   - layer l's pool row s receives new_kv_row[b] unchanged;
+ *   - page_table[b][t] = s, and ctx_len_out[b] = t + 1.
+ * A sequence whose t is outside [0, pt_stride), whose index row falls outside
+ * [0, n_idx_rows) or whose slot is outside [0, n_slots) is left untouched and
+ * gets ctx_len_out[b] = t. The caller keeps room after each sequence's index
+ * rows for the tokens it appends. ctx_len_out may be batch->ctx_len (updated
+ * in place) or NULL; page_table is the table to update (usually
+ * batch->page_table). At most 64 layers per call. */
+typedef struct {
+    const float *new_idx_key;   /* device f32 [batch][idx_dim]: the new token's index key */
+    const void *new_kv_row;     /* device bf16 [batch][row_elems]: its K and V, pool-row layout */
+    uint8_t *idx_keys;          /* this layer's index codes [n_idx_rows][idx_dim] */
+    uint16_t *idx_scales;       /* this layer's scales [n_idx_rows] */
+    void *kv_pool;              /* this layer's pool [n_slots][row_bytes], device or pinned host */
+} qsa_append_layer_t;
+
+qsa_status_t qsa_append_token(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_append_layer_t *layers,
+                              int32_t n_layers, qsa_kv_location_t kv_location, const int32_t *new_slot,
+                              int32_t *page_table, int32_t *ctx_len_out, qsa_stream_t stream);
+
 /* Workspace bytes needed by qsa_decode_step (n_layers >= 1); the same call
  * with n_layers = 1 covers qsa_topk_blocks and qsa_sparse_decode. */
 size_t qsa_workspace_size(const qsa_config_t *cfg, int32_t batch, int32_t max_ctx, int32_t n_layers,

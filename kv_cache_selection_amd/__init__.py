@@ -24,6 +24,7 @@ QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1
 
 # Every symbol include/libqsa.h declares.
 EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
+           "qsa_append_token",
            "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
 
 
@@ -46,6 +47,11 @@ class Batch(ctypes.Structure):
                 ("n_slots", ctypes.c_int64), ("n_idx_rows", ctypes.c_int64)]
 
 
+class AppendLayer(ctypes.Structure):
+    _fields_ = [("new_idx_key", ctypes.c_void_p), ("new_kv_row", ctypes.c_void_p), ("idx_keys", ctypes.c_void_p),
+                ("idx_scales", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p)]
+
+
 class Layer(ctypes.Structure):
     _fields_ = [("idx_keys", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p), ("q_idx", ctypes.c_void_p),
                 ("w_idx", ctypes.c_void_p), ("q", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p),
@@ -63,9 +69,11 @@ def _load():
     lib.qsa_topk_blocks.argtypes = [CP, BP, P, i64, P, P, P, P, sz, P]
     lib.qsa_gather_kv.argtypes = [CP, BP, P, P, P, i32, P, P, P]
     lib.qsa_sparse_decode.argtypes = [CP, i32, P, P, P, P, P, sz, P]
+    lib.qsa_append_token.argtypes = [CP, BP, ctypes.POINTER(AppendLayer), i32, i32, P, P, P, P]
     lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P,
                                     ctypes.POINTER(ctypes.c_void_p), i32]
-    for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step"):
+    for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
+              "qsa_append_token"):
         getattr(lib, f).restype = i32
     lib.qsa_workspace_size.argtypes = [CP, i32, i32, i32, i32]
     lib.qsa_workspace_size.restype = sz
@@ -181,3 +189,16 @@ def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes,
     _check("qsa_decode_step", lib.qsa_decode_step(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
                                                   kv_location, _p(workspace), workspace_bytes, _stream(compute),
                                                   sarr if side else None, len(side)))
+
+
+def make_append_layer(new_idx_key, new_kv_row, idx_keys, idx_scales, kv_pool) -> AppendLayer:
+    lay = AppendLayer(_p(new_idx_key), _p(new_kv_row), _p(idx_keys), _p(idx_scales), _p(kv_pool))
+    lay._keep = (new_idx_key, new_kv_row, idx_keys, idx_scales, kv_pool)
+    return lay
+
+
+def qsa_append_token(cfg, batch, layers, kv_location, new_slot, page_table, ctx_len_out=None, stream=None):
+    arr = (AppendLayer * len(layers))(*layers)
+    _check("qsa_append_token", lib.qsa_append_token(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
+                                                    kv_location, _p(new_slot), _p(page_table), _p(ctx_len_out),
+                                                    _stream(stream)))

@@ -312,6 +312,40 @@ qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uin
                                               attn_ws(workspace, w, 0), out, (hipStream_t)stream));
 }
 
+qsa_status_t qsa_append_token(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_append_layer_t *layers,
+                              int32_t n_layers, qsa_kv_location_t kv_location, const int32_t *new_slot,
+                              int32_t *page_table, int32_t *ctx_len_out, qsa_stream_t stream)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if (!batch || batch->batch < 1 || !batch->ctx_len || !batch->idx_row0 || batch->n_idx_rows < 0 ||
+        batch->pt_stride < 1 || batch->n_slots < 1)
+        return QSA_ERR_INVALID_ARGUMENT;
+    if (!layers || n_layers < 1 || n_layers > kMaxAppendLayers || !new_slot || !page_table ||
+        (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
+        return QSA_ERR_INVALID_ARGUMENT;
+    AppendLayers ly = {};
+    for (int l = 0; l < n_layers; l++) {
+        const qsa_append_layer_t &L = layers[l];
+        if (!L.new_idx_key || !L.new_kv_row || !L.idx_keys || !L.idx_scales || !L.kv_pool ||
+            !aligned(L.new_idx_key, 4) || !aligned(L.new_kv_row, 16) || !aligned(L.kv_pool, 16) ||
+            !aligned(L.idx_scales, 2))
+            return QSA_ERR_INVALID_ARGUMENT;
+        const void *pool = pool_device_ptr(L.kv_pool, kv_location);
+        if (!pool)
+            return QSA_ERR_INVALID_ARGUMENT;
+        ly.new_key[l] = L.new_idx_key;
+        ly.new_row[l] = static_cast<const uint8_t *>(L.new_kv_row);
+        ly.keys[l] = L.idx_keys;
+        ly.scales[l] = L.idx_scales;
+        ly.pool[l] = static_cast<uint8_t *>(const_cast<void *>(pool));
+    }
+    return hip_status(launch_append(ly, n_layers, batch->batch, batch->ctx_len, batch->idx_row0, batch->n_idx_rows,
+                                    batch->pt_stride, batch->n_slots, new_slot, page_table, ctx_len_out,
+                                    (hipStream_t)stream));
+}
+
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
                              size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,

@@ -122,4 +122,18 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
                                   int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s);
 
+// Per-layer pointers of the append step, passed by value.
+constexpr int kMaxAppendLayers = 64;
+struct AppendLayers {
+    const float *new_key[kMaxAppendLayers];     // [B][kIdxD]
+    const uint8_t *new_row[kMaxAppendLayers];   // [B][kRowBytes]
+    uint8_t *keys[kMaxAppendLayers];            // [rows][kIdxD]
+    uint16_t *scales[kMaxAppendLayers];         // [rows]
+    uint8_t *pool[kMaxAppendLayers];            // [n_slots][kRowBytes]
+};
+
+hipError_t launch_append(const AppendLayers &ly, int n_layers, int batch, const int32_t *ctx_len,
+                         const int64_t *row0, int64_t n_rows, int64_t pt_stride, int64_t n_slots,
+                         const int32_t *new_slot, int32_t *page_table, int32_t *ctx_out, hipStream_t s);
+
 } // namespace qsa

@@ -20,7 +20,7 @@ def _declared():
                                  txt, re.M)))
 
 
-def test_header_declares_the_five_calls_and_helpers():
+def test_header_declares_the_calls_and_helpers():
     names = _declared()
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
               "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string"):
@@ -155,3 +155,28 @@ def test_structs_keep_their_tensors_alive():
     assert rk() is not None and lay.idx_keys == rk().data_ptr()
     with pytest.raises(ValueError):
         qsa.make_batch(1, 4, FAKE, FAKE)          # index rows without their count
+
+
+def test_append_bad_arguments_rejected():
+    cfg = qsa.make_config(256)
+    E = qsa.QSA_ERR_INVALID_ARGUMENT
+    good = qsa.make_append_layer(FAKE, FAKE, FAKE, FAKE, FAKE)
+    cases = [
+        lambda: qsa.qsa_append_token(cfg, _batch(), [], 0, FAKE, FAKE),                          # no layers
+        lambda: qsa.qsa_append_token(cfg, _batch(), [good] * 65, 0, FAKE, FAKE),                 # too many
+        lambda: qsa.qsa_append_token(cfg, _batch(), [good], 0, None, FAKE),                      # no slots
+        lambda: qsa.qsa_append_token(cfg, _batch(), [good], 0, FAKE, None),                      # no table
+        lambda: qsa.qsa_append_token(cfg, _batch(), [good], 5, FAKE, FAKE),                      # bad location
+        lambda: qsa.qsa_append_token(cfg, _batch(), [qsa.make_append_layer(FAKE, FAKE + 8, FAKE, FAKE, FAKE)],
+                                     0, FAKE, FAKE),                                             # misaligned row
+        lambda: qsa.qsa_append_token(cfg, _batch(), [qsa.make_append_layer(None, FAKE, FAKE, FAKE, FAKE)],
+                                     0, FAKE, FAKE),
+        lambda: qsa.qsa_append_token(cfg, _batch(n_slots=0), [good], 0, FAKE, FAKE),
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(qsa.QsaError) as ei:
+            c()
+        assert ei.value.status == E, i
+    with pytest.raises(qsa.QsaError) as ei:
+        qsa.qsa_append_token(qsa.make_config(2048, head_dim=128), _batch(), [good], 0, FAKE, FAKE)
+    assert ei.value.status == qsa.QSA_ERR_UNSUPPORTED
