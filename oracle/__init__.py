@@ -286,3 +286,42 @@ def append_token(ctx, row0, pt, slot, keys_layers, scales_layers, pools, new_key
         pt[b, t] = slot[b]
         out[b] = t + 1
     return out
+
+
+# --------------------------------------------------------------- hot cache
+
+def hot_cache_update(hot_map, owner, tokens, b: int, H: int):
+    """One sequence-layer's hot-cache update before attention (test reference,
+    plain Python).
+
+    The memory-ledger section of "双卡RTX4090跑通Qwen3-Next" keeps only hot
+    rows on the GPU and moves missing rows back from pinned host memory on
+    demand, with a per-layer mapping from logical tokens to cache slots. Here
+    the cache of sequence b holds H rows, global slot ids b*H .. b*H + H - 1:
+      hot_map[t]  = slot id holding logical token t, or -1;
+      owner[h]    = logical token held by local slot h, or -1.
+    `tokens` are this step's selected tokens in ascending order. Tokens already
+    cached are hits and keep their slots. The misses, in ascending token
+    order, take the slots not used by a hit this step, in ascending slot
+    order; a slot's previous token loses its mapping. Returns the list of
+    (token, local slot) fetches, in that order. hot_map and owner are updated
+    in place."""
+    used = [False] * H
+    misses = []
+    for t in tokens:
+        h = int(hot_map[t])
+        if h >= 0:
+            used[h - b * H] = True
+        else:
+            misses.append(int(t))
+    free = [h for h in range(H) if not used[h]]
+    assert len(free) >= len(misses), "hot cache smaller than the selection"
+    fetches = []
+    for t, h in zip(misses, free):
+        old = int(owner[h])
+        if old >= 0:
+            hot_map[old] = -1
+        owner[h] = t
+        hot_map[t] = b * H + h
+        fetches.append((t, h))
+    return fetches

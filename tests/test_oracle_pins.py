@@ -464,3 +464,54 @@ def test_append_token_reference():
         assert np.array_equal(keys[l][3], c) and scales[l][3] == s
         assert np.array_equal(pools[l][4], nr[l][0]) and np.array_equal(pools[l][1], nr[l][1])
         assert not keys[l][4].any() and not pools[l][0].any()
+
+
+# ---------------------------------------------------------------- hot cache
+
+def test_hot_cache_worked_example():
+    """A hand-checked example, H = 4 slots of sequence b = 1 (ids 4..7)."""
+    H, b = 4, 1
+    hot_map = np.full(20, -1, np.int64)
+    owner = np.full(H, -1, np.int64)
+    assert oracle.hot_cache_update(hot_map, owner, [2, 5, 9], b, H) == [(2, 0), (5, 1), (9, 2)]
+    assert list(owner) == [2, 5, 9, -1] and hot_map[9] == 6
+    # 5 hits (slot 1), 3 and 11 miss: slots 0 and 2 are free of hits, so token
+    # 2 and token 9 are evicted; token 3 -> slot 0, token 11 -> slot 2
+    assert oracle.hot_cache_update(hot_map, owner, [3, 5, 11], b, H) == [(3, 0), (11, 2)]
+    assert list(owner) == [3, 5, 11, -1]
+    assert hot_map[2] == -1 and hot_map[9] == -1 and hot_map[3] == 4 and hot_map[11] == 6 and hot_map[5] == 5
+    # everything cached: no fetch
+    assert oracle.hot_cache_update(hot_map, owner, [3, 5], b, H) == []
+
+
+def test_hot_cache_invariants_random():
+    """Over many random steps: map and owner stay inverse to each other, every
+    selected token is cached after the update, hits never move, evicted
+    tokens were not selected, and the fetch count is the number of selected
+    tokens not cached before the step."""
+    rng = np.random.default_rng(41)
+    n_tok_ctx, H, b = 300, 48, 2
+    hot_map = np.full(n_tok_ctx, -1, np.int64)
+    owner = np.full(H, -1, np.int64)
+    prev = set()
+    for step in range(200):
+        k = int(rng.integers(0, H + 1))
+        keep = [t for t in sorted(prev) if rng.random() < 0.8][:k]
+        fresh = rng.choice(n_tok_ctx, k, replace=False).tolist()
+        toks = sorted(set(keep) | set(fresh))[:k]
+        before_map = hot_map.copy()
+        cached_before = {t for t in toks if before_map[t] >= 0}
+        fetches = oracle.hot_cache_update(hot_map, owner, toks, b, H)
+        assert len(fetches) == len(toks) - len(cached_before)
+        assert [t for t, _ in fetches] == sorted(set(toks) - cached_before)
+        for t in toks:
+            assert hot_map[t] >= 0 and owner[hot_map[t] - b * H] == t
+            if t in cached_before:
+                assert hot_map[t] == before_map[t]
+        for h in range(H):
+            if owner[h] >= 0:
+                assert hot_map[owner[h]] == b * H + h
+        assert (hot_map >= 0).sum() == (owner >= 0).sum()
+        evicted = {t for t in range(n_tok_ctx) if before_map[t] >= 0 and hot_map[t] < 0}
+        assert not evicted & set(toks)
+        prev = set(toks)
