@@ -150,6 +150,28 @@ qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uin
                                qsa_stream_t stream);
 
 /* One QSA layer's inputs and outputs for qsa_decode_step. */
+/* A hot row cache in HBM in front of a KV pool in pinned host memory
+ * (article, memory-ledger section: the full history stays in pinned host
+ * memory, the GPU keeps the hot rows, and missing rows are brought back on
+ * demand through a per-layer mapping of logical tokens to cache slots).
+ * One per layer. Sequence b owns cache rows b*hot_slots .. +hot_slots-1.
+ * In every decode step, after the selection:
+ *   - selected tokens already in the cache (hits) keep their rows;
+ *   - the others (misses), in ascending token order, take the rows that no
+ *     hit uses this step, in ascending row order, and unmap each row's
+ *     previous token;
+ *   - only the misses' rows are read from the host pool (over PCIe);
+ *   - attention reads every selected row from the cache.
+ * The result is identical to the uncached path's. Initialise map and owner
+ * with qsa_hot_reset. hot_slots >= budget_tokens and <= 16384. */
+typedef struct qsa_hot_cache {
+    void *rows;             /* device [batch][hot_slots][row_bytes] */
+    int32_t *map;           /* device [batch][pt_stride]: cache row id of each logical token, or -1 */
+    int32_t *owner;         /* device [batch][hot_slots]: logical token held by each row, or -1 */
+    int32_t hot_slots;      /* rows per sequence */
+    int32_t *n_miss;        /* optional device [batch]: rows fetched over PCIe in the last step */
+} qsa_hot_cache_t;
+
 typedef struct {
     const uint8_t *idx_keys;    /* [rows][idx_dim] */
     const uint16_t *idx_scales; /* [rows] */
@@ -161,6 +183,7 @@ typedef struct {
     float *out;                 /* [B][n_q_heads][head_dim] */
     int32_t *sel_blocks;        /* optional [B][K] copy of the selection, or NULL */
     int32_t *n_sel;             /* optional [B], or NULL */
+    const struct qsa_hot_cache *hot; /* optional hot row cache (pinned-host pools only), or NULL */
     void *score_events[2];      /* optional pair of timing-enabled hipEvent_t that take the begin
                                    and end timestamps of this layer's index-scoring kernel (it is
                                    then launched through hipExtLaunchKernel); NULL to skip */
@@ -194,6 +217,10 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
                              size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
                              int32_t n_side);
+
+/* Empties a hot cache: map[b][0..pt_stride) and owner[b][0..hot_slots) = -1
+ * for every sequence of the batch. */
+qsa_status_t qsa_hot_reset(const qsa_batch_t *batch, const qsa_hot_cache_t *hot, qsa_stream_t stream);
 
 /* Step 0 of the next decode step (article, memory-ledger section: the index,
  * its quantisation scales and the page layout are kept aligned; a token's

@@ -24,7 +24,7 @@ QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1
 
 # Every symbol include/libqsa.h declares.
 EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-           "qsa_append_token",
+           "qsa_append_token", "qsa_hot_reset",
            "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
 
 
@@ -56,7 +56,12 @@ class Layer(ctypes.Structure):
     _fields_ = [("idx_keys", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p), ("q_idx", ctypes.c_void_p),
                 ("w_idx", ctypes.c_void_p), ("q", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p),
                 ("page_table", ctypes.c_void_p), ("out", ctypes.c_void_p), ("sel_blocks", ctypes.c_void_p),
-                ("n_sel", ctypes.c_void_p), ("score_events", ctypes.c_void_p * 2)]
+                ("n_sel", ctypes.c_void_p), ("hot", ctypes.c_void_p), ("score_events", ctypes.c_void_p * 2)]
+
+
+class HotCache(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_void_p), ("map", ctypes.c_void_p), ("owner", ctypes.c_void_p),
+                ("hot_slots", ctypes.c_int32), ("n_miss", ctypes.c_void_p)]
 
 
 def _load():
@@ -70,10 +75,11 @@ def _load():
     lib.qsa_gather_kv.argtypes = [CP, BP, P, P, P, i32, P, P, P]
     lib.qsa_sparse_decode.argtypes = [CP, i32, P, P, P, P, P, sz, P]
     lib.qsa_append_token.argtypes = [CP, BP, ctypes.POINTER(AppendLayer), i32, i32, P, P, P, P]
+    lib.qsa_hot_reset.argtypes = [BP, ctypes.POINTER(HotCache), P]
     lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P,
                                     ctypes.POINTER(ctypes.c_void_p), i32]
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-              "qsa_append_token"):
+              "qsa_append_token", "qsa_hot_reset"):
         getattr(lib, f).restype = i32
     lib.qsa_workspace_size.argtypes = [CP, i32, i32, i32, i32]
     lib.qsa_workspace_size.restype = sz
@@ -167,12 +173,25 @@ def qsa_sparse_decode(cfg, batch_size, q, kv, n_tok, out, workspace, workspace_b
 
 
 def make_layer(idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, out, page_table=None, sel_blocks=None,
-               n_sel=None, score_events=None) -> Layer:
+               n_sel=None, score_events=None, hot=None) -> Layer:
     ev = (ctypes.c_void_p * 2)(*(score_events or (None, None)))
+    hot_ptr = ctypes.cast(ctypes.pointer(hot), ctypes.c_void_p).value if hot is not None else None
     lay = Layer(_p(idx_keys), _p(idx_scales), _p(q_idx), _p(w_idx), _p(q), _p(kv_pool), _p(page_table), _p(out),
-                _p(sel_blocks), _p(n_sel), ev)
-    lay._keep = (idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, page_table, out, sel_blocks, n_sel)
+                _p(sel_blocks), _p(n_sel), hot_ptr, ev)
+    lay._keep = (idx_keys, idx_scales, q_idx, w_idx, q, kv_pool, page_table, out, sel_blocks, n_sel, hot)
     return lay
+
+
+def make_hot_cache(rows, map_, owner, hot_slots, n_miss=None) -> HotCache:
+    """A layer's hot row cache: rows [B][hot_slots][row_bytes], map [B][pt_stride]
+    and owner [B][hot_slots] int32, optional n_miss [B] int32 (device)."""
+    hc = HotCache(_p(rows), _p(map_), _p(owner), int(hot_slots), _p(n_miss))
+    hc._keep = (rows, map_, owner, n_miss)
+    return hc
+
+
+def qsa_hot_reset(batch, hot, stream=None):
+    _check("qsa_hot_reset", lib.qsa_hot_reset(ctypes.byref(batch), ctypes.byref(hot), _stream(stream)))
 
 
 def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, side=None):

@@ -22,9 +22,10 @@ int n_split_of(int budget_tokens) { return (budget_tokens + kTPS - 1) / kTPS; }
 struct WsLayout {
     int B = 0, K = 0, n_blk_max = 0, n_slices = 0, n_layers = 0, n_split = 0, budget = 0;
     size_t hist = 0, zero_bytes = 0;
-    size_t cnt = 0, sdef = 0, scand = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0;
+    size_t cnt = 0, sdef = 0, scand = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0,
+           fetch = 0, nfetch = 0;
     size_t per_hist = 0, per_cnt = 0, per_sdef = 0, per_scand = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
-           per_ntok = 0, per_po = 0, per_plse = 0, per_stage = 0;
+           per_ntok = 0, per_po = 0, per_plse = 0, per_stage = 0, per_fetch = 0, per_nfetch = 0;
     size_t total = 0;
 };
 
@@ -51,6 +52,9 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.per_po = align_up((size_t)batch * kHq * w.n_split * kDh * 4);
     w.per_plse = align_up((size_t)batch * kHq * w.n_split * 4);
     w.per_stage = (loc == QSA_KV_HOST_PINNED) ? align_up((size_t)batch * w.budget * kRowBytes) : 0;
+    // hot-cache fetch lists (pinned-host pools only)
+    w.per_fetch = (loc == QSA_KV_HOST_PINNED) ? align_up((size_t)batch * w.budget * 8) : 0;
+    w.per_nfetch = (loc == QSA_KV_HOST_PINNED) ? align_up((size_t)batch * 4) : 0;
     size_t off = 0;
     w.hist = off;
     off += w.per_hist * n_layers;
@@ -77,6 +81,10 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     off += w.per_plse * n_layers;
     w.stage = off;
     off += w.per_stage * 2;
+    w.fetch = off;
+    off += w.per_fetch * n_layers;
+    w.nfetch = off;
+    off += w.per_nfetch * n_layers;
     w.total = off;
     return w;
 }
@@ -312,6 +320,17 @@ qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uin
                                               attn_ws(workspace, w, 0), out, (hipStream_t)stream));
 }
 
+qsa_status_t qsa_hot_reset(const qsa_batch_t *batch, const qsa_hot_cache_t *hot, qsa_stream_t stream)
+{
+    if (!batch || batch->batch < 1 || batch->pt_stride < 1 || !hot || !hot->map || !hot->owner ||
+        hot->hot_slots < 1 || hot->hot_slots > kMaxHot)
+        return QSA_ERR_INVALID_ARGUMENT;
+    hipError_t e = launch_fill_i32(hot->map, (int64_t)batch->batch * batch->pt_stride, -1, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = launch_fill_i32(hot->owner, (int64_t)batch->batch * hot->hot_slots, -1, (hipStream_t)stream);
+    return hip_status(e);
+}
+
 qsa_status_t qsa_append_token(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_append_layer_t *layers,
                               int32_t n_layers, qsa_kv_location_t kv_location, const int32_t *new_slot,
                               int32_t *page_table, int32_t *ctx_len_out, qsa_stream_t stream)
@@ -359,12 +378,24 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     if (!layers || n_layers < 1 || !workspace || !aligned(workspace, kAlign) ||
         (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
         return QSA_ERR_INVALID_ARGUMENT;
+    int n_hot = 0;
     for (int l = 0; l < n_layers; l++) {
         const qsa_layer_t &L = layers[l];
         if (!L.idx_keys || !L.idx_scales || !L.q_idx || !L.w_idx || !L.q || !L.kv_pool || !L.out ||
             !aligned(L.idx_keys, 16) || !aligned(L.q_idx, 8) || !aligned(L.kv_pool, 16))
             return QSA_ERR_INVALID_ARGUMENT;
+        if (L.hot) {
+            const qsa_hot_cache_t &H = *L.hot;
+            if (kv_location != QSA_KV_HOST_PINNED || !H.rows || !H.map || !H.owner || !aligned(H.rows, 16) ||
+                H.hot_slots < cfg->budget_tokens || H.hot_slots > kMaxHot ||
+                (int64_t)batch->batch * H.hot_slots > INT32_MAX)
+                return QSA_ERR_INVALID_ARGUMENT;
+            n_hot++;
+        }
     }
+    if (n_hot != 0 && n_hot != n_layers)
+        return QSA_ERR_INVALID_ARGUMENT;            // every layer cached, or none
+    const bool hot = n_hot > 0;
     if (n_side < 0 || n_side > QSA_MAX_SIDE_STREAMS || (n_side > 0 && !side))
         return QSA_ERR_INVALID_ARGUMENT;
     for (int k = 0; k < n_side; k++) {
@@ -387,7 +418,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     hipStream_t sc = (hipStream_t)compute;
     const bool offload = kv_location == QSA_KV_HOST_PINNED;
     const bool two_streams = n_side > 0;
-    const int NS = offload ? (n_side > 0 ? 1 : 0) : n_side;
+    const int NS = (offload && !hot) ? (n_side > 0 ? 1 : 0) : n_side;
     hipStream_t sx = NS > 0 ? (hipStream_t)side[0] : nullptr;
     std::vector<hipEvent_t> ev;
     if (two_streams && (st = get_events(3 * n_layers + NS + 1, ev)) != QSA_OK)
@@ -405,6 +436,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         SelectWs sw;
         AttnWs aw;
         void *stage;
+        int2 *fetch;
+        int32_t *nfetch;
     };
     std::vector<Lw> lw((size_t)n_layers);
     for (int l = 0; l < n_layers; l++) {
@@ -418,6 +451,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         x.sw = select_ws(workspace, w, l);
         x.aw = attn_ws(workspace, w, l);
         x.stage = offload ? at<void>(workspace, w.stage + w.per_stage * (l & 1)) : nullptr;
+        x.fetch = offload ? at<int2>(workspace, w.fetch + w.per_fetch * l) : nullptr;
+        x.nfetch = offload ? at<int32_t>(workspace, w.nfetch + w.per_nfetch * l) : nullptr;
     }
     auto score = [&](int l, hipStream_t s) {
         const qsa_layer_t &Ly = layers[l];
@@ -430,7 +465,25 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return launch_select(lw[l].bs, bs_stride, batch->ctx_len, B, batch->max_ctx, lw[l].sw, K, cfg->sink_blocks,
                              cfg->tail_tokens, lw[l].sel, lw[l].nsel, lw[l].ntok, s);
     };
+    // Hot cache: update the mapping, fetch the misses over PCIe, then attend
+    // the cached rows with the mapping as the page table.
+    auto attend_hot = [&](int l, hipStream_t s) {
+        const qsa_hot_cache_t &H = *layers[l].hot;
+        hipError_t r = launch_hot_update(lw[l].sel, lw[l].ntok, B, K, cfg->budget_tokens, batch->max_ctx, H.map,
+                                         batch->pt_stride, H.owner, H.hot_slots, lw[l].fetch, lw[l].nfetch, H.n_miss,
+                                         s);
+        if (r == hipSuccess)
+            r = launch_hot_fetch(lw[l].fetch, lw[l].nfetch, B, cfg->budget_tokens, lw[l].pt, batch->pt_stride,
+                                 batch->n_slots, batch->max_ctx, pools[l], H.rows, H.hot_slots, s);
+        if (r == hipSuccess)
+            r = launch_attention_paged(layers[l].q, H.rows, H.map, batch->pt_stride, (int64_t)B * H.hot_slots,
+                                       lw[l].sel, lw[l].ntok, batch->ctx_len, batch->max_ctx, B, K,
+                                       cfg->budget_tokens, cfg->sm_scale, lw[l].aw, layers[l].out, s);
+        return r;
+    };
     auto attend_paged = [&](int l, hipStream_t s) {
+        if (hot)
+            return attend_hot(l, s);
         return launch_attention_paged(layers[l].q, pools[l], lw[l].pt, batch->pt_stride, batch->n_slots, lw[l].sel,
                                       lw[l].ntok, batch->ctx_len, batch->max_ctx, B, K, cfg->budget_tokens,
                                       cfg->sm_scale, lw[l].aw, layers[l].out, s);
@@ -452,17 +505,17 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             e = score(l, sc);
             if (e == hipSuccess)
                 e = select(l, sc);
-            if (e == hipSuccess && !offload)
+            if (e == hipSuccess && (!offload || hot))
                 e = attend_paged(l, sc);
-            if (e == hipSuccess && offload)
+            if (e == hipSuccess && offload && !hot)
                 e = gather(l, sc);
-            if (e == hipSuccess && offload)
+            if (e == hipSuccess && offload && !hot)
                 e = attend_staged(l, sc);
         }
         return hip_status(e);
     }
 
-    if (!offload) {
+    if (!offload || hot) {
         // Pools in HBM: layer l's whole chain (score, select, attend, merge)
         // runs on stream l % (NS + 1) of {compute, side...}, after the
         // compute stream has cleared the histograms. Several chains are in

@@ -90,6 +90,33 @@ __device__ __forceinline__ int64_t safe_slot(int32_t slot, int64_t n_slots)
     return ((uint64_t)(int64_t)slot < (uint64_t)n_slots) ? (int64_t)slot : 0;
 }
 
+// Block-wide inclusive prefix sum of one uint32 per thread.
+template <int NT>
+__device__ inline uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [NT / 64] */, uint32_t *total)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d);
+        if (lane >= d)
+            v += o;
+    }
+    if (lane == 63)
+        sh[wave] = v;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w++) {
+        const uint32_t x = sh[w];
+        off += (w < wave) ? x : 0u;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return v + off;
+}
+
 // Kernel launchers (one translation unit each).
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
@@ -121,6 +148,17 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
                                   const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
                                   int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s);
+
+// Hot row cache in front of a pinned-host pool (hotcache.hip).
+constexpr int kMaxHot = 16384;                   // cache rows per sequence and layer
+
+hipError_t launch_hot_update(const int32_t *sel, const int32_t *n_tok, int batch, int budget_blocks,
+                             int budget_tokens, int max_ctx, int32_t *map, int64_t map_stride, int32_t *owner, int H,
+                             int2 *fetch, int32_t *n_fetch, int32_t *n_miss_out, hipStream_t s);
+hipError_t launch_hot_fetch(const int2 *fetch, const int32_t *n_fetch, int batch, int budget_tokens,
+                            const int32_t *pt, int64_t pt_stride, int64_t n_slots, int max_ctx, const void *pool,
+                            void *rows, int H, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 
 // Per-layer pointers of the append step, passed by value.
 constexpr int kMaxAppendLayers = 64;

@@ -66,33 +66,6 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t *counter)
     return base;
 }
 
-// Block-wide inclusive prefix sum of one uint32 per thread.
-template <int NT>
-__device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [NT / 64] */, uint32_t *total)
-{
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d);
-        if (lane >= d)
-            v += o;
-    }
-    if (lane == 63)
-        sh[wave] = v;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; w++) {
-        const uint32_t x = sh[w];
-        off += (w < wave) ? x : 0u;
-        tot += x;
-    }
-    __syncthreads();
-    *total = tot;
-    return v + off;
-}
-
 // Walk a histogram of NT * W bins from the top: the bin where the running
 // count first reaches `want`, and the count strictly above it. The histogram
 // is the sum of R copies laid out kHistBins apart.

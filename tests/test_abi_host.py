@@ -180,3 +180,20 @@ def test_append_bad_arguments_rejected():
     with pytest.raises(qsa.QsaError) as ei:
         qsa.qsa_append_token(qsa.make_config(2048, head_dim=128), _batch(), [good], 0, FAKE, FAKE)
     assert ei.value.status == qsa.QSA_ERR_UNSUPPORTED
+
+
+def test_hot_cache_bad_configurations_rejected():
+    cfg = qsa.make_config(256)
+    ok = qsa.make_hot_cache(FAKE, FAKE, FAKE, 256)
+    small = qsa.make_hot_cache(FAKE, FAKE, FAKE, 255)
+    huge = qsa.make_hot_cache(FAKE, FAKE, FAKE, 16385)
+    lay = lambda hc: qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, hot=hc)
+    E = qsa.QSA_ERR_INVALID_ARGUMENT
+    for layers, loc in [([lay(ok)], qsa.QSA_KV_DEVICE), ([lay(small)], qsa.QSA_KV_HOST_PINNED),
+                        ([lay(huge)], qsa.QSA_KV_HOST_PINNED), ([lay(ok), lay(None)], qsa.QSA_KV_HOST_PINNED)]:
+        with pytest.raises(qsa.QsaError) as ei:
+            qsa.qsa_decode_step(cfg, _batch(), layers, loc, FAKE, 1 << 30)
+        assert ei.value.status == E
+    with pytest.raises(qsa.QsaError) as ei:
+        qsa.qsa_hot_reset(_batch(), huge)
+    assert ei.value.status == E
