@@ -344,10 +344,6 @@ def main():
     if args.op == "append":
         bench_append(args)
         return
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the QSA decode step runs on a single MI355X and this build has "
-              "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
 
     import numpy as np
     import torch
@@ -376,14 +372,36 @@ def main():
     # select/attention (HBM pools) or the PCIe gather (host pools) overlap the scoring on side streams
     side = [torch.cuda.Stream() for _ in range(args.side_streams)]
 
-    def layers(events=None):
-        return [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l], di.out[l],
-                               None, sel[l], ns[l], events[l] if events else None) for l in range(NL)]
+    # Workloads that run many decode steps cycle through step_variants query
+    # sets (drifting indexer queries); the others repeat one step.
+    NV = max(1, wl.step_variants)
+    qv = []
+    for v in range(NV if NV > 1 else 0):
+        qi, qq = S.step_queries(wl, di.hi, v)
+        qv.append((torch.from_numpy(qi.view(np.int16)).to(dev), torch.from_numpy(qq.view(np.int16)).to(dev)))
+    hot, n_miss = None, None
+    if wl.hot_slots:
+        H = wl.hot_slots
+        n_miss = torch.zeros((NL, di.batch), dtype=torch.int32, device=dev)
+        hot = []
+        for l in range(NL):
+            hc = qsa.make_hot_cache(torch.zeros((di.batch, H, g.row_elems), dtype=torch.int16, device=dev),
+                                    torch.zeros((di.batch, di.pt_stride), dtype=torch.int32, device=dev),
+                                    torch.zeros((di.batch, H), dtype=torch.int32, device=dev), H, n_miss[l])
+            qsa.qsa_hot_reset(bt, hc)
+            hot.append(hc)
 
-    plain = layers()
+    def layers(v=0, events=None):
+        return [qsa.make_layer(di.keys[l], di.scales[l], qv[v][0][l] if qv else di.q_idx[l], di.w_idx[l],
+                               qv[v][1][l] if qv else di.q[l], di.pool[l], di.out[l], None, sel[l], ns[l],
+                               events[l] if events else None, hot[l] if hot else None) for l in range(NL)]
 
-    def step(lys):
-        qsa.qsa_decode_step(cfg, bt, lys, loc, ws, nws, stream, side)
+    plain = [layers(v) for v in range(NV)]
+    n_done = [0]
+
+    def step(lys, streams=True):
+        qsa.qsa_decode_step(cfg, bt, lys[n_done[0] % NV], loc, ws, nws, stream, side if streams else None)
+        n_done[0] += 1
 
     for _ in range(args.warmup):
         step(plain)
@@ -405,7 +423,7 @@ def main():
     if side:
         e0.record(stream)
         for _ in range(args.steps):
-            qsa.qsa_decode_step(cfg, bt, plain, loc, ws, nws, stream, None)
+            step(plain, streams=False)
         e1.record(stream)
         torch.cuda.synchronize()
         ms_serial = e0.elapsed_time(e1) / args.steps
@@ -416,13 +434,24 @@ def main():
     # GPU with the previous layer's selection and attention.
     hev = HipEvents()
     evs = [(hev.create(), hev.create()) for _ in range(NL)]
-    timed = layers(evs)
+    timed = [layers(v, evs) for v in range(NV)]
     durs = []
     for _ in range(args.steps):
-        qsa.qsa_decode_step(cfg, bt, timed, loc, ws, nws, stream, None)
+        step(timed, streams=False)
         torch.cuda.synchronize()
         durs.extend(hev.elapsed_ms(a, b) for (a, b) in evs)
     score_ms = float(np.mean(durs))
+
+    # Hot cache: rows fetched over PCIe per step, over one cycle of the query
+    # variants in the cache's steady state (untimed).
+    fetched = None
+    if hot:
+        tot = 0
+        for _ in range(NV):
+            step(plain)
+            torch.cuda.synchronize()
+            tot += int(n_miss.sum())
+        fetched = tot / NV
 
     ctx = di.hi.lay.ctx
     ntok = tokens_selected(sel.cpu().numpy(), ns.cpu().numpy(), ctx)
@@ -447,7 +476,8 @@ def main():
         "data": "synthetic (seeded SplitMix64 generator; planted relevant blocks)",
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(ctx.max()), "layers": NL,
                    "budget_tokens": wl.budget, "sink_blocks": wl.sink_blocks, "tail_tokens": wl.tail_tokens,
-                   "kv": "host-pinned" if di.kv_host else "hbm", "side_streams": args.side_streams},
+                   "kv": "host-pinned" if di.kv_host else "hbm", "side_streams": args.side_streams,
+                   "hot_cache_rows": wl.hot_slots},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(wl.name), "bytes_per_launch": idx_bytes_launch,
@@ -458,11 +488,16 @@ def main():
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes},
     }
     if di.kv_host:
-        # every gathered row crosses PCIe once per step
-        pcie_bytes = int(ntok.sum()) * g.row_bytes
+        # every gathered row crosses PCIe once per step (with a hot cache: the misses only)
+        pcie_bytes = int(ntok.sum()) * g.row_bytes if fetched is None else int(round(fetched)) * g.row_bytes
         pcie_gbs = pcie_bytes / (ms_step * 1e-3) / 1e9
         result["pcie"] = {"achieved": round(pcie_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                           "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "bytes_per_step": pcie_bytes}
+        if fetched is not None:
+            result["hot_cache"] = {"rows_per_layer": wl.hot_slots, "drift": wl.drift, "query_variants": NV,
+                                   "rows_fetched_per_step": round(fetched, 1),
+                                   "rows_selected_per_step": int(ntok.sum()),
+                                   "hit_rate": round(1.0 - fetched / max(int(ntok.sum()), 1), 4)}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, di.hi, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -30,7 +30,7 @@ M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
 
 # tensor ids of the named streams
-T_QIDX, T_W, T_Q, T_IDXKEY, T_PLANT_NOISE, T_KV = 1, 2, 3, 4, 5, 6
+T_QIDX, T_W, T_Q, T_IDXKEY, T_PLANT_NOISE, T_KV, T_DRIFT, T_STEP_Q = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def mix64(z):
@@ -166,6 +166,9 @@ class Workload:
     kv_host: bool = False
     ragged: tuple = None  # (lo, hi) inclusive for drawn lengths
     seed: int = 0
+    hot_slots: int = 0    # rows of a hot cache per sequence and layer (0: none)
+    drift: float = 0.0    # per-step noise on the indexer queries (see step_queries)
+    step_variants: int = 1
 
 
 WORKLOADS = {
@@ -176,6 +179,8 @@ WORKLOADS = {
     "batch8-256k": Workload("batch8-256k", 8, (262144,) * 8, 12, 2048, sink_blocks=1,
                             planted=32, seed=3),
     "offload-1m": Workload("offload-1m", 1, (1048576,), 12, 2048, planted=8, kv_host=True, seed=4),
+    "offload-1m-hot": Workload("offload-1m-hot", 1, (1048576,), 12, 2048, planted=8, kv_host=True, seed=4,
+                               hot_slots=4096, drift=0.25, step_variants=8),
 }
 
 
@@ -369,3 +374,26 @@ def host_pool_layer(hi: HostInputs, layer: int, g: Geometry = GEOM, chunk: int =
         e = min(a + chunk, hi.lay.n_slots)
         out[a:e] = kv_rows(hi.wl.seed, layer, np.arange(a, e), g)
     return out
+
+
+# ------------------------------------------------------------ decode steps
+
+def step_queries(wl: Workload, hi: HostInputs, variant: int, g: Geometry = GEOM):
+    """Queries of decode step `variant` (for workloads that run many steps):
+    indexer queries = bf16(q_idx + drift * N(0,1)), noise from stream
+    (seed, T_DRIFT, layer) at counters offset by the variant, so consecutive
+    steps select overlapping token sets; attention queries are fresh N(0,1)
+    draws from stream (seed, T_STEP_Q, layer). Returns (q_idx bits
+    [layers][B][4][64], q bits [layers][B][16][256])."""
+    B = wl.batch
+    nqi = B * g.idx_heads * g.idx_dim
+    nq = B * g.n_q_heads * g.head_dim
+    qi, qq = [], []
+    for l in range(wl.layers):
+        noise = normals(stream_key(wl.seed, T_DRIFT, l), np.arange(nqi, dtype=np.uint64) + np.uint64(variant * nqi))
+        base = bf16_bits_to_f32(hi.q_idx[l]).reshape(-1)
+        qi.append(f32_to_bf16_bits((base + np.float32(wl.drift) * noise).astype(np.float32))
+                  .reshape(B, g.idx_heads, g.idx_dim))
+        v = normals(stream_key(wl.seed, T_STEP_Q, l), np.arange(nq, dtype=np.uint64) + np.uint64(variant * nq))
+        qq.append(f32_to_bf16_bits(v).reshape(B, g.n_q_heads, g.head_dim))
+    return np.stack(qi), np.stack(qq)
