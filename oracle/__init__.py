@@ -325,3 +325,77 @@ def hot_cache_update(hot_map, owner, tokens, b: int, H: int):
         hot_map[t] = b * H + h
         fetches.append((t, h))
     return fetches
+
+
+# ------------------------------------------------------------ slot leases
+
+class SlotPoolModel:
+    """Reference model of slot leases (test infrastructure, plain Python).
+
+    The memory-ledger section of "双卡RTX4090跑通Qwen3-Next" lets requests
+    finish, be cancelled and hand their cache to new requests safely through
+    leases, generation markers and a tail ring buffer, after which the cache
+    capacity and slots return to their initial values. The model:
+      - the pool has n_slots physical slots, each with a generation counter
+        starting at 0; free slots are handed out lowest first;
+      - a lease (one request) may keep a tail ring of R slots, taken when the
+        lease opens: token t is written to ring slot ring[t % R]; when token
+        t >= R arrives, token t - R leaves the ring and moves to a body slot
+        taken from the pool (its row is copied ring -> body first);
+      - without a ring (R = 0) every token takes a body slot directly;
+      - closing a lease returns every slot it holds and increments each one's
+        generation, so that a page-table entry recorded under the old
+        generation is recognisably stale.
+    next_token returns the plan of one appended token:
+      (slot, generation, spill) with spill = None or (token, from_slot,
+      to_slot, to_generation)."""
+
+    def __init__(self, n_slots: int):
+        self.n = n_slots
+        self.gen = [0] * n_slots
+        self.free = list(range(n_slots))          # kept sorted
+        self.leases = {}
+        self.next_id = 1
+
+    def _take(self):
+        if not self.free:
+            raise MemoryError("pool exhausted")
+        return self.free.pop(0)
+
+    def _give(self, s):
+        self.gen[s] += 1
+        self.free.append(s)
+        self.free.sort()
+
+    def open(self, ring: int) -> int:
+        if ring > len(self.free):
+            raise MemoryError("pool exhausted")
+        lid = self.next_id
+        self.next_id += 1
+        self.leases[lid] = {"ring": [self._take() for _ in range(ring)], "body": [], "t": 0}
+        return lid
+
+    def next_token(self, lid: int):
+        L = self.leases[lid]
+        t, R = L["t"], len(L["ring"])
+        if R == 0:
+            s = self._take()
+            L["body"].append(s)
+            L["t"] += 1
+            return s, self.gen[s], None
+        spill = None
+        s = L["ring"][t % R]
+        if t >= R:
+            to = self._take()
+            L["body"].append(to)
+            spill = (t - R, s, to, self.gen[to])
+        L["t"] += 1
+        return s, self.gen[s], spill
+
+    def close(self, lid: int):
+        L = self.leases.pop(lid)
+        for s in L["ring"] + L["body"]:
+            self._give(s)
+
+    def free_slots(self) -> int:
+        return len(self.free)

@@ -515,3 +515,57 @@ def test_hot_cache_invariants_random():
         evicted = {t for t in range(n_tok_ctx) if before_map[t] >= 0 and hot_map[t] < 0}
         assert not evicted & set(toks)
         prev = set(toks)
+
+
+# ---------------------------------------------------------------- slot leases
+
+def test_slot_pool_model_worked_example():
+    """Ring of 2 slots, 4 tokens: tokens 0 and 1 use the ring; token 2 reuses
+    token 0's ring slot after token 0 moves to a body slot, and so on."""
+    m = oracle.SlotPoolModel(8)
+    a = m.open(2)                                       # ring = slots 0, 1
+    assert m.next_token(a) == (0, 0, None)
+    assert m.next_token(a) == (1, 0, None)
+    assert m.next_token(a) == (0, 0, (0, 0, 2, 0))      # token 0: slot 0 -> body slot 2
+    assert m.next_token(a) == (1, 0, (1, 1, 3, 0))
+    b = m.open(0)
+    assert m.next_token(b) == (4, 0, None)
+    assert m.free_slots() == 3
+    m.close(a)
+    assert m.free_slots() == 7 and m.gen[:5] == [1, 1, 1, 1, 0]
+    assert m.next_token(b) == (0, 1, None)              # lowest free slot, new generation
+
+
+def test_slot_pool_model_reclaims_everything():
+    """Random interleavings of opens, appends and closes: no slot is held by
+    two leases, and once every lease is closed the free count is back to the
+    pool size, with each used slot's generation advanced once per release."""
+    rng = np.random.default_rng(51)
+    m = oracle.SlotPoolModel(64)
+    releases = [0] * 64
+    open_ = []
+    for _ in range(2000):
+        r = rng.random()
+        if r < 0.15 or not open_:
+            try:
+                open_.append(m.open(int(rng.integers(0, 5))))
+            except MemoryError:
+                pass
+        elif r < 0.25:
+            lid = open_.pop(int(rng.integers(0, len(open_))))
+            held = m.leases[lid]["ring"] + m.leases[lid]["body"]
+            for s in held:
+                releases[s] += 1
+            m.close(lid)
+        else:
+            try:
+                m.next_token(open_[int(rng.integers(0, len(open_)))])
+            except MemoryError:
+                pass
+        held = [s for L in m.leases.values() for s in L["ring"] + L["body"]]
+        assert len(held) == len(set(held)) and len(held) + m.free_slots() == 64
+    for lid in open_:
+        for s in m.leases[lid]["ring"] + m.leases[lid]["body"]:
+            releases[s] += 1
+        m.close(lid)
+    assert m.free_slots() == 64 and m.gen == releases
