@@ -77,7 +77,8 @@ typedef enum {
     QSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment */
     QSA_ERR_UNSUPPORTED = 2,        /* geometry other than the compiled one */
     QSA_ERR_WORKSPACE_TOO_SMALL = 3,
-    QSA_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
+    QSA_ERR_HIP = 4,                /* a HIP launch or runtime call failed */
+    QSA_ERR_OUT_OF_SLOTS = 5        /* a slot pool has no free slot left */
 } qsa_status_t;
 
 typedef enum {
@@ -249,7 +250,65 @@ typedef struct {
 
 qsa_status_t qsa_append_token(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_append_layer_t *layers,
                               int32_t n_layers, qsa_kv_location_t kv_location, const int32_t *new_slot,
-                              int32_t *page_table, int32_t *ctx_len_out, qsa_stream_t stream);
+                              int32_t *page_table, int32_t *ctx_len_out, const uint32_t *new_gen,
+                              uint32_t *tok_gen, qsa_stream_t stream);
+/* (new_gen, tok_gen: optional device [batch] and [batch][pt_stride]; when
+ * tok_gen is given, tok_gen[b][t] receives new_gen[b] (0 without new_gen),
+ * the generation of the slot the token was placed in.) */
+
+/* ------------------------------------------------------------ slot leases
+ * Host-side slot pool for the KV pools (article, memory-ledger section:
+ * leases, generation markers and a tail ring buffer let requests end, be
+ * cancelled and hand their cache to new requests; afterwards the cache
+ * capacity and slots are back at their initial values).
+ *   - n physical slots, each with a generation counter starting at 0; free
+ *     slots are handed out lowest first;
+ *   - a lease (one request) may take a tail ring of R slots when it opens:
+ *     token t is placed in ring slot ring[t % R]; when token t >= R arrives,
+ *     token t - R leaves the ring for a body slot taken from the pool, and the
+ *     caller moves its rows there (qsa_move_tokens) before appending t;
+ *     without a ring every token takes a body slot;
+ *   - closing a lease returns all its slots and increments their generations.
+ * Host memory only; calls on one pool are serialised by a mutex. */
+typedef struct qsa_slot_pool qsa_slot_pool_t;
+
+typedef struct {
+    int64_t token;              /* the appended token's position in its sequence */
+    int32_t slot;               /* its slot */
+    uint32_t generation;        /* that slot's generation */
+    int64_t spill_token;        /* token leaving the tail ring, or -1 */
+    int32_t spill_from;         /* its ring slot (== slot), or -1 */
+    int32_t spill_to;           /* the body slot it moves to, or -1 */
+    uint32_t spill_generation;  /* that body slot's generation */
+} qsa_slot_plan_t;
+
+qsa_status_t qsa_pool_create(int64_t n_slots, qsa_slot_pool_t **pool);
+void qsa_pool_destroy(qsa_slot_pool_t *pool);
+/* QSA_ERR_OUT_OF_SLOTS when fewer than ring_slots slots are free. */
+qsa_status_t qsa_pool_open(qsa_slot_pool_t *pool, int32_t ring_slots, int32_t *lease);
+/* The next token of a lease; QSA_ERR_OUT_OF_SLOTS when a body slot is needed
+ * and none is free (the lease is then unchanged). */
+qsa_status_t qsa_pool_next(qsa_slot_pool_t *pool, int32_t lease, qsa_slot_plan_t *plan);
+qsa_status_t qsa_pool_close(qsa_slot_pool_t *pool, int32_t lease);
+int64_t qsa_pool_free_slots(qsa_slot_pool_t *pool);
+/* Copies every slot's generation into host gen_out[n_slots]. */
+qsa_status_t qsa_pool_generations(qsa_slot_pool_t *pool, uint32_t *gen_out);
+
+/* For each sequence b with token[b] >= 0: every layer's pool row of the
+ * token's slot (page_table[b][token[b]]) is copied to slot to_slot[b], the page
+ * table points the token there, and tok_gen[b][token[b]] = to_gen[b] when
+ * tok_gen is given. Entries out of range leave the sequence untouched.
+ * kv_pools: host array of n_layers pool pointers (device or pinned host).
+ * token int64 [batch], to_slot int32 [batch], to_gen uint32 [batch] or NULL. */
+qsa_status_t qsa_move_tokens(const qsa_batch_t *batch, void *const *kv_pools, int32_t n_layers,
+                             qsa_kv_location_t kv_location, const int64_t *token, const int32_t *to_slot,
+                             const uint32_t *to_gen, int32_t *page_table, uint32_t *tok_gen, qsa_stream_t stream);
+
+/* stale[b] = number of tokens t < ctx_len[b] whose slot page_table[b][t] is out
+ * of range or has a generation slot_gen[slot] other than the one recorded in
+ * tok_gen[b][t]. slot_gen: device [n_slots] copy of the pool's generations. */
+qsa_status_t qsa_check_generations(const qsa_batch_t *batch, const int32_t *page_table, const uint32_t *tok_gen,
+                                   const uint32_t *slot_gen, int32_t *stale, qsa_stream_t stream);
 
 /* Workspace bytes needed by qsa_decode_step (n_layers >= 1); the same call
  * with n_layers = 1 covers qsa_topk_blocks and qsa_sparse_decode. */

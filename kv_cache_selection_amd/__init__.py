@@ -19,12 +19,14 @@ except ImportError:  # pragma: no cover
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
-QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE_TOO_SMALL, QSA_ERR_HIP = range(5)
+QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE_TOO_SMALL, QSA_ERR_HIP, QSA_ERR_OUT_OF_SLOTS = range(6)
 QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1
 
 # Every symbol include/libqsa.h declares.
 EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-           "qsa_append_token", "qsa_hot_reset",
+           "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations",
+           "qsa_pool_create", "qsa_pool_destroy", "qsa_pool_open", "qsa_pool_next", "qsa_pool_close",
+           "qsa_pool_free_slots", "qsa_pool_generations",
            "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
 
 
@@ -52,6 +54,12 @@ class AppendLayer(ctypes.Structure):
                 ("idx_scales", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p)]
 
 
+class SlotPlan(ctypes.Structure):
+    _fields_ = [("token", ctypes.c_int64), ("slot", ctypes.c_int32), ("generation", ctypes.c_uint32),
+                ("spill_token", ctypes.c_int64), ("spill_from", ctypes.c_int32), ("spill_to", ctypes.c_int32),
+                ("spill_generation", ctypes.c_uint32)]
+
+
 class Layer(ctypes.Structure):
     _fields_ = [("idx_keys", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p), ("q_idx", ctypes.c_void_p),
                 ("w_idx", ctypes.c_void_p), ("q", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p),
@@ -74,12 +82,24 @@ def _load():
     lib.qsa_topk_blocks.argtypes = [CP, BP, P, i64, P, P, P, P, sz, P]
     lib.qsa_gather_kv.argtypes = [CP, BP, P, P, P, i32, P, P, P]
     lib.qsa_sparse_decode.argtypes = [CP, i32, P, P, P, P, P, sz, P]
-    lib.qsa_append_token.argtypes = [CP, BP, ctypes.POINTER(AppendLayer), i32, i32, P, P, P, P]
+    lib.qsa_append_token.argtypes = [CP, BP, ctypes.POINTER(AppendLayer), i32, i32, P, P, P, P, P, P]
+    lib.qsa_move_tokens.argtypes = [BP, ctypes.POINTER(ctypes.c_void_p), i32, i32, P, P, P, P, P, P]
+    lib.qsa_check_generations.argtypes = [BP, P, P, P, P, P]
+    lib.qsa_pool_create.argtypes = [i64, ctypes.POINTER(ctypes.c_void_p)]
+    lib.qsa_pool_destroy.argtypes = [P]
+    lib.qsa_pool_destroy.restype = None
+    lib.qsa_pool_open.argtypes = [P, i32, ctypes.POINTER(ctypes.c_int32)]
+    lib.qsa_pool_next.argtypes = [P, i32, ctypes.POINTER(SlotPlan)]
+    lib.qsa_pool_close.argtypes = [P, i32]
+    lib.qsa_pool_free_slots.argtypes = [P]
+    lib.qsa_pool_free_slots.restype = i64
+    lib.qsa_pool_generations.argtypes = [P, P]
     lib.qsa_hot_reset.argtypes = [BP, ctypes.POINTER(HotCache), P]
     lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P,
                                     ctypes.POINTER(ctypes.c_void_p), i32]
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-              "qsa_append_token", "qsa_hot_reset"):
+              "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_pool_create",
+              "qsa_pool_open", "qsa_pool_next", "qsa_pool_close", "qsa_pool_generations"):
         getattr(lib, f).restype = i32
     lib.qsa_workspace_size.argtypes = [CP, i32, i32, i32, i32]
     lib.qsa_workspace_size.restype = sz
@@ -216,8 +236,65 @@ def make_append_layer(new_idx_key, new_kv_row, idx_keys, idx_scales, kv_pool) ->
     return lay
 
 
-def qsa_append_token(cfg, batch, layers, kv_location, new_slot, page_table, ctx_len_out=None, stream=None):
+def qsa_append_token(cfg, batch, layers, kv_location, new_slot, page_table, ctx_len_out=None, stream=None,
+                     new_gen=None, tok_gen=None):
     arr = (AppendLayer * len(layers))(*layers)
     _check("qsa_append_token", lib.qsa_append_token(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
                                                     kv_location, _p(new_slot), _p(page_table), _p(ctx_len_out),
-                                                    _stream(stream)))
+                                                    _p(new_gen), _p(tok_gen), _stream(stream)))
+
+
+def qsa_move_tokens(batch, kv_pools, kv_location, token, to_slot, page_table, to_gen=None, tok_gen=None,
+                    stream=None):
+    arr = (ctypes.c_void_p * len(kv_pools))(*[_p(x) for x in kv_pools])
+    _check("qsa_move_tokens", lib.qsa_move_tokens(ctypes.byref(batch), arr, len(kv_pools), kv_location, _p(token),
+                                                  _p(to_slot), _p(to_gen), _p(page_table), _p(tok_gen),
+                                                  _stream(stream)))
+
+
+def qsa_check_generations(batch, page_table, tok_gen, slot_gen, stale, stream=None):
+    _check("qsa_check_generations", lib.qsa_check_generations(ctypes.byref(batch), _p(page_table), _p(tok_gen),
+                                                              _p(slot_gen), _p(stale), _stream(stream)))
+
+
+class SlotPool:
+    """The library's host-side slot pool (qsa_pool_*)."""
+
+    def __init__(self, n_slots: int):
+        h = ctypes.c_void_p()
+        _check("qsa_pool_create", lib.qsa_pool_create(int(n_slots), ctypes.byref(h)))
+        self._h = h
+        self.n_slots = int(n_slots)
+
+    def close_pool(self):
+        if self._h:
+            lib.qsa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close_pool()
+        except Exception:
+            pass
+
+    def open(self, ring: int) -> int:
+        lid = ctypes.c_int32()
+        _check("qsa_pool_open", lib.qsa_pool_open(self._h, int(ring), ctypes.byref(lid)))
+        return lid.value
+
+    def next_token(self, lease: int) -> SlotPlan:
+        plan = SlotPlan()
+        _check("qsa_pool_next", lib.qsa_pool_next(self._h, int(lease), ctypes.byref(plan)))
+        return plan
+
+    def close(self, lease: int):
+        _check("qsa_pool_close", lib.qsa_pool_close(self._h, int(lease)))
+
+    def free_slots(self) -> int:
+        return int(lib.qsa_pool_free_slots(self._h))
+
+    def generations(self):
+        import numpy as np
+        g = np.zeros(self.n_slots, np.uint32)
+        _check("qsa_pool_generations", lib.qsa_pool_generations(self._h, ctypes.c_void_p(g.ctypes.data)))
+        return g

@@ -235,6 +235,8 @@ const char *qsa_status_string(qsa_status_t s)
         return "workspace too small";
     case QSA_ERR_HIP:
         return "HIP runtime error";
+    case QSA_ERR_OUT_OF_SLOTS:
+        return "slot pool exhausted";
     }
     return "unknown status";
 }
@@ -333,7 +335,8 @@ qsa_status_t qsa_hot_reset(const qsa_batch_t *batch, const qsa_hot_cache_t *hot,
 
 qsa_status_t qsa_append_token(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_append_layer_t *layers,
                               int32_t n_layers, qsa_kv_location_t kv_location, const int32_t *new_slot,
-                              int32_t *page_table, int32_t *ctx_len_out, qsa_stream_t stream)
+                              int32_t *page_table, int32_t *ctx_len_out, const uint32_t *new_gen,
+                              uint32_t *tok_gen, qsa_stream_t stream)
 {
     qsa_status_t st = check_config(cfg);
     if (st != QSA_OK)
@@ -361,8 +364,39 @@ qsa_status_t qsa_append_token(const qsa_config_t *cfg, const qsa_batch_t *batch,
         ly.pool[l] = static_cast<uint8_t *>(const_cast<void *>(pool));
     }
     return hip_status(launch_append(ly, n_layers, batch->batch, batch->ctx_len, batch->idx_row0, batch->n_idx_rows,
-                                    batch->pt_stride, batch->n_slots, new_slot, page_table, ctx_len_out,
-                                    (hipStream_t)stream));
+                                    batch->pt_stride, batch->n_slots, new_slot, page_table, ctx_len_out, new_gen,
+                                    tok_gen, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_move_tokens(const qsa_batch_t *batch, void *const *kv_pools, int32_t n_layers,
+                             qsa_kv_location_t kv_location, const int64_t *token, const int32_t *to_slot,
+                             const uint32_t *to_gen, int32_t *page_table, uint32_t *tok_gen, qsa_stream_t stream)
+{
+    if (!batch || batch->batch < 1 || batch->pt_stride < 1 || batch->n_slots < 1 || !kv_pools || n_layers < 1 ||
+        n_layers > kMaxAppendLayers || !token || !to_slot || !page_table ||
+        (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
+        return QSA_ERR_INVALID_ARGUMENT;
+    AppendLayers ly = {};
+    for (int l = 0; l < n_layers; l++) {
+        if (!kv_pools[l] || !aligned(kv_pools[l], 16))
+            return QSA_ERR_INVALID_ARGUMENT;
+        const void *pool = pool_device_ptr(kv_pools[l], kv_location);
+        if (!pool)
+            return QSA_ERR_INVALID_ARGUMENT;
+        ly.pool[l] = static_cast<uint8_t *>(const_cast<void *>(pool));
+    }
+    return hip_status(launch_move(ly, n_layers, batch->batch, token, to_slot, to_gen, page_table, batch->pt_stride,
+                                  batch->n_slots, tok_gen, (hipStream_t)stream));
+}
+
+qsa_status_t qsa_check_generations(const qsa_batch_t *batch, const int32_t *page_table, const uint32_t *tok_gen,
+                                   const uint32_t *slot_gen, int32_t *stale, qsa_stream_t stream)
+{
+    if (!batch || batch->batch < 1 || !batch->ctx_len || batch->pt_stride < 1 || batch->n_slots < 1 ||
+        !page_table || !tok_gen || !slot_gen || !stale)
+        return QSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_check_gen(batch->ctx_len, batch->batch, batch->pt_stride, page_table, tok_gen, slot_gen,
+                                       batch->n_slots, stale, (hipStream_t)stream));
 }
 
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,

@@ -46,7 +46,9 @@ __global__ __launch_bounds__(64) void append_kernel(AppendLayers ly, int n_layer
                                                     const int64_t *__restrict__ row0, int64_t n_rows,
                                                     int64_t pt_stride, int64_t n_slots,
                                                     const int32_t *__restrict__ new_slot,
-                                                    int32_t *__restrict__ page_table, int32_t *__restrict__ ctx_out)
+                                                    int32_t *__restrict__ page_table, int32_t *__restrict__ ctx_out,
+                                                    const uint32_t *__restrict__ new_gen,
+                                                    uint32_t *__restrict__ tok_gen)
 {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
@@ -94,8 +96,11 @@ __global__ __launch_bounds__(64) void append_kernel(AppendLayers ly, int n_layer
         }
     }
     if (lane == 0) {
-        if (ok)
+        if (ok) {
             page_table[(int64_t)b * pt_stride + t] = slot;
+            if (tok_gen)
+                tok_gen[(int64_t)b * pt_stride + t] = new_gen ? new_gen[b] : 0u;
+        }
         if (ctx_out)
             ctx_out[b] = ok ? t + 1 : t;
     }
@@ -105,10 +110,11 @@ __global__ __launch_bounds__(64) void append_kernel(AppendLayers ly, int n_layer
 
 hipError_t launch_append(const AppendLayers &ly, int n_layers, int batch, const int32_t *ctx_len,
                          const int64_t *row0, int64_t n_rows, int64_t pt_stride, int64_t n_slots,
-                         const int32_t *new_slot, int32_t *page_table, int32_t *ctx_out, hipStream_t s)
+                         const int32_t *new_slot, int32_t *page_table, int32_t *ctx_out, const uint32_t *new_gen,
+                         uint32_t *tok_gen, hipStream_t s)
 {
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)batch), dim3(64), 0, s, ly, n_layers, ctx_len, row0, n_rows,
-                       pt_stride, n_slots, new_slot, page_table, ctx_out);
+                       pt_stride, n_slots, new_slot, page_table, ctx_out, new_gen, tok_gen);
     return hipGetLastError();
 }
 

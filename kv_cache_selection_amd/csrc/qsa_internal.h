@@ -172,6 +172,13 @@ struct AppendLayers {
 
 hipError_t launch_append(const AppendLayers &ly, int n_layers, int batch, const int32_t *ctx_len,
                          const int64_t *row0, int64_t n_rows, int64_t pt_stride, int64_t n_slots,
-                         const int32_t *new_slot, int32_t *page_table, int32_t *ctx_out, hipStream_t s);
+                         const int32_t *new_slot, int32_t *page_table, int32_t *ctx_out, const uint32_t *new_gen,
+                         uint32_t *tok_gen, hipStream_t s);
+hipError_t launch_move(const AppendLayers &ly, int n_layers, int batch, const int64_t *token, const int32_t *to_slot,
+                       const uint32_t *to_gen, int32_t *pt, int64_t pt_stride, int64_t n_slots, uint32_t *tok_gen,
+                       hipStream_t s);
+hipError_t launch_check_gen(const int32_t *ctx_len, int batch, int64_t pt_stride, const int32_t *pt,
+                            const uint32_t *tok_gen, const uint32_t *slot_gen, int64_t n_slots, int32_t *stale,
+                            hipStream_t s);
 
 } // namespace qsa

@@ -16,7 +16,7 @@ qsa = pytest.importorskip("kv_cache_selection_amd")
 
 def _declared():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:qsa_status_t|size_t|void|const char \*)\s*\*?\s*(qsa_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:qsa_status_t|size_t|void|int64_t|const char \*)\s*\*?\s*(qsa_\w+)\s*\(",
                                  txt, re.M)))
 
 
@@ -197,3 +197,54 @@ def test_hot_cache_bad_configurations_rejected():
     with pytest.raises(qsa.QsaError) as ei:
         qsa.qsa_hot_reset(_batch(), huge)
     assert ei.value.status == E
+
+
+def test_slot_pool_matches_the_reference_model():
+    """The library's slot pool (host C++) gives the oracle model's plans, free
+    counts and generations under random interleavings of opens, appends and
+    closes, including exhaustion."""
+    import numpy as np
+    oracle = pytest.importorskip("oracle")
+    rng = np.random.default_rng(52)
+    pool = qsa.SlotPool(48)
+    model = oracle.SlotPoolModel(48)
+    ids = []                                      # (library id, model id)
+    for _ in range(3000):
+        r = rng.random()
+        if r < 0.12 or not ids:
+            ring = int(rng.integers(0, 6))
+            try:
+                mid = model.open(ring)
+            except MemoryError:
+                with pytest.raises(qsa.QsaError) as ei:
+                    pool.open(ring)
+                assert ei.value.status == qsa.QSA_ERR_OUT_OF_SLOTS
+                continue
+            ids.append((pool.open(ring), mid))
+        elif r < 0.2:
+            lid, mid = ids.pop(int(rng.integers(0, len(ids))))
+            pool.close(lid)
+            model.close(mid)
+        else:
+            lid, mid = ids[int(rng.integers(0, len(ids)))]
+            try:
+                slot, gen, spill = model.next_token(mid)
+            except MemoryError:
+                with pytest.raises(qsa.QsaError) as ei:
+                    pool.next_token(lid)
+                assert ei.value.status == qsa.QSA_ERR_OUT_OF_SLOTS
+                continue
+            p = pool.next_token(lid)
+            assert (p.slot, p.generation) == (slot, gen)
+            if spill is None:
+                assert p.spill_token == -1 and p.spill_to == -1
+            else:
+                assert (p.spill_token, p.spill_from, p.spill_to, p.spill_generation) == spill
+        assert pool.free_slots() == model.free_slots()
+    for lid, mid in ids:
+        pool.close(lid)
+        model.close(mid)
+    assert pool.free_slots() == 48
+    assert list(pool.generations()) == model.gen
+    with pytest.raises(qsa.QsaError):
+        pool.close(12345)
