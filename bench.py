@@ -311,6 +311,93 @@ def bench_append(args):
     }), flush=True)
 
 
+def bench_lease(args):
+    """Slot leases: the host pool's throughput, and the two device calls that
+    go with it -- the generation check over a whole batch (a bandwidth-bound
+    scan of the page table and token generations) and a ring spill move."""
+    import numpy as np
+    import torch
+    import kv_cache_selection_amd as qsa
+    import qsa_synth as S
+    g = S.GEOM
+    wl = S.WORKLOADS[args.workload]
+    B, NL = wl.batch, wl.layers
+    dev = torch.device("cuda:0")
+    # host pool: 8 leases with a 64-slot tail ring, 4096 tokens each, then closed
+    pool = qsa.SlotPool(B * 4096 + B * 64)
+    t0 = time.perf_counter()
+    leases = [pool.open(64) for _ in range(B)]
+    n_ops = 0
+    for _ in range(4096):
+        for lid in leases:
+            pool.next_token(lid)
+            n_ops += 1
+    for lid in leases:
+        pool.close(lid)
+    host_s = time.perf_counter() - t0
+    assert pool.free_slots() == pool.n_slots
+    # generation check at the workload's full size
+    ctx = np.array(S.ctx_lengths(wl), np.int32)
+    stride = int(ctx.max())
+    n_slots = int(ctx.sum())
+    rng = np.random.default_rng(wl.seed)
+    perm = rng.permutation(n_slots).astype(np.int32)
+    pt = np.full((B, stride), -1, np.int32)
+    off = 0
+    for b in range(B):
+        pt[b, :ctx[b]] = perm[off:off + ctx[b]]
+        off += ctx[b]
+    slot_gen = rng.integers(0, 1 << 20, n_slots).astype(np.uint32)
+    tok_gen = np.where(pt >= 0, slot_gen[np.maximum(pt, 0)], 0).astype(np.uint32)
+    d_ctx = torch.from_numpy(ctx).to(dev)
+    d_pt = torch.from_numpy(pt).to(dev)
+    d_tg = torch.from_numpy(tok_gen.view(np.int32)).to(dev)
+    d_sg = torch.from_numpy(slot_gen.view(np.int32)).to(dev)
+    stale = torch.zeros(B, dtype=torch.int32, device=dev)
+    bt = qsa.make_batch(B, stride, d_ctx, torch.zeros(B, dtype=torch.int64, device=dev), d_pt, stride, n_slots, 0)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        qsa.qsa_check_generations(bt, d_pt, d_tg, d_sg, stale, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        qsa.qsa_check_generations(bt, d_pt, d_tg, d_sg, stale, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    check_us = e0.elapsed_time(e1) / args.steps * 1e3
+    assert int(stale.sum()) == 0
+    check_bytes = int(ctx.sum()) * 12          # page-table entry + token generation + slot generation
+    check_gbs = check_bytes / (check_us * 1e-6) / 1e9
+    # a ring spill: one token per sequence moves in every layer's pool
+    pools = [torch.zeros((1 << 16, g.row_elems), dtype=torch.int16, device=dev) for _ in range(NL)]
+    mpt = torch.from_numpy(rng.permutation(1 << 16)[:B * 64].reshape(B, 64).astype(np.int32)).to(dev)
+    mb = qsa.make_batch(B, 64, d_ctx, torch.zeros(B, dtype=torch.int64, device=dev), mpt, 64, 1 << 16, 0)
+    tok = torch.full((B,), 5, dtype=torch.int64, device=dev)
+    dst = torch.from_numpy(rng.permutation(1 << 16)[:B].astype(np.int32)).to(dev)
+    for _ in range(args.warmup):
+        qsa.qsa_move_tokens(mb, pools, qsa.QSA_KV_DEVICE, tok, dst, mpt, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        qsa.qsa_move_tokens(mb, pools, qsa.QSA_KV_DEVICE, tok, dst, mpt, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    move_us = e0.elapsed_time(e1) / args.steps * 1e3
+    print(json.dumps({
+        "metric": "QSA slot leases: generation check of a whole batch's page table",
+        "value": round(int(ctx.sum()) / (check_us * 1e-6) / 1e9, 3), "unit": "G tokens checked/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "us_per_check": round(check_us, 2), "higher_is_better": True,
+        "dtype": "int32 / uint32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "tokens": int(ctx.sum()), "op": "lease"},
+        "roofline": {"bound": "hbm", "achieved": round(check_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(check_gbs / HBM_PEAK_GBS, 4), "bytes_per_check": check_bytes},
+        "move_tokens_us": round(move_us, 2),
+        "host_pool": {"ops_per_s": round(n_ops / host_s), "ops": n_ops,
+                      "note": "open + next_token + close through ctypes, one host thread"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,8 +408,8 @@ def main():
                     help="oracle time spent on the CPU baseline (0: skip)")
     ap.add_argument("--side-streams", type=int, default=3,
                     help="side streams of the overlapped schedule (default 3); 0: every kernel in order on one stream")
-    ap.add_argument("--op", choices=("step", "append"), default="step",
-                    help="step: the decode step (default); append: the append step alone")
+    ap.add_argument("--op", choices=("step", "append", "lease"), default="step",
+                    help="step: the decode step (default); append: the append step alone; lease: slot leases")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=4, metavar="CSV", help=argparse.SUPPRESS)
     ap.add_argument("--stats-summary", metavar="CSV", help=argparse.SUPPRESS)
@@ -343,6 +430,9 @@ def main():
         sys.exit(2)
     if args.op == "append":
         bench_append(args)
+        return
+    if args.op == "lease":
+        bench_lease(args)
         return
 
     import numpy as np

@@ -204,21 +204,30 @@ __global__ __launch_bounds__(64) void move_kernel(AppendLayers ly, int n_layers,
     }
 }
 
-// stale[b] = number of tokens t < ctx_len[b] whose slot's generation differs
-// from the one recorded when the token was placed (or whose slot is out of
-// range). One workgroup per sequence.
-__global__ __launch_bounds__(256) void check_gen_kernel(const int32_t *__restrict__ ctx_len, int64_t pt_stride,
-                                                        const int32_t *__restrict__ pt,
-                                                        const uint32_t *__restrict__ tok_gen,
-                                                        const uint32_t *__restrict__ slot_gen, int64_t n_slots,
-                                                        int32_t *__restrict__ stale)
+// stale[b] += number of tokens t < ctx_len[b] in this workgroup's chunk whose
+// slot's generation differs from the one recorded when the token was placed
+// (or whose slot is out of range). Grid (chunks of kCheckChunk tokens, B);
+// stale[] is cleared first, and a chunk adds to it only when it found
+// something, so a clean cache costs no atomics.
+constexpr int kCheckThreads = 256;
+constexpr int kCheckChunk = 8192;
+
+__global__ __launch_bounds__(kCheckThreads) void check_gen_kernel(const int32_t *__restrict__ ctx_len,
+                                                                  int64_t pt_stride, const int32_t *__restrict__ pt,
+                                                                  const uint32_t *__restrict__ tok_gen,
+                                                                  const uint32_t *__restrict__ slot_gen,
+                                                                  int64_t n_slots, int32_t *__restrict__ stale)
 {
-    __shared__ uint32_t red[4];
-    const int b = blockIdx.x;
+    __shared__ uint32_t red[kCheckThreads / 64];
+    const int b = blockIdx.y;
     int64_t L = ctx_len[b];
     L = L < 0 ? 0 : (L > pt_stride ? pt_stride : L);
+    const int64_t t0 = (int64_t)blockIdx.x * kCheckChunk;
+    if (t0 >= L)
+        return;
+    const int64_t t1 = t0 + kCheckChunk < L ? t0 + kCheckChunk : L;
     uint32_t bad = 0;
-    for (int64_t t = threadIdx.x; t < L; t += 256) {
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += kCheckThreads) {
         const int32_t s = pt[(int64_t)b * pt_stride + t];
         const bool ok = s >= 0 && (int64_t)s < n_slots && slot_gen[s] == tok_gen[(int64_t)b * pt_stride + t];
         bad += ok ? 0u : 1u;
@@ -228,8 +237,13 @@ __global__ __launch_bounds__(256) void check_gen_kernel(const int32_t *__restric
     if ((threadIdx.x & 63) == 0)
         red[threadIdx.x >> 6] = bad;
     __syncthreads();
-    if (threadIdx.x == 0)
-        stale[b] = (int32_t)(red[0] + red[1] + red[2] + red[3]);
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0;
+        for (int w = 0; w < kCheckThreads / 64; w++)
+            tot += red[w];
+        if (tot)
+            atomicAdd(&stale[b], (int32_t)tot);
+    }
 }
 
 } // namespace
@@ -247,8 +261,12 @@ hipError_t launch_check_gen(const int32_t *ctx_len, int batch, int64_t pt_stride
                             const uint32_t *tok_gen, const uint32_t *slot_gen, int64_t n_slots, int32_t *stale,
                             hipStream_t s)
 {
-    hipLaunchKernelGGL(check_gen_kernel, dim3((unsigned)batch), dim3(256), 0, s, ctx_len, pt_stride, pt, tok_gen,
-                       slot_gen, n_slots, stale);
+    hipError_t e = launch_fill_i32(stale, batch, 0, s);
+    if (e != hipSuccess)
+        return e;
+    dim3 grid((unsigned)((pt_stride + kCheckChunk - 1) / kCheckChunk), (unsigned)batch);
+    hipLaunchKernelGGL(check_gen_kernel, grid, dim3(kCheckThreads), 0, s, ctx_len, pt_stride, pt, tok_gen, slot_gen,
+                       n_slots, stale);
     return hipGetLastError();
 }
 
