@@ -399,3 +399,24 @@ class SlotPoolModel:
 
     def free_slots(self) -> int:
         return len(self.free)
+
+
+# ----------------------------------------------------- multi-query scoring
+
+def multi_block_scores(keys, scales, q_idx, w, pos, n_blk_out, bt: int = 4):
+    """Block scores of several queries of one sequence against its index (for
+    prefill or chunked decode), each query seeing the tokens up to and
+    including its own position pos[i] (causal). Query i's block j is the max
+    of its token scores over the tokens of j that it sees, -inf when it sees
+    none of them. The scores themselves are the single-query scores of the
+    indexer (digest, mechanism section; the workload's formula), so each row
+    is `block_scores(token_scores(keys[:pos+1], ...))` padded with -inf.
+    Returns float32 [Q][n_blk_out]."""
+    Q = len(pos)
+    out = np.full((Q, n_blk_out), -np.inf, np.float32)
+    for i in range(Q):
+        n = int(pos[i]) + 1
+        ts = token_scores(keys[:n], scales[:n], q_idx[i], w[i])
+        bs = block_scores(ts, bt)
+        out[i, :len(bs)] = bs
+    return out

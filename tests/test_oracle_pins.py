@@ -569,3 +569,30 @@ def test_slot_pool_model_reclaims_everything():
             releases[s] += 1
         m.close(lid)
     assert m.free_slots() == 64 and m.gen == releases
+
+
+# ---------------------------------------------------------- multi-query scoring
+
+def test_multi_query_scores_are_causal_single_query_scores():
+    """Each query's row equals a brute-force loop over its visible tokens,
+    blocks past its position are -inf, and a block cut by the position keeps
+    the max over its visible tokens only."""
+    rng = np.random.default_rng(81)
+    L = 37
+    keys = rng.integers(0, 256, (L, 64)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0                     # no NaN codes
+    scales = np.float16(rng.uniform(0.01, 1, L)).view(np.uint16)
+    q_idx = (torch.from_numpy(rng.standard_normal((3, 4, 64)).astype(np.float32)).to(torch.bfloat16)
+             .view(torch.int16).numpy().view(np.uint16))
+    w = rng.uniform(0, 1, (3, 4)).astype(np.float32)
+    pos = np.array([0, 17, 36])
+    got = oracle.multi_block_scores(keys, scales, q_idx, w, pos, 10)
+    dec = np.array([[oracle.decode_e4m3(c) for c in row] for row in keys])
+    sig = np.array([oracle.decode_f16(s) for s in scales])
+    for i, p in enumerate(pos):
+        q = np.array([[oracle.decode_bf16(v) for v in row] for row in q_idx[i]])
+        s = np.array([sum(w[i, h] * max(0.0, sig[t] * float(q[h] @ dec[t])) for h in range(4)) for t in range(p + 1)])
+        for j in range(10):
+            lo, hi = 4 * j, min(4 * j + 4, p + 1)
+            want = np.float32(s[lo:hi].max()) if lo < hi else -np.inf
+            assert got[i, j] == pytest.approx(want, rel=1e-6, abs=1e-30), (i, j)
