@@ -133,6 +133,21 @@ qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                              int64_t bs_stride, int32_t *sel_blocks, int32_t *n_sel, int32_t *n_tok,
                              void *workspace, size_t workspace_bytes, qsa_stream_t stream);
 
+/* Step 1 for several queries per sequence (prefill or chunked decode): each
+ * of the n_queries queries of sequence b scores the index with the same
+ * formula, causally -- query i sees tokens t <= q_pos[b][i] -- and gets C4
+ * block scores: the max over the block's visible tokens, -inf for a block it
+ * does not see. Dense [4 Q x 64] x [64 x L] contraction on the matrix cores.
+ *   q_idx bf16 [B][Q][idx_heads][idx_dim], w_idx f32 [B][Q][idx_heads],
+ *   q_pos int32 [B][Q]; block_scores f32 [B][Q][bs_stride], written for
+ *   blocks j < ceil(ctx_len[b] / 4). n_queries in {4, 8, 16, 32, 64}.
+ * Each (b, i) row can go to qsa_topk_blocks as a sequence of its own with
+ * length q_pos[b][i] + 1. */
+qsa_status_t qsa_index_score_multi(const qsa_config_t *cfg, const qsa_batch_t *batch, int32_t n_queries,
+                                   const uint8_t *idx_keys, const uint16_t *idx_scales, const uint16_t *q_idx,
+                                   const float *w_idx, const int32_t *q_pos, float *block_scores, int64_t bs_stride,
+                                   qsa_stream_t stream);
+
 /* Step 4 (page-table translate + row gather). Copies the rows of the selected
  * tokens, in ascending logical order, from kv_pool ([n_slots][row_bytes];
  * device memory, or host-pinned memory for QSA_KV_HOST_PINNED) to kv_out

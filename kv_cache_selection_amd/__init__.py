@@ -24,7 +24,7 @@ QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1
 
 # Every symbol include/libqsa.h declares.
 EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-           "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations",
+           "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi",
            "qsa_pool_create", "qsa_pool_destroy", "qsa_pool_open", "qsa_pool_next", "qsa_pool_close",
            "qsa_pool_free_slots", "qsa_pool_generations",
            "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
@@ -83,6 +83,7 @@ def _load():
     lib.qsa_gather_kv.argtypes = [CP, BP, P, P, P, i32, P, P, P]
     lib.qsa_sparse_decode.argtypes = [CP, i32, P, P, P, P, P, sz, P]
     lib.qsa_append_token.argtypes = [CP, BP, ctypes.POINTER(AppendLayer), i32, i32, P, P, P, P, P, P]
+    lib.qsa_index_score_multi.argtypes = [CP, BP, i32, P, P, P, P, P, P, i64, P]
     lib.qsa_move_tokens.argtypes = [BP, ctypes.POINTER(ctypes.c_void_p), i32, i32, P, P, P, P, P, P]
     lib.qsa_check_generations.argtypes = [BP, P, P, P, P, P]
     lib.qsa_pool_create.argtypes = [i64, ctypes.POINTER(ctypes.c_void_p)]
@@ -98,7 +99,7 @@ def _load():
     lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P,
                                     ctypes.POINTER(ctypes.c_void_p), i32]
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-              "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_pool_create",
+              "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi", "qsa_pool_create",
               "qsa_pool_open", "qsa_pool_next", "qsa_pool_close", "qsa_pool_generations"):
         getattr(lib, f).restype = i32
     lib.qsa_workspace_size.argtypes = [CP, i32, i32, i32, i32]
@@ -298,3 +299,11 @@ class SlotPool:
         g = np.zeros(self.n_slots, np.uint32)
         _check("qsa_pool_generations", lib.qsa_pool_generations(self._h, ctypes.c_void_p(g.ctypes.data)))
         return g
+
+
+def qsa_index_score_multi(cfg, batch, n_queries, idx_keys, idx_scales, q_idx, w_idx, q_pos, block_scores, bs_stride,
+                          stream=None):
+    _check("qsa_index_score_multi", lib.qsa_index_score_multi(ctypes.byref(cfg), ctypes.byref(batch), int(n_queries),
+                                                              _p(idx_keys), _p(idx_scales), _p(q_idx), _p(w_idx),
+                                                              _p(q_pos), _p(block_scores), int(bs_stride),
+                                                              _stream(stream)))

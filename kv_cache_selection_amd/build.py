@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqsa.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "index_score.hip", "select.hip", "gather.hip", "attention.hip", "append.hip", "hotcache.hip", "slots.hip"]
+SOURCES = ["api.hip", "index_score.hip", "select.hip", "gather.hip", "attention.hip", "append.hip", "hotcache.hip", "slots.hip", "multiscore.hip"]
 
 HIPCC = os.environ.get("HIPCC", "hipcc")
 FLAGS = [

@@ -258,6 +258,26 @@ qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                          nullptr, 0, 0, 0, (hipStream_t)stream));
 }
 
+qsa_status_t qsa_index_score_multi(const qsa_config_t *cfg, const qsa_batch_t *batch, int32_t n_queries,
+                                   const uint8_t *idx_keys, const uint16_t *idx_scales, const uint16_t *q_idx,
+                                   const float *w_idx, const int32_t *q_pos, float *block_scores, int64_t bs_stride,
+                                   qsa_stream_t stream)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if ((st = check_batch(batch, true, false)) != QSA_OK)
+        return st;
+    if (!(n_queries == 4 || n_queries == 8 || n_queries == 16 || n_queries == 32 || n_queries == 64))
+        return QSA_ERR_UNSUPPORTED;
+    if (!idx_keys || !idx_scales || !q_idx || !w_idx || !q_pos || !block_scores || !aligned(idx_keys, 16) ||
+        !aligned(q_idx, 16) || !aligned(w_idx, 4) || bs_stride < (batch->max_ctx + kBT - 1) / kBT)
+        return QSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_multi_score(n_queries, idx_keys, idx_scales, q_idx, w_idx, q_pos, batch->ctx_len,
+                                         batch->idx_row0, batch->n_idx_rows, batch->batch, batch->max_ctx,
+                                         block_scores, bs_stride, (hipStream_t)stream));
+}
+
 qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, const float *block_scores,
                              int64_t bs_stride, int32_t *sel_blocks, int32_t *n_sel, int32_t *n_tok,
                              void *workspace, size_t workspace_bytes, qsa_stream_t stream)

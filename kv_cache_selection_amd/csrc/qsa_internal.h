@@ -117,6 +117,21 @@ __device__ inline uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [NT 
     return v + off;
 }
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+// Eight e4m3 codes (two dwords, lowest byte first) -> eight bf16 (exact). The
+// packed results are moved as whole 32-bit words: extracting single __bf16
+// elements of a pair lets the compiler duplicate the low half.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1)
+{
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+    const u32x4_t v = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Kernel launchers (one translation unit each).
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
@@ -148,6 +163,11 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
                                   const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
                                   int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s);
+
+// Several queries per sequence (multiscore.hip); n_queries in {4, 8, 16, 32, 64}.
+hipError_t launch_multi_score(int n_queries, const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
+                              const float *w_idx, const int32_t *q_pos, const int32_t *ctx_len, const int64_t *row0,
+                              int64_t n_rows, int batch, int max_ctx, float *out, int64_t bs_stride, hipStream_t s);
 
 // Hot row cache in front of a pinned-host pool (hotcache.hip).
 constexpr int kMaxHot = 16384;                   // cache rows per sequence and layer
