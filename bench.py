@@ -398,6 +398,73 @@ def bench_lease(args):
     }), flush=True)
 
 
+def bench_multi(args):
+    """Multi-query scoring (prefill / chunked decode): n_queries causal queries
+    per sequence, the chunk of positions at the end of each sequence, over the
+    workload's index (one layer)."""
+    import numpy as np
+    import torch
+    import kv_cache_selection_amd as qsa
+    import qsa_synth as S
+    from qsa_synth.device import DeviceInputs
+    g = S.GEOM
+    wl = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    di = DeviceInputs(wl, dev, layers=1, kv_host=False)
+    B, Q = di.batch, args.queries
+    rng = np.random.default_rng(wl.seed)
+    ctx = di.hi.lay.ctx
+    pos = np.stack([np.arange(int(ctx[b]) - Q, int(ctx[b])) for b in range(B)]).astype(np.int32)
+    q_idx = torch.from_numpy(S.f32_to_bf16_bits(rng.standard_normal((B, Q, g.idx_heads, g.idx_dim))
+                                                .astype(np.float32)).view(np.int16)).to(dev)
+    w = torch.from_numpy(rng.uniform(0, 1, (B, Q, g.idx_heads)).astype(np.float32)).to(dev)
+    d_pos = torch.from_numpy(pos).to(dev)
+    nb = (di.max_ctx + 3) // 4
+    out = torch.empty((B, Q, nb), dtype=torch.float32, device=dev)
+    cfg = qsa.make_config(wl.budget, wl.sink_blocks, wl.tail_tokens, g.sm_scale)
+    bt = qsa.make_batch(B, di.max_ctx, di.ctx, di.row0, di.pt, di.pt_stride, di.n_slots, di.n_rows)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        qsa.qsa_index_score_multi(cfg, bt, Q, di.keys[0], di.scales[0], q_idx, w, d_pos, out, nb, stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    tokens = int(ctx.sum())
+    moved = tokens * (g.index_row_bytes + Q)                  # index read + Q/4 fp32 block scores per token
+    flops = tokens * 512 * Q                                  # 4 heads x 64 dims x 2, per query and token
+    lane_ops = tokens * 9 * Q                                 # per query-token: 4 ReLU, 4 weight fma, 1 scale
+    gbs = moved / (us * 1e-6) / 1e9
+    tfs = flops / (us * 1e-6) / 1e12
+    tops = lane_ops / (us * 1e-6) / 1e12
+    mfma_peak = 2500.0                                        # dense bf16 TFLOP/s
+    valu_peak = 256 * 4 * 16 * 2.4e9 / 1e12                   # fp32 lane-ops/s without packed math: 39.3 T
+    hbm_bound = gbs / HBM_PEAK_GBS >= tfs / mfma_peak
+    print(json.dumps({
+        "metric": "QSA multi-query index scoring: query-token scores per second",
+        "value": round(tokens * Q / (us * 1e-6) / 1e9, 2), "unit": "G query-token scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "us_per_launch": round(us, 2), "higher_is_better": True,
+        "dtype": "fp8e4m3 keys, bf16 queries, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "ctx": int(ctx.max()), "queries": Q, "op": "multi"},
+        "roofline": ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": moved}
+                     if hbm_bound else
+                     {"bound": "mfma", "achieved": round(tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                      "frac": round(tfs / mfma_peak, 4), "flops_per_launch": flops}),
+        "mfma": {"achieved": round(tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(tfs / mfma_peak, 4)},
+        "valu": {"achieved": round(tops, 2), "peak": round(valu_peak, 1), "unit": "T fp32 lane-ops/s",
+                 "frac": round(tops / valu_peak, 4), "lane_ops_per_launch": lane_ops},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,8 +475,10 @@ def main():
                     help="oracle time spent on the CPU baseline (0: skip)")
     ap.add_argument("--side-streams", type=int, default=3,
                     help="side streams of the overlapped schedule (default 3); 0: every kernel in order on one stream")
-    ap.add_argument("--op", choices=("step", "append", "lease"), default="step",
-                    help="step: the decode step (default); append: the append step alone; lease: slot leases")
+    ap.add_argument("--op", choices=("step", "append", "lease", "multi"), default="step",
+                    help="step: the decode step (default); append: the append step alone; lease: slot leases; "
+                         "multi: multi-query scoring")
+    ap.add_argument("--queries", type=int, default=64, help="queries per sequence for --op multi")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=4, metavar="CSV", help=argparse.SUPPRESS)
     ap.add_argument("--stats-summary", metavar="CSV", help=argparse.SUPPRESS)
@@ -433,6 +502,9 @@ def main():
         return
     if args.op == "lease":
         bench_lease(args)
+        return
+    if args.op == "multi":
+        bench_multi(args)
         return
 
     import numpy as np
