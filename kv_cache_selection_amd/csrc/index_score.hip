@@ -39,9 +39,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                      // 8 waves: half as many histogram clears and flushes
 constexpr int kWaveTok = 64;                       // tokens per wave iteration
-constexpr int kWgTok = kThreads / 64 * kWaveTok;   // 256 tokens per workgroup iteration
+constexpr int kWgTok = kThreads / 64 * kWaveTok;   // 512 tokens per workgroup iteration
 
 template <bool kTokens, bool kHist>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(
@@ -246,10 +246,10 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
 {
     if (max_ctx <= 0)
         return hipSuccess;
-    // Tokens per workgroup: a multiple of 256, grown while the grid keeps
-    // at least 1024 workgroups (4 per CU) so every CU streams.
+    // Tokens per workgroup: a multiple of 512, grown while the grid keeps
+    // at least 512 workgroups (2 per CU, 16 waves) so every CU streams.
     int chunk = kWgTok;
-    while (chunk < 4096 && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 1024)
+    while (chunk < 8192 && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 512)
         chunk *= 2;
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)batch);
 #define QSA_SCORE_ARGS keys, scales, q_idx, w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, \

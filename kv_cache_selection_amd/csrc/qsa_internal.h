@@ -28,7 +28,7 @@ constexpr int kHistShift = 32 - kHistBits;
 // Each sequence's histogram is kept in kHistReps copies; scoring workgroup x
 // adds into copy x % kHistReps, so that no more than 1/kHistReps of a
 // sequence's workgroups queue up on the same counter. Readers sum the copies.
-constexpr int kHistReps = 4;
+constexpr int kHistReps = 2;
 
 // Attention: tokens per split.
 constexpr int kTPS = 128;

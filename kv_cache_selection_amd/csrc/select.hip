@@ -17,7 +17,7 @@
 //     index asc)); it writes them with their counts to the slice's own slot;
 //  3. finish_kernel: one workgroup per sequence gathers the slots through
 //     prefix offsets, picks the best need = K - |F| - |definite| candidates
-//     exactly with a radix select over the composites' remaining 52 bits
+//     exactly with a radix select over the composites' remaining 64 - 12 bits
 //     (11-bit digits, finishing by direct ranking once few are left), and
 //     writes the union in ascending order through an LDS bitmap, so the
 //     output needs no sort.
@@ -277,10 +277,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         T64 = 0;
     } else if (need > 0) {
         auto cand_at = [&](uint32_t i) -> uint64_t { return i < (uint32_t)kCandCap ? cand[i] : spill_b[i]; };
-        uint64_t pmask = 0xFFFull << 52;
+        // the candidates share the histogram bin: the composite's top kHistBits bits
+        uint64_t pmask = ((1ull << kHistBits) - 1ull) << (64 - kHistBits);
         uint64_t prefix = cand[0] & pmask;
         uint32_t want = need;
-        int shift = 52;
+        int shift = 64 - kHistBits;
         uint32_t *h = work;                         // 2048-bin histogram
         bool done = false;
         while (!done) {
