@@ -473,8 +473,9 @@ def main():
     ap.add_argument("--workload", default="batch8-256k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time spent on the CPU baseline (0: skip)")
-    ap.add_argument("--side-streams", type=int, default=3,
-                    help="side streams of the overlapped schedule (default 3); 0: every kernel in order on one stream")
+    ap.add_argument("--side-streams", type=int, default=None,
+                    help="side streams of the overlapped schedule (default: 1 for pools in HBM, whose schedule uses "
+                         "one; 3 for pools in pinned host memory); 0: every kernel in order on one stream")
     ap.add_argument("--op", choices=("step", "append", "lease", "multi"), default="step",
                     help="step: the decode step (default); append: the append step alone; lease: slot leases; "
                          "multi: multi-query scoring")
@@ -531,7 +532,9 @@ def main():
     nws = qsa.qsa_workspace_size(cfg, di.batch, di.max_ctx, NL, loc)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    # select/attention (HBM pools) or the PCIe gather (host pools) overlap the scoring on side streams
+    # the second scan stream (HBM pools) or the PCIe gather and per-layer chains (host pools) run on side streams
+    if args.side_streams is None:
+        args.side_streams = 3 if di.kv_host else 1
     side = [torch.cuda.Stream() for _ in range(args.side_streams)]
 
     # Workloads that run many decode steps cycle through step_variants query

@@ -569,10 +569,75 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return hip_status(e);
     }
 
-    if (!offload || hot) {
-        // Pools in HBM: layer l's whole chain (score, select, attend, merge)
-        // runs on stream l % (NS + 1) of {compute, side...}, after the
-        // compute stream has cleared the histograms. Several chains are in
+    if (!offload && !hot) {
+        // Pools in HBM. The index scans alternate over two streams (compute
+        // and side 0), so two run at once and the ramp and tail of one hide
+        // under the other. The selection and attention of up to
+        // kMaxChainLayers layers then run as one group: one launch of each
+        // kernel (collect, finish, attention, merge) for all of them, once
+        // the group's scans are done. A group costs one latency chain instead
+        // of one per layer, its attention is a single wide launch, and
+        // running the chains during the scans instead would only take CUs
+        // and bandwidth from the scans. The chains run on the compute stream;
+        // with more layers than one group and a second side stream they run
+        // on side 1, so that a group's chain overlaps the next group's scans.
+        const hipStream_t scan_s[2] = {sc, (hipStream_t)side[0]};
+        const hipStream_t cs = (NS >= 2 && n_layers > kMaxChainLayers) ? (hipStream_t)side[1] : sc;
+        // only the side streams this schedule uses are forked and joined
+        const int n_used = (NS >= 2 && n_layers > kMaxChainLayers) ? 2 : 1;
+        if (e == hipSuccess)
+            e = hipEventRecord(ev[0], sc);
+        for (int k = 0; k < n_used && e == hipSuccess; k++)
+            e = hipStreamWaitEvent((hipStream_t)side[k], ev[0], 0);
+        for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
+            const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
+            SelectLayers SL = {};
+            AttnLayers AL = {};
+            for (int i = 0; i < nl && e == hipSuccess; i++) {
+                const int l = l0 + i;
+                hipStream_t ss = scan_s[l & 1];
+                e = score(l, ss);
+                if (e == hipSuccess && ss != cs) {
+                    e = hipEventRecord(ev[1 + NS + l], ss);
+                    if (e == hipSuccess)
+                        e = hipStreamWaitEvent(cs, ev[1 + NS + l], 0);
+                }
+                SL.bs[i] = lw[l].bs;
+                SL.ws[i] = lw[l].sw;
+                SL.sel[i] = lw[l].sel;
+                SL.n_sel[i] = lw[l].nsel;
+                SL.n_tok[i] = lw[l].ntok;
+                AL.q[i] = layers[l].q;
+                AL.rows[i] = static_cast<const uint8_t *>(pools[l]);
+                AL.pt[i] = lw[l].pt;
+                AL.n_slots[i] = batch->n_slots;
+                AL.sel[i] = lw[l].sel;
+                AL.n_tok[i] = lw[l].ntok;
+                AL.part_o[i] = lw[l].aw.part_o;
+                AL.part_lse[i] = lw[l].aw.part_lse;
+                AL.out[i] = layers[l].out;
+            }
+            if (e == hipSuccess)
+                e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
+                                         cfg->tail_tokens, cs);
+            if (e == hipSuccess)
+                e = launch_attention_layers(true, AL, nl, batch->pt_stride, batch->max_ctx, B, K,
+                                            cfg->budget_tokens, cfg->sm_scale, lw[l0].aw.n_split, cs);
+        }
+        // The caller synchronises on the compute stream: join the side streams.
+        for (int k = 0; k < n_used && e == hipSuccess; k++) {
+            e = hipEventRecord(ev[1 + k], (hipStream_t)side[k]);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(sc, ev[1 + k], 0);
+        }
+        return hip_status(e);
+    }
+
+    if (hot) {
+        // Hot-cached pinned-host pools: layer l's whole chain (score, select,
+        // hot-cache update and fetch, attend, merge) runs on stream
+        // l % (NS + 1) of {compute, side...}, after the compute stream has
+        // cleared the histograms. Several chains are in
         // flight at once, so the latency-bound selection and attention of one
         // layer, and the ramp and tail of each scan, hide under the index
         // scans of the others. No more than kScansInFlight scans run at once

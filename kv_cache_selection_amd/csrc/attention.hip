@@ -70,13 +70,22 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool kPaged>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(
-    const uint16_t *__restrict__ q, const uint8_t *__restrict__ rows, const int32_t *__restrict__ pt,
-    int64_t pt_stride, int64_t n_slots, const int32_t *__restrict__ sel, const int32_t *__restrict__ n_tok,
-    int max_ctx, int budget_blocks, int budget_tokens, float sm_scale, float *__restrict__ part_o,
-    float *__restrict__ part_lse, int n_split)
+// Grid (n_split, kHkv * layers, B): workgroup (split s, KV head g of layer ly,
+// sequence b) with blockIdx.y = g + kHkv * ly.
+template <bool kPaged, int N>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx,
+                                                              int budget_blocks, int budget_tokens, float sm_scale,
+                                                              int n_split)
 {
+    const int ly = blockIdx.y / kHkv;
+    const uint16_t *__restrict__ q = Ls.q[ly];
+    const uint8_t *__restrict__ rows = Ls.rows[ly];
+    const int32_t *__restrict__ pt = Ls.pt[ly];
+    const int64_t n_slots = Ls.n_slots[ly];
+    const int32_t *__restrict__ sel = Ls.sel[ly];
+    const int32_t *__restrict__ n_tok = Ls.n_tok[ly];
+    float *__restrict__ part_o = Ls.part_o[ly];
+    float *__restrict__ part_lse = Ls.part_lse[ly];
     __shared__ __attribute__((aligned(16))) float ps[kWaves][kGroup][kWaveTok];  // the wave's probabilities
     __shared__ float sstat[kWaves][kGroup][2];      // per-wave (max, sum) for the workgroup merge
     // V tiles during the token loop, then the per-wave partial outputs
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     float(*so)[kGroup][kDh] = reinterpret_cast<float(*)[kGroup][kDh]>(smem);
 
     const int s = blockIdx.x;
-    const int g = blockIdx.y;
+    const int g = blockIdx.y % kHkv;
     const int b = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -308,14 +317,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 
 constexpr int kMergeUnroll = 16;
 
-// One workgroup per (sequence, head); thread d owns output dim d. Every
-// thread reads the (uniform) split LSEs itself and its column of partial
-// outputs in the same batch, so the whole merge is one round of loads: for
-// each batch of splits, the running max is raised and the sums rescaled.
-__global__ __launch_bounds__(kDh) void merge_kernel(const float *__restrict__ part_o,
-                                                    const float *__restrict__ part_lse, int n_split,
-                                                    float *__restrict__ out)
+// One workgroup per (sequence, head) and layer (grid (B * kHq, layers));
+// thread d owns output dim d. Every thread reads the (uniform) split LSEs
+// itself and its column of partial outputs in the same batch, so the whole
+// merge is one round of loads: for each batch of splits, the running max is
+// raised and the sums rescaled.
+template <int N>
+__global__ __launch_bounds__(kDh) void merge_kernel(const AttnLayersT<N> Ls, int n_split)
 {
+    const float *__restrict__ part_o = Ls.part_o[blockIdx.y];
+    const float *__restrict__ part_lse = Ls.part_lse[blockIdx.y];
+    float *__restrict__ out = Ls.out[blockIdx.y];
     const int bh = blockIdx.x;              // b * kHq + h
     const int tid = threadIdx.x;
     const float *lse = part_lse + (int64_t)bh * n_split;
@@ -353,24 +365,52 @@ __global__ __launch_bounds__(kDh) void merge_kernel(const float *__restrict__ pa
 
 } // namespace
 
-static hipError_t launch_merge(const AttnWs &ws, int batch, float *out, hipStream_t s)
+template <int N>
+static hipError_t launch_attention_n(bool paged, const AttnLayersT<N> &L, int n_layers, int64_t pt_stride,
+                                     int max_ctx, int batch, int budget_blocks, int budget_tokens, float sm_scale,
+                                     int n_split, hipStream_t s)
 {
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(batch * kHq)), dim3(kDh), 0, s, ws.part_o, ws.part_lse,
-                       ws.n_split, out);
+    dim3 grid((unsigned)n_split, (unsigned)(kHkv * n_layers), (unsigned)batch);
+    if (paged)
+        hipLaunchKernelGGL((attn_split_kernel<true, N>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
+                           budget_blocks, budget_tokens, sm_scale, n_split);
+    else
+        hipLaunchKernelGGL((attn_split_kernel<false, N>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
+                           budget_blocks, budget_tokens, sm_scale, n_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((merge_kernel<N>), dim3((unsigned)(batch * kHq), (unsigned)n_layers), dim3(kDh), 0, s, L,
+                       n_split);
     return hipGetLastError();
+}
+
+hipError_t launch_attention_layers(bool paged, const AttnLayers &L, int n_layers, int64_t pt_stride, int max_ctx,
+                                   int batch, int budget_blocks, int budget_tokens, float sm_scale, int n_split,
+                                   hipStream_t s)
+{
+    if (n_layers < 1 || n_layers > kMaxChainLayers)
+        return hipErrorInvalidValue;
+    if (n_layers > 1)
+        return launch_attention_n(paged, L, n_layers, pt_stride, max_ctx, batch, budget_blocks, budget_tokens,
+                                  sm_scale, n_split, s);
+    const AttnLayersT<1> L1 = {{L.q[0]},     {L.rows[0]},   {L.pt[0]},       {L.n_slots[0]}, {L.sel[0]},
+                               {L.n_tok[0]}, {L.part_o[0]}, {L.part_lse[0]}, {L.out[0]}};
+    return launch_attention_n(paged, L1, 1, pt_stride, max_ctx, batch, budget_blocks, budget_tokens, sm_scale,
+                              n_split, s);
 }
 
 hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int32_t *n_tok, int batch,
                                    int budget_tokens, float sm_scale, const AttnWs &ws, float *out, hipStream_t s)
 {
-    dim3 grid((unsigned)ws.n_split, (unsigned)kHkv, (unsigned)batch);
-    hipLaunchKernelGGL((attn_split_kernel<false>), grid, dim3(kThreads), 0, s, q,
-                       static_cast<const uint8_t *>(kv), nullptr, 0, 0, nullptr, n_tok, 0, 0, budget_tokens, sm_scale,
-                       ws.part_o, ws.part_lse, ws.n_split);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    return launch_merge(ws, batch, out, s);
+    AttnLayers L = {};
+    L.q[0] = q;
+    L.rows[0] = static_cast<const uint8_t *>(kv);
+    L.n_tok[0] = n_tok;
+    L.part_o[0] = ws.part_o;
+    L.part_lse[0] = ws.part_lse;
+    L.out[0] = out;
+    return launch_attention_layers(false, L, 1, 0, 0, batch, 0, budget_tokens, sm_scale, ws.n_split, s);
 }
 
 hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int32_t *pt, int64_t pt_stride,
@@ -378,14 +418,19 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
                                   int max_ctx, int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s)
 {
-    dim3 grid((unsigned)ws.n_split, (unsigned)kHkv, (unsigned)batch);
-    hipLaunchKernelGGL((attn_split_kernel<true>), grid, dim3(kThreads), 0, s, q,
-                       static_cast<const uint8_t *>(pool), pt, pt_stride, n_slots, sel, n_tok, max_ctx, budget_blocks,
-                       budget_tokens, sm_scale, ws.part_o, ws.part_lse, ws.n_split);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    return launch_merge(ws, batch, out, s);
+    (void)ctx_len;
+    AttnLayers L = {};
+    L.q[0] = q;
+    L.rows[0] = static_cast<const uint8_t *>(pool);
+    L.pt[0] = pt;
+    L.n_slots[0] = n_slots;
+    L.sel[0] = sel;
+    L.n_tok[0] = n_tok;
+    L.part_o[0] = ws.part_o;
+    L.part_lse[0] = ws.part_lse;
+    L.out[0] = out;
+    return launch_attention_layers(true, L, 1, pt_stride, max_ctx, batch, budget_blocks, budget_tokens, sm_scale,
+                                   ws.n_split, s);
 }
 
 } // namespace qsa

@@ -83,6 +83,38 @@ struct AttnWs {
     int n_split;
 };
 
+// One launch of the selection or attention kernels may cover several layers
+// (independent units of one step): the per-layer pointers travel in the
+// kernel arguments and the layer is a grid coordinate, so a group of layers
+// costs one latency chain instead of one per layer.
+// A single-layer launch passes tables of one entry (N = 1), so that its
+// kernel arguments stay small.
+constexpr int kMaxChainLayers = 16;
+
+template <int N>
+struct SelectLayersT {
+    const float *bs[N];                   // block scores [B][bs_stride]
+    SelectWs ws[N];
+    int32_t *sel[N];                      // [B][budget_blocks]
+    int32_t *n_sel[N];                    // [B]
+    int32_t *n_tok[N];                    // [B] or null
+};
+using SelectLayers = SelectLayersT<kMaxChainLayers>;
+
+template <int N>
+struct AttnLayersT {
+    const uint16_t *q[N];                 // [B][kHq][kDh] bf16
+    const uint8_t *rows[N];               // pool rows (paged) or staged rows [B][budget_tokens]
+    const int32_t *pt[N];                 // page table [B][pt_stride] (paged)
+    int64_t n_slots[N];                   // rows in the pool (paged)
+    const int32_t *sel[N];                // [B][budget_blocks] (paged)
+    const int32_t *n_tok[N];
+    float *part_o[N];
+    float *part_lse[N];
+    float *out[N];                        // [B][kHq][kDh] fp32
+};
+using AttnLayers = AttnLayersT<kMaxChainLayers>;
+
 // A physical slot read from a page table, forced into [0, n_slots) so that a
 // bad entry can never address memory outside the pool.
 __device__ __forceinline__ int64_t safe_slot(int32_t slot, int64_t n_slots)
@@ -149,6 +181,11 @@ hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int
                          int max_ctx, const SelectWs &ws, int budget_blocks, int sink_blocks, int tail_tokens,
                          int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s);
 
+// Selection of layers 0 .. n_layers - 1 of L (n_layers <= kMaxChainLayers).
+hipError_t launch_select_layers(const SelectLayers &L, int n_layers, int64_t bs_stride, const int32_t *ctx_len,
+                                int batch, int max_ctx, int budget_blocks, int sink_blocks, int tail_tokens,
+                                hipStream_t s);
+
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
                          const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out, int budget_blocks,
                          int budget_tokens, int32_t *n_tok, hipStream_t s);
@@ -163,6 +200,12 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
                                   const int32_t *sel, const int32_t *n_tok, const int32_t *ctx_len, int max_ctx,
                                   int batch, int budget_blocks, int budget_tokens, float sm_scale,
                                   const AttnWs &ws, float *out, hipStream_t s);
+
+// Attention (split kernel + merge) of layers 0 .. n_layers - 1 of L, through
+// the page tables (paged) or over staged rows.
+hipError_t launch_attention_layers(bool paged, const AttnLayers &L, int n_layers, int64_t pt_stride, int max_ctx,
+                                   int batch, int budget_blocks, int budget_tokens, float sm_scale, int n_split,
+                                   hipStream_t s);
 
 // Several queries per sequence (multiscore.hip); n_queries in {4, 8, 16, 32, 64}.
 hipError_t launch_multi_score(int n_queries, const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,

@@ -108,11 +108,18 @@ __device__ __forceinline__ int rest_to_take(int L, int n, int K, int sink_blocks
     return K - forced_count(n, sink_blocks, *tail_first);   // host guarantees >= 0
 }
 
-__global__ __launch_bounds__(kCollectThreads) void collect_kernel(
-    const float *__restrict__ block_scores, int64_t bs_stride, const int32_t *__restrict__ ctx_len, int max_ctx,
-    const uint32_t *__restrict__ hist, uint32_t *__restrict__ slot_count, int32_t *__restrict__ slot_def,
-    uint64_t *__restrict__ slot_cand, int n_slices, int K, int sink_blocks, int tail_tokens)
+// Grid (n_slices, B, layers).
+template <int N>
+__global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLayersT<N> Ls, int64_t bs_stride,
+                                                                  const int32_t *__restrict__ ctx_len, int max_ctx,
+                                                                  int n_slices, int K, int sink_blocks,
+                                                                  int tail_tokens)
 {
+    const float *__restrict__ block_scores = Ls.bs[blockIdx.z];
+    const uint32_t *__restrict__ hist = Ls.ws[blockIdx.z].hist;
+    uint32_t *__restrict__ slot_count = Ls.ws[blockIdx.z].slot_count;
+    int32_t *__restrict__ slot_def = Ls.ws[blockIdx.z].slot_def;
+    uint64_t *__restrict__ slot_cand = Ls.ws[blockIdx.z].slot_cand;
     __shared__ int32_t ldef[kSliceBlocks];          // 8 KB
     __shared__ uint64_t lcand[kSliceBlocks];        // 16 KB
     __shared__ uint32_t sh_scan[kCollectThreads / 64];
@@ -193,12 +200,21 @@ __device__ __forceinline__ int slot_of(const uint32_t *off, int ns, uint32_t p)
     return lo;
 }
 
-__global__ __launch_bounds__(kThreads) void finish_kernel(
-    const int32_t *__restrict__ ctx_len, int max_ctx, const uint32_t *__restrict__ slot_count,
-    const int32_t *__restrict__ slot_def, const uint64_t *__restrict__ slot_cand, int n_slices,
-    uint64_t *__restrict__ spill, int64_t spill_stride, int K, int sink_blocks, int tail_tokens,
-    int32_t *__restrict__ sel, int32_t *__restrict__ n_sel, int32_t *__restrict__ n_tok)
+// Grid (B, layers).
+template <int N>
+__global__ __launch_bounds__(kThreads) void finish_kernel(const SelectLayersT<N> Ls, const int32_t *__restrict__ ctx_len,
+                                                          int max_ctx, int n_slices, int K, int sink_blocks,
+                                                          int tail_tokens)
 {
+    const SelectWs &ws = Ls.ws[blockIdx.y];
+    const uint32_t *__restrict__ slot_count = ws.slot_count;
+    const int32_t *__restrict__ slot_def = ws.slot_def;
+    const uint64_t *__restrict__ slot_cand = ws.slot_cand;
+    uint64_t *__restrict__ spill = ws.spill;
+    const int64_t spill_stride = ws.spill_stride;
+    int32_t *__restrict__ sel = Ls.sel[blockIdx.y];
+    int32_t *__restrict__ n_sel = Ls.n_sel[blockIdx.y];
+    int32_t *__restrict__ n_tok = Ls.n_tok[blockIdx.y];
     extern __shared__ uint64_t smem64[];
     uint64_t *cand = smem64;                                            // [kCandCap]
     int32_t *defl = reinterpret_cast<int32_t *>(smem64 + kCandCap);     // [kDefCap]
@@ -412,25 +428,51 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
 
 } // namespace
 
-hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
-                         int max_ctx, const SelectWs &ws, int budget_blocks, int sink_blocks, int tail_tokens,
-                         int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s)
+template <int N>
+static hipError_t launch_select_n(const SelectLayersT<N> &L, int n_layers, int64_t bs_stride, const int32_t *ctx_len,
+                                  int batch, int max_ctx, int budget_blocks, int sink_blocks, int tail_tokens,
+                                  hipStream_t s)
 {
     const int n_blk_max = (max_ctx + kBT - 1) / kBT;
     const int n_slices = n_blk_max > 0 ? (n_blk_max + kSliceBlocks - 1) / kSliceBlocks : 1;
     if (n_blk_max > budget_blocks) {
-        dim3 grid((unsigned)n_slices, (unsigned)batch);
-        hipLaunchKernelGGL(collect_kernel, grid, dim3(kCollectThreads), 0, s, block_scores, bs_stride, ctx_len,
-                           max_ctx, ws.hist, ws.slot_count, ws.slot_def, ws.slot_cand, n_slices, budget_blocks,
-                           sink_blocks, tail_tokens);
+        dim3 grid((unsigned)n_slices, (unsigned)batch, (unsigned)n_layers);
+        hipLaunchKernelGGL((collect_kernel<N>), grid, dim3(kCollectThreads), 0, s, L, bs_stride, ctx_len, max_ctx,
+                           n_slices, budget_blocks, sink_blocks, tail_tokens);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)batch), dim3(kThreads), kSmemBytes, s, ctx_len, max_ctx,
-                       ws.slot_count, ws.slot_def, ws.slot_cand, n_slices, ws.spill, ws.spill_stride, budget_blocks,
-                       sink_blocks, tail_tokens, sel, n_sel, n_tok);
+    hipLaunchKernelGGL((finish_kernel<N>), dim3((unsigned)batch, (unsigned)n_layers), dim3(kThreads), kSmemBytes, s,
+                       L, ctx_len, max_ctx, n_slices, budget_blocks, sink_blocks, tail_tokens);
     return hipGetLastError();
+}
+
+hipError_t launch_select_layers(const SelectLayers &L, int n_layers, int64_t bs_stride, const int32_t *ctx_len,
+                                int batch, int max_ctx, int budget_blocks, int sink_blocks, int tail_tokens,
+                                hipStream_t s)
+{
+    if (n_layers < 1 || n_layers > kMaxChainLayers)
+        return hipErrorInvalidValue;
+    if (n_layers > 1)
+        return launch_select_n(L, n_layers, bs_stride, ctx_len, batch, max_ctx, budget_blocks, sink_blocks,
+                               tail_tokens, s);
+    const SelectLayersT<1> L1 = {{L.bs[0]}, {L.ws[0]}, {L.sel[0]}, {L.n_sel[0]}, {L.n_tok[0]}};
+    return launch_select_n(L1, 1, bs_stride, ctx_len, batch, max_ctx, budget_blocks, sink_blocks, tail_tokens, s);
+}
+
+hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
+                         int max_ctx, const SelectWs &ws, int budget_blocks, int sink_blocks, int tail_tokens,
+                         int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s)
+{
+    SelectLayers L = {};
+    L.bs[0] = block_scores;
+    L.ws[0] = ws;
+    L.sel[0] = sel;
+    L.n_sel[0] = n_sel;
+    L.n_tok[0] = n_tok;
+    return launch_select_layers(L, 1, bs_stride, ctx_len, batch, max_ctx, budget_blocks, sink_blocks, tail_tokens,
+                                s);
 }
 
 } // namespace qsa
