@@ -212,16 +212,22 @@ typedef struct {
  * double-buffered staging area.
  * Streams: `side` holds n_side extra streams (all distinct from `compute`);
  * with n_side = 0 (side may then be NULL) every kernel runs in order on
- * `compute`. With side streams the layers overlap:
- *   - HBM pools: after `compute` has cleared the step's scratch, layer l's
- *     whole chain (score, select, attend, merge) runs on stream
- *     l % (n_side + 1) of {compute, side[0], side[1], ...}, so several layers
- *     are in flight at once and the latency-bound parts of one hide under the
- *     index scans of the others; at most two index scans run at a time (this
- *     treats the layers as independent, which they are within one call);
- *   - host pools: side[0] gathers layer l over PCIe while `compute` scores
- *     and selects layer l+1 and attends layer l-1 (further side streams are
- *     not used).
+ * `compute`. With side streams the layers overlap (this treats the layers
+ * as independent, which they are within one call):
+ *   - HBM pools: after `compute` has cleared the step's scratch, the index
+ *     scans alternate between `compute` and side[0] (two at a time); then
+ *     the selection and attention of up to 16 layers run as one group, one
+ *     launch of each kernel for the whole group, on `compute`. With more
+ *     than 16 layers and n_side >= 2, each group's selection and attention
+ *     run on side[1] and overlap the next group's scans. Further side
+ *     streams are not used;
+ *   - host pools with a hot cache: layer l's whole chain (score, select,
+ *     cache update, miss fetch, attend, merge) runs on stream
+ *     l % (n_side + 1) of {compute, side[0], side[1], ...}, with at most two
+ *     index scans at a time;
+ *   - host pools without a hot cache: side[0] gathers layer l over PCIe
+ *     while `compute` scores and selects layer l+1 and attends layer l-1
+ *     (further side streams are not used).
  * The call leaves `compute` ordered after all of its work, so a sync on
  * `compute` covers the step. Results are bit-identical for every schedule.
  * The overlapped schedules record events owned by the library (one set per

@@ -120,8 +120,6 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
     uint32_t *__restrict__ slot_count = Ls.ws[blockIdx.z].slot_count;
     int32_t *__restrict__ slot_def = Ls.ws[blockIdx.z].slot_def;
     uint64_t *__restrict__ slot_cand = Ls.ws[blockIdx.z].slot_cand;
-    __shared__ int32_t ldef[kSliceBlocks];          // 8 KB
-    __shared__ uint64_t lcand[kSliceBlocks];        // 16 KB
     __shared__ uint32_t sh_scan[kCollectThreads / 64];
     __shared__ uint32_t sh_u[4];                    // 0,1: crossing bin / count above; 2,3: list lengths
 
@@ -155,6 +153,11 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
                                                                            (uint32_t)r, sh_scan, &sh_u[0], &sh_u[1]);
     const uint32_t bstar = sh_u[0];
 
+    // The slot is this workgroup's own: list entries go straight to it, at
+    // positions handed out by the LDS counters (one atomic per wave and list).
+    const int64_t slot = (int64_t)b * n_slices + slice;
+    int32_t *my_def = slot_def + slot * kSliceBlocks;
+    uint64_t *my_cand = slot_cand + slot * kSliceBlocks;
 #pragma unroll
     for (int k = 0; k < kCollectPer; k++) {
         const int j = j0 + k * kCollectThreads + tid;
@@ -169,21 +172,15 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
         const uint32_t pd = wave_append(is_def, &sh_u[2]);
         const uint32_t pc = wave_append(is_cand, &sh_u[3]);
         if (is_def)
-            ldef[pd] = j;                           // at most kSliceBlocks items per slice
+            my_def[pd] = j;                         // at most kSliceBlocks items per slice
         if (is_cand)
-            lcand[pc] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+            my_cand[pc] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
     }
     __syncthreads();
-    const uint32_t nd = sh_u[2], nc = sh_u[3];
-    const int64_t slot = (int64_t)b * n_slices + slice;
     if (tid == 0) {
-        slot_count[2 * slot] = nd;
-        slot_count[2 * slot + 1] = nc;
+        slot_count[2 * slot] = sh_u[2];
+        slot_count[2 * slot + 1] = sh_u[3];
     }
-    for (uint32_t i = tid; i < nd; i += kCollectThreads)
-        slot_def[slot * kSliceBlocks + i] = ldef[i];
-    for (uint32_t i = tid; i < nc; i += kCollectThreads)
-        slot_cand[slot * kSliceBlocks + i] = lcand[i];
 }
 
 // Index of the slot whose [off[s], off[s+1]) range holds p (off ascending, off[0] = 0).
