@@ -9,10 +9,13 @@ A step is one full pass of the hot path over all 12 layers (score -> select ->
 paged attention -> merge) through the C ABI; the metric is layer-steps/s.
 
 Prints one JSON line with the driver's fields plus:
-  roofline      the dominant kernel (index scoring): algorithmic bytes per
-                launch / its average duration, timed with HIP events recorded
-                on the compute stream around each scoring launch, with the
-                steps run on one stream so that each launch has the GPU alone;
+  roofline      the dominant kernel (index scoring) as the headline step
+                launches it: algorithmic bytes per launch / its average
+                duration, timed with HIP events taken by the launch itself.
+                With pools in HBM one launch scans all the layers (up to 16),
+                so a launch's bytes are the layers' index bytes together;
+  one_stream_score  the same for the per-layer scoring launch of the
+                one-stream step (each launch has the GPU alone);
   one_stream    the step time with every kernel in order on one stream;
   step_hbm      the whole step's algorithmic bytes (index scan + gathered
                 rows) over the step time, against the same HBM peak;
@@ -102,7 +105,9 @@ def pmc_summary(paths, workload):
              "source_sha256: %s" % score_source_hash(),
              "fetch_factor: %.4f" % f_fetch,
              "write_factor: %.4f" % f_write]
-    score = None
+    # the scoring kernel comes as a launch over a group of layers (the
+    # overlapped step) and as a launch per layer (the one-stream step)
+    score = {}
     rows = []
     for name in sorted(set(fetch) | set(write)):
         fv, wv = fetch.get(name, []), write.get(name, [])
@@ -111,10 +116,13 @@ def pmc_summary(paths, workload):
         byt = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
         rows.append((byt, name, len(fv), fk, wk))
         if SCORE_KERNEL in name:
-            score = byt
-    if score is None:
+            score["layer" if "ScoreLayersT<1>" in name else "group"] = byt
+    if not score:
         raise SystemExit("no %s dispatch in the counter files" % SCORE_KERNEL)
-    lines.append("traffic_bytes_per_launch: %d" % round(score))
+    if "group" in score:
+        lines.append("traffic_bytes_per_group_launch: %d" % round(score["group"]))
+    if "layer" in score:
+        lines.append("traffic_bytes_per_layer_launch: %d" % round(score["layer"]))
     lines.append("")
     lines.append("%14s %8s %14s %14s  %s" % ("bytes/dispatch", "dispatch", "FETCH KiB", "WRITE KiB", "kernel"))
     for byt, name, n, fk, wk in sorted(rows, reverse=True):
@@ -130,8 +138,8 @@ def stats_summary(path, workload, op="step", bench_args=""):
              "#   rocprofv3 --kernel-trace --stats -f csv -d OUT -o run -- python3 bench.py %s" % bench_args,
              "# summary: python3 bench.py --stats-summary OUT/run_kernel_stats.csv %s" % bench_args]
     if op == "step":
-        lines += ["# averages over every launch of the run (warm-up, the overlapped steps and the two one-stream",
-                  "# regions); under the tracer the streams hardly overlap, so they match the one-stream timing"]
+        lines += ["# averages over every launch of the run: warm-up and the timed regions, overlapped steps (one",
+                  "# scoring launch over all layers, <..., 16>) and one-stream steps (one launch per layer, <..., 1>)"]
     lines += ["",
              "%8s %12s %10s %10s %10s %7s  %s" % ("calls", "total ms", "avg us", "min us", "max us", "%", "kernel")]
     with open(path, newline="") as f:
@@ -142,9 +150,10 @@ def stats_summary(path, workload, op="step", bench_args=""):
     return "\n".join(lines) + "\n"
 
 
-def read_traffic(workload):
-    """The scoring kernel's measured HBM bytes per launch, or None when there
-    is no summary for this workload or the kernel changed since."""
+def read_traffic(workload, grouped):
+    """The scoring kernel's measured HBM bytes per launch (of a group of
+    layers, or of one layer), or None when there is no summary for this
+    workload or the kernel changed since."""
     path = pmc_file(workload)
     if not os.path.exists(path):
         return None
@@ -153,9 +162,10 @@ def read_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != score_source_hash() or "traffic_bytes_per_launch" not in kv:
+    key = "traffic_bytes_per_group_launch" if grouped else "traffic_bytes_per_layer_launch"
+    if kv.get("source_sha256") != score_source_hash() or key not in kv:
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    return int(kv[key])
 
 
 def copy_calibration():
@@ -593,19 +603,32 @@ def main():
         torch.cuda.synchronize()
         ms_serial = e0.elapsed_time(e1) / args.steps
 
-    # Timed region 3: the same steps on one stream with HIP events around
-    # every scoring launch, so that each launch is timed on its own (as a
-    # kernel-trace profile of this script sees it) rather than sharing the
-    # GPU with the previous layer's selection and attention.
+    # Timed region 3: the headline schedule again, with HIP events around
+    # the scoring launches. With pools in HBM and side streams one launch
+    # scans all the layers (up to 16), and the first layer's events time it;
+    # otherwise every layer's scan is a launch of its own.
     hev = HipEvents()
+    grouped = bool(side) and not di.kv_host and NL <= 16
     evs = [(hev.create(), hev.create()) for _ in range(NL)]
-    timed = [layers(v, evs) for v in range(NV)]
+    ev_used = evs[:1] if grouped else evs
+    timed = [layers(v, ev_used + [None] * (NL - len(ev_used))) for v in range(NV)]
     durs = []
     for _ in range(args.steps):
-        step(timed, streams=False)
+        step(timed)
         torch.cuda.synchronize()
-        durs.extend(hev.elapsed_ms(a, b) for (a, b) in evs)
+        durs.extend(hev.elapsed_ms(a, b) for (a, b) in ev_used)
     score_ms = float(np.mean(durs))
+    layers_per_launch = NL if grouped else 1
+
+    # Timed region 4: one-stream steps with events around every per-layer
+    # scoring launch (each scan alone, as a kernel-trace profile sees it).
+    durs1 = []
+    timed1 = [layers(v, evs) for v in range(NV)]
+    for _ in range(args.steps):
+        step(timed1, streams=False)
+        torch.cuda.synchronize()
+        durs1.extend(hev.elapsed_ms(a, b) for (a, b) in evs)
+    score1_ms = float(np.mean(durs1))
 
     # Hot cache: rows fetched over PCIe per step, over one cycle of the query
     # variants in the cache's steady state (untimed).
@@ -620,9 +643,11 @@ def main():
 
     ctx = di.hi.lay.ctx
     ntok = tokens_selected(sel.cpu().numpy(), ns.cpu().numpy(), ctx)
-    idx_bytes_launch = int(ctx.sum()) * g.index_row_bytes
-    step_bytes = idx_bytes_launch * NL + int(ntok.sum()) * g.row_bytes
+    idx_bytes_layer = int(ctx.sum()) * g.index_row_bytes
+    idx_bytes_launch = idx_bytes_layer * layers_per_launch
+    step_bytes = idx_bytes_layer * NL + int(ntok.sum()) * g.row_bytes
     achieved = idx_bytes_launch / (score_ms * 1e-3) / 1e9
+    achieved1 = idx_bytes_layer / (score1_ms * 1e-3) / 1e9
     step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     value = NL / (ms_step * 1e-3)
 
@@ -645,8 +670,14 @@ def main():
                    "hot_cache_rows": wl.hot_slots},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(wl.name), "bytes_per_launch": idx_bytes_launch,
+                     "traffic": read_traffic(wl.name, grouped), "bytes_per_launch": idx_bytes_launch,
+                     "layers_per_launch": layers_per_launch,
                      "avg_launch_us": round(score_ms * 1e3, 2)},
+        # the per-layer scoring launch of the one-stream step, each launch alone
+        "one_stream_score": {"achieved": round(achieved1, 1), "unit": "GB/s",
+                             "frac": round(achieved1 / HBM_PEAK_GBS, 4), "bytes_per_launch": idx_bytes_layer,
+                             "avg_launch_us": round(score1_ms * 1e3, 2),
+                             "traffic": read_traffic(wl.name, False)},
         "one_stream": {"ms_per_step": round(ms_serial if ms_serial is not None else ms_step, 4),
                        "value": round(NL / ((ms_serial if ms_serial is not None else ms_step) * 1e-3), 2)},
         "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -202,7 +202,10 @@ typedef struct {
     const struct qsa_hot_cache *hot; /* optional hot row cache (pinned-host pools only), or NULL */
     void *score_events[2];      /* optional pair of timing-enabled hipEvent_t that take the begin
                                    and end timestamps of this layer's index-scoring kernel (it is
-                                   then launched through hipExtLaunchKernel); NULL to skip */
+                                   then launched through hipExtLaunchKernel); NULL to skip. Where
+                                   one launch scans a group of layers (HBM pools with side
+                                   streams), the group's first layer's events time that launch
+                                   and the other layers' events are not recorded */
 } qsa_layer_t;
 
 /* The whole decode step over n_layers independent QSA layers: for each layer,
@@ -214,13 +217,11 @@ typedef struct {
  * with n_side = 0 (side may then be NULL) every kernel runs in order on
  * `compute`. With side streams the layers overlap (this treats the layers
  * as independent, which they are within one call):
- *   - HBM pools: after `compute` has cleared the step's scratch, the index
- *     scans alternate between `compute` and side[0] (two at a time); then
- *     the selection and attention of up to 16 layers run as one group, one
- *     launch of each kernel for the whole group, on `compute`. With more
- *     than 16 layers and n_side >= 2, each group's selection and attention
- *     run on side[1] and overlap the next group's scans. Further side
- *     streams are not used;
+ *   - HBM pools: the layers go in groups of up to 16; one launch scans the
+ *     whole group's index, then one launch each of the selection and
+ *     attention kernels covers the whole group, all on `compute`. With more
+ *     than 16 layers, each group's selection and attention run on side[0]
+ *     and overlap the next group's scan. Further side streams are not used;
  *   - host pools with a hot cache: layer l's whole chain (score, select,
  *     cache update, miss fetch, attend, merge) runs on stream
  *     l % (n_side + 1) of {compute, side[0], side[1], ...}, with at most two

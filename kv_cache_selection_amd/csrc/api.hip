@@ -570,44 +570,44 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     }
 
     if (!offload && !hot) {
-        // Pools in HBM. The index scans alternate over two streams (compute
-        // and side 0), so two run at once and the ramp and tail of one hide
-        // under the other. The selection and attention of up to
-        // kMaxChainLayers layers then run as one group: one launch of each
-        // kernel (collect, finish, attention, merge) for all of them, once
-        // the group's scans are done. A group costs one latency chain instead
-        // of one per layer, its attention is a single wide launch, and
-        // running the chains during the scans instead would only take CUs
-        // and bandwidth from the scans. The chains run on the compute stream;
-        // with more layers than one group and a second side stream they run
-        // on side 1, so that a group's chain overlaps the next group's scans.
-        const hipStream_t scan_s[2] = {sc, (hipStream_t)side[0]};
-        const hipStream_t cs = (NS >= 2 && n_layers > kMaxChainLayers) ? (hipStream_t)side[1] : sc;
-        // only the side streams this schedule uses are forked and joined
-        const int n_used = (NS >= 2 && n_layers > kMaxChainLayers) ? 2 : 1;
-        if (e == hipSuccess)
+        // Pools in HBM. The layers go in groups of up to kMaxChainLayers: one
+        // launch scans the whole group's index (the layer is a grid
+        // coordinate, so the scan streams without a break between layers),
+        // then one launch each of collect, finish, attention and merge
+        // selects and attends the whole group. A group costs one latency
+        // chain instead of one per layer, and its attention is a single wide
+        // launch; running the chains during the scans instead only takes CUs
+        // and bandwidth from the scans. With one group everything runs on
+        // the compute stream. With several, the chains run on side 0, so a
+        // group's chain overlaps the next group's scan. The first layer's
+        // score events of a group time that group's scan.
+        const hipStream_t cs = n_layers > kMaxChainLayers ? (hipStream_t)side[0] : sc;
+        const int n_used = cs != sc ? 1 : 0;
+        if (e == hipSuccess && n_used) {
             e = hipEventRecord(ev[0], sc);
-        for (int k = 0; k < n_used && e == hipSuccess; k++)
-            e = hipStreamWaitEvent((hipStream_t)side[k], ev[0], 0);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(cs, ev[0], 0);
+        }
         for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
             const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
+            ScoreLayers CL = {};
             SelectLayers SL = {};
             AttnLayers AL = {};
-            for (int i = 0; i < nl && e == hipSuccess; i++) {
+            for (int i = 0; i < nl; i++) {
                 const int l = l0 + i;
-                hipStream_t ss = scan_s[l & 1];
-                e = score(l, ss);
-                if (e == hipSuccess && ss != cs) {
-                    e = hipEventRecord(ev[1 + NS + l], ss);
-                    if (e == hipSuccess)
-                        e = hipStreamWaitEvent(cs, ev[1 + NS + l], 0);
-                }
+                const qsa_layer_t &Ly = layers[l];
+                CL.keys[i] = Ly.idx_keys;
+                CL.scales[i] = Ly.idx_scales;
+                CL.q_idx[i] = Ly.q_idx;
+                CL.w_idx[i] = Ly.w_idx;
+                CL.block_scores[i] = lw[l].bs;
+                CL.hist[i] = lw[l].sw.hist;
                 SL.bs[i] = lw[l].bs;
                 SL.ws[i] = lw[l].sw;
                 SL.sel[i] = lw[l].sel;
                 SL.n_sel[i] = lw[l].nsel;
                 SL.n_tok[i] = lw[l].ntok;
-                AL.q[i] = layers[l].q;
+                AL.q[i] = Ly.q;
                 AL.rows[i] = static_cast<const uint8_t *>(pools[l]);
                 AL.pt[i] = lw[l].pt;
                 AL.n_slots[i] = batch->n_slots;
@@ -615,7 +615,16 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                 AL.n_tok[i] = lw[l].ntok;
                 AL.part_o[i] = lw[l].aw.part_o;
                 AL.part_lse[i] = lw[l].aw.part_lse;
-                AL.out[i] = layers[l].out;
+                AL.out[i] = Ly.out;
+            }
+            e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B,
+                                          batch->max_ctx, bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
+                                          (hipEvent_t)layers[l0].score_events[0],
+                                          (hipEvent_t)layers[l0].score_events[1]);
+            if (e == hipSuccess && cs != sc) {
+                e = hipEventRecord(ev[1 + NS + l0], sc);
+                if (e == hipSuccess)
+                    e = hipStreamWaitEvent(cs, ev[1 + NS + l0], 0);
             }
             if (e == hipSuccess)
                 e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
@@ -624,11 +633,11 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                 e = launch_attention_layers(true, AL, nl, batch->pt_stride, batch->max_ctx, B, K,
                                             cfg->budget_tokens, cfg->sm_scale, lw[l0].aw.n_split, cs);
         }
-        // The caller synchronises on the compute stream: join the side streams.
-        for (int k = 0; k < n_used && e == hipSuccess; k++) {
-            e = hipEventRecord(ev[1 + k], (hipStream_t)side[k]);
+        // The caller synchronises on the compute stream: join the side stream.
+        if (e == hipSuccess && n_used) {
+            e = hipEventRecord(ev[1], cs);
             if (e == hipSuccess)
-                e = hipStreamWaitEvent(sc, ev[1 + k], 0);
+                e = hipStreamWaitEvent(sc, ev[1], 0);
         }
         return hip_status(e);
     }

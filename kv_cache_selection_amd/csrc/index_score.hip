@@ -43,14 +43,22 @@ constexpr int kThreads = 512;                      // 8 waves: half as many hist
 constexpr int kWaveTok = 64;                       // tokens per wave iteration
 constexpr int kWgTok = kThreads / 64 * kWaveTok;   // 512 tokens per workgroup iteration
 
-template <bool kTokens, bool kHist>
-__global__ __launch_bounds__(kThreads) void index_score_kernel(
-    const uint8_t *__restrict__ keys, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ q_idx,
-    const float *__restrict__ w_idx, const int32_t *__restrict__ ctx_len, const int64_t *__restrict__ row0,
-    int64_t n_rows, int max_ctx, int chunk_tokens, float *__restrict__ token_scores, float *__restrict__ block_scores,
-    int64_t bs_stride, uint32_t *__restrict__ hist, int budget_blocks, int sink_blocks, int tail_tokens)
+// Grid (chunks of chunk_tokens, B, layers).
+template <bool kTokens, bool kHist, int N>
+__global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayersT<N> Ls,
+                                                               const int32_t *__restrict__ ctx_len,
+                                                               const int64_t *__restrict__ row0, int64_t n_rows,
+                                                               int max_ctx, int chunk_tokens, int64_t bs_stride,
+                                                               int budget_blocks, int sink_blocks, int tail_tokens)
 {
     __shared__ uint32_t lhist[kHist ? kHistBins : 1];
+    const uint8_t *__restrict__ keys = Ls.keys[blockIdx.z];
+    const uint16_t *__restrict__ scales = Ls.scales[blockIdx.z];
+    const uint16_t *__restrict__ q_idx = Ls.q_idx[blockIdx.z];
+    const float *__restrict__ w_idx = Ls.w_idx[blockIdx.z];
+    float *__restrict__ token_scores = Ls.token_scores[blockIdx.z];
+    float *__restrict__ block_scores = Ls.block_scores[blockIdx.z];
+    uint32_t *__restrict__ hist = Ls.hist[blockIdx.z];
 
     const int b = blockIdx.y;
     const int64_t r0 = row0[b];
@@ -238,35 +246,70 @@ void launch_timed(Kernel k, dim3 grid, hipStream_t s, hipEvent_t ev0, hipEvent_t
         hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, args...);
 }
 
+template <int N>
+static hipError_t launch_score_n(const ScoreLayersT<N> &L, int n_layers, const int32_t *ctx_len,
+                                 const int64_t *row0, int64_t n_rows, int batch, int max_ctx, int64_t bs_stride,
+                                 int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s, hipEvent_t ev0,
+                                 hipEvent_t ev1)
+{
+    // Tokens per workgroup: a multiple of 512, grown while the grid keeps
+    // at least 512 workgroups (2 per CU, 16 waves) per layer so every CU streams.
+    int chunk = kWgTok;
+    while (chunk < 8192 && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 512)
+        chunk *= 2;
+    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)batch, (unsigned)n_layers);
+#define QSA_SCORE_ARGS L, ctx_len, row0, n_rows, max_ctx, chunk, bs_stride, budget_blocks, sink_blocks, tail_tokens
+    if (L.token_scores[0]) {
+        if (L.hist[0])
+            launch_timed(index_score_kernel<true, true, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
+        else
+            launch_timed(index_score_kernel<true, false, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
+    } else {
+        if (L.hist[0])
+            launch_timed(index_score_kernel<false, true, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
+        else
+            launch_timed(index_score_kernel<false, false, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
+    }
+#undef QSA_SCORE_ARGS
+    return hipGetLastError();
+}
+
+hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const int32_t *ctx_len, const int64_t *row0,
+                                     int64_t n_rows, int batch, int max_ctx, int64_t bs_stride, int budget_blocks,
+                                     int sink_blocks, int tail_tokens, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
+{
+    if (n_layers < 1 || n_layers > kMaxChainLayers)
+        return hipErrorInvalidValue;
+    if (max_ctx <= 0)
+        return hipSuccess;
+    for (int l = 1; l < n_layers; l++)
+        if (!L.token_scores[l] != !L.token_scores[0] || !L.hist[l] != !L.hist[0])
+            return hipErrorInvalidValue;
+    if (n_layers > 1)
+        return launch_score_n(L, n_layers, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks,
+                              sink_blocks, tail_tokens, s, ev0, ev1);
+    const ScoreLayersT<1> L1 = {{L.keys[0]},         {L.scales[0]},       {L.q_idx[0]}, {L.w_idx[0]},
+                                {L.token_scores[0]}, {L.block_scores[0]}, {L.hist[0]}};
+    return launch_score_n(L1, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks, sink_blocks,
+                          tail_tokens, s, ev0, ev1);
+}
+
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s,
                               hipEvent_t ev0, hipEvent_t ev1)
 {
-    if (max_ctx <= 0)
-        return hipSuccess;
-    // Tokens per workgroup: a multiple of 512, grown while the grid keeps
-    // at least 512 workgroups (2 per CU, 16 waves) so every CU streams.
-    int chunk = kWgTok;
-    while (chunk < 8192 && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 512)
-        chunk *= 2;
-    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)batch);
-#define QSA_SCORE_ARGS keys, scales, q_idx, w_idx, ctx_len, row0, n_rows, max_ctx, chunk, token_scores, block_scores, \
-                       bs_stride, hist, budget_blocks, sink_blocks, tail_tokens
-    if (token_scores) {
-        if (hist)
-            launch_timed(index_score_kernel<true, true>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
-        else
-            launch_timed(index_score_kernel<true, false>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
-    } else {
-        if (hist)
-            launch_timed(index_score_kernel<false, true>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
-        else
-            launch_timed(index_score_kernel<false, false>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
-    }
-#undef QSA_SCORE_ARGS
-    return hipGetLastError();
+    ScoreLayers L = {};
+    L.keys[0] = keys;
+    L.scales[0] = scales;
+    L.q_idx[0] = q_idx;
+    L.w_idx[0] = w_idx;
+    L.token_scores[0] = token_scores;
+    L.block_scores[0] = block_scores;
+    L.hist[0] = hist;
+    return launch_index_score_layers(L, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks,
+                                     sink_blocks, tail_tokens, s, ev0, ev1);
 }
 
 hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,

@@ -92,6 +92,18 @@ struct AttnWs {
 constexpr int kMaxChainLayers = 16;
 
 template <int N>
+struct ScoreLayersT {
+    const uint8_t *keys[N];               // index codes [rows][kIdxD]
+    const uint16_t *scales[N];            // fp16 scales [rows]
+    const uint16_t *q_idx[N];             // bf16 [B][kIdxH][kIdxD]
+    const float *w_idx[N];                // [B][kIdxH]
+    float *token_scores[N];               // [rows] or null
+    float *block_scores[N];               // [B][bs_stride]
+    uint32_t *hist[N];                    // [B][kHistReps][kHistBins] or null
+};
+using ScoreLayers = ScoreLayersT<kMaxChainLayers>;
+
+template <int N>
 struct SelectLayersT {
     const float *bs[N];                   // block scores [B][bs_stride]
     SelectWs ws[N];
@@ -172,6 +184,13 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
                               hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
+// Index scoring of layers 0 .. n_layers - 1 of L in one launch (grid z =
+// layer); token_scores and hist must be null for all layers or for none.
+hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const int32_t *ctx_len, const int64_t *row0,
+                                     int64_t n_rows, int batch, int max_ctx, int64_t bs_stride, int budget_blocks,
+                                     int sink_blocks, int tail_tokens, hipStream_t s, hipEvent_t ev0 = nullptr,
+                                     hipEvent_t ev1 = nullptr);
 
 hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
                              int max_ctx, uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
