@@ -12,8 +12,8 @@ Prints one JSON line with the driver's fields plus:
   roofline      the dominant kernel (index scoring) as the headline step
                 launches it: algorithmic bytes per launch / its average
                 duration, timed with HIP events taken by the launch itself.
-                With pools in HBM one launch scans all the layers (up to 16),
-                so a launch's bytes are the layers' index bytes together;
+                Without a hot cache one launch scans all the layers (up to
+                16), so a launch's bytes are the layers' index bytes together;
   one_stream_score  the same for the per-layer scoring launch of the
                 one-stream step (each launch has the GPU alone);
   one_stream    the step time with every kernel in order on one stream;
@@ -604,11 +604,11 @@ def main():
         ms_serial = e0.elapsed_time(e1) / args.steps
 
     # Timed region 3: the headline schedule again, with HIP events around
-    # the scoring launches. With pools in HBM and side streams one launch
+    # the scoring launches. With side streams and no hot cache one launch
     # scans all the layers (up to 16), and the first layer's events time it;
     # otherwise every layer's scan is a launch of its own.
     hev = HipEvents()
-    grouped = bool(side) and not di.kv_host and NL <= 16
+    grouped = bool(side) and not hot and NL <= 16
     evs = [(hev.create(), hev.create()) for _ in range(NL)]
     ev_used = evs[:1] if grouped else evs
     timed = [layers(v, ev_used + [None] * (NL - len(ev_used))) for v in range(NV)]

@@ -203,8 +203,8 @@ typedef struct {
     void *score_events[2];      /* optional pair of timing-enabled hipEvent_t that take the begin
                                    and end timestamps of this layer's index-scoring kernel (it is
                                    then launched through hipExtLaunchKernel); NULL to skip. Where
-                                   one launch scans a group of layers (HBM pools with side
-                                   streams), the group's first layer's events time that launch
+                                   one launch scans a group of layers (side streams, no hot
+                                   cache), the group's first layer's events time that launch
                                    and the other layers' events are not recorded */
 } qsa_layer_t;
 
@@ -226,9 +226,11 @@ typedef struct {
  *     cache update, miss fetch, attend, merge) runs on stream
  *     l % (n_side + 1) of {compute, side[0], side[1], ...}, with at most two
  *     index scans at a time;
- *   - host pools without a hot cache: side[0] gathers layer l over PCIe
- *     while `compute` scores and selects layer l+1 and attends layer l-1
- *     (further side streams are not used).
+ *   - host pools without a hot cache: `compute` scans and selects every
+ *     layer (one launch each per group of up to 16 layers); then side[0]
+ *     gathers the layers' rows over PCIe one after another into two staging
+ *     buffers while `compute` attends each layer as its rows land (further
+ *     side streams are not used).
  * The call leaves `compute` ordered after all of its work, so a sync on
  * `compute` covers the step. Results are bit-identical for every schedule.
  * The overlapped schedules record events owned by the library (one set per

@@ -682,45 +682,61 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return hip_status(e);
     }
 
-    // Pools in pinned host memory: the copy stream gathers layer l over PCIe
-    // once its selection exists and once attention(l-2) has released the
-    // staging buffer; the compute stream goes on scoring layer l+1 and attends
-    // layer l when its rows have landed.
+    // Pools in pinned host memory: the compute stream first scans and
+    // selects every layer, in groups of up to kMaxChainLayers (one launch
+    // each). Index scans running beside the gather slow its PCIe reads far
+    // more than they gain, so the gathers start after them: the copy stream
+    // gathers layer l as soon as attention(l-2) has released the staging
+    // buffer, and the compute stream attends layer l when its rows have
+    // landed, so the PCIe reads run back to back.
+    for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
+        const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
+        ScoreLayers CL = {};
+        SelectLayers SL = {};
+        for (int i = 0; i < nl; i++) {
+            const int l = l0 + i;
+            const qsa_layer_t &Ly = layers[l];
+            CL.keys[i] = Ly.idx_keys;
+            CL.scales[i] = Ly.idx_scales;
+            CL.q_idx[i] = Ly.q_idx;
+            CL.w_idx[i] = Ly.w_idx;
+            CL.block_scores[i] = lw[l].bs;
+            CL.hist[i] = lw[l].sw.hist;
+            SL.bs[i] = lw[l].bs;
+            SL.ws[i] = lw[l].sw;
+            SL.sel[i] = lw[l].sel;
+            SL.n_sel[i] = lw[l].nsel;
+            SL.n_tok[i] = lw[l].ntok;
+        }
+        e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B, batch->max_ctx,
+                                      bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
+                                      (hipEvent_t)layers[l0].score_events[0], (hipEvent_t)layers[l0].score_events[1]);
+        if (e == hipSuccess)
+            e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
+                                     cfg->tail_tokens, sc);
+    }
+    if (e == hipSuccess)
+        e = hipEventRecord(ev[0], sc);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(sx, ev[0], 0);
     for (int l = 0; l < n_layers && e == hipSuccess; l++) {
-        hipEvent_t e_sel = ev[3 * l], e_gat = ev[3 * l + 1];
-        e = score(l, sc);
-        if (e == hipSuccess)
-            e = select(l, sc);
-        if (e == hipSuccess)
-            e = hipEventRecord(e_sel, sc);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(sx, e_sel, 0);
-        if (e == hipSuccess && l >= 2)
+        if (l >= 2)
             e = hipStreamWaitEvent(sx, ev[3 * (l - 2) + 2], 0);
         if (e == hipSuccess)
             e = gather(l, sx);
         if (e == hipSuccess)
-            e = hipEventRecord(e_gat, sx);
-        if (e == hipSuccess && l >= 1) {
-            e = hipStreamWaitEvent(sc, ev[3 * (l - 1) + 1], 0);
-            if (e == hipSuccess)
-                e = attend_staged(l - 1, sc);
-            if (e == hipSuccess)
-                e = hipEventRecord(ev[3 * (l - 1) + 2], sc);
-        }
-    }
-    if (e == hipSuccess) {
-        const int l = n_layers - 1;
-        e = hipStreamWaitEvent(sc, ev[3 * l + 1], 0);
+            e = hipEventRecord(ev[3 * l + 1], sx);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(sc, ev[3 * l + 1], 0);
         if (e == hipSuccess)
             e = attend_staged(l, sc);
         if (e == hipSuccess)
             e = hipEventRecord(ev[3 * l + 2], sc);
-        // The copy stream must not run ahead of this call's last attention
-        // into a later call that reuses the staging buffers.
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(sx, ev[3 * l + 2], 0);
     }
+    // The copy stream must not run ahead of this call's last attention into
+    // a later call that reuses the staging buffers.
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(sx, ev[3 * (n_layers - 1) + 2], 0);
     return hip_status(e);
 }
 
