@@ -211,8 +211,8 @@ typedef struct {
 /* The whole decode step over n_layers independent QSA layers: for each layer,
  * score -> select -> gather/attend -> merge. With KV in HBM the gather is
  * fused into attention (rows are read through the page table in place). With
- * QSA_KV_HOST_PINNED the selected rows are copied over PCIe into a
- * double-buffered staging area.
+ * QSA_KV_HOST_PINNED the selected rows are copied over PCIe into a staging
+ * area in the workspace, one buffer per layer (B x budget_tokens x 2048 B).
  * Streams: `side` holds n_side extra streams (all distinct from `compute`);
  * with n_side = 0 (side may then be NULL) every kernel runs in order on
  * `compute`. With side streams the layers overlap (this treats the layers
@@ -226,11 +226,10 @@ typedef struct {
  *     cache update, miss fetch, attend, merge) runs on stream
  *     l % (n_side + 1) of {compute, side[0], side[1], ...}, with at most two
  *     index scans at a time;
- *   - host pools without a hot cache: `compute` scans and selects every
- *     layer (one launch each per group of up to 16 layers); then side[0]
- *     gathers the layers' rows over PCIe one after another into two staging
- *     buffers while `compute` attends each layer as its rows land (further
- *     side streams are not used).
+ *   - host pools without a hot cache: per group of up to 16 layers, one
+ *     launch each scans, selects, gathers the selected rows over PCIe into
+ *     the layers' staging buffers, and attends them, all on `compute` (side
+ *     streams are not used).
  * The call leaves `compute` ordered after all of its work, so a sync on
  * `compute` covers the step. Results are bit-identical for every schedule.
  * The overlapped schedules record events owned by the library (one set per

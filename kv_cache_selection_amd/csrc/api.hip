@@ -80,7 +80,7 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.plse = off;
     off += w.per_plse * n_layers;
     w.stage = off;
-    off += w.per_stage * 2;
+    off += w.per_stage * (size_t)n_layers;
     w.fetch = off;
     off += w.per_fetch * n_layers;
     w.nfetch = off;
@@ -472,10 +472,12 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     hipStream_t sc = (hipStream_t)compute;
     const bool offload = kv_location == QSA_KV_HOST_PINNED;
     const bool two_streams = n_side > 0;
-    const int NS = (offload && !hot) ? (n_side > 0 ? 1 : 0) : n_side;
-    hipStream_t sx = NS > 0 ? (hipStream_t)side[0] : nullptr;
+    // side streams the overlapped schedules use: none for pinned-host pools
+    // without a hot cache (one stream), side[0] for HBM pools with more layers
+    // than one group, all of them for hot-cached pools
+    const int NS = (offload && !hot) ? 0 : n_side;
     std::vector<hipEvent_t> ev;
-    if (two_streams && (st = get_events(3 * n_layers + NS + 1, ev)) != QSA_OK)
+    if (two_streams && NS > 0 && (st = get_events(3 * n_layers + NS + 1, ev)) != QSA_OK)
         return st;
 
     const int B = batch->batch;
@@ -504,7 +506,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         x.ntok = at<int32_t>(workspace, w.ntok + w.per_ntok * l);
         x.sw = select_ws(workspace, w, l);
         x.aw = attn_ws(workspace, w, l);
-        x.stage = offload ? at<void>(workspace, w.stage + w.per_stage * (l & 1)) : nullptr;
+        x.stage = offload ? at<void>(workspace, w.stage + w.per_stage * l) : nullptr;
         x.fetch = offload ? at<int2>(workspace, w.fetch + w.per_fetch * l) : nullptr;
         x.nfetch = offload ? at<int32_t>(workspace, w.nfetch + w.per_nfetch * l) : nullptr;
     }
@@ -682,17 +684,19 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return hip_status(e);
     }
 
-    // Pools in pinned host memory: the compute stream first scans and
-    // selects every layer, in groups of up to kMaxChainLayers (one launch
-    // each). Index scans running beside the gather slow its PCIe reads far
-    // more than they gain, so the gathers start after them: the copy stream
-    // gathers layer l as soon as attention(l-2) has released the staging
-    // buffer, and the compute stream attends layer l when its rows have
-    // landed, so the PCIe reads run back to back.
+    // Pools in pinned host memory, side streams allowed: per group of up to
+    // kMaxChainLayers layers, one launch each scans, selects, gathers the
+    // selected rows over PCIe into the layers' own staging buffers, and
+    // attends them. Index scans running beside a gather slow its PCIe reads
+    // far more than they gain, so nothing overlaps the gather: the PCIe reads
+    // of all the group's layers stream in one launch. Everything runs on
+    // the compute stream.
     for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
         const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
         ScoreLayers CL = {};
         SelectLayers SL = {};
+        GatherLayers GL = {};
+        AttnLayers AL = {};
         for (int i = 0; i < nl; i++) {
             const int l = l0 + i;
             const qsa_layer_t &Ly = layers[l];
@@ -707,6 +711,18 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             SL.sel[i] = lw[l].sel;
             SL.n_sel[i] = lw[l].nsel;
             SL.n_tok[i] = lw[l].ntok;
+            GL.sel[i] = lw[l].sel;
+            GL.n_sel[i] = lw[l].nsel;
+            GL.pt[i] = lw[l].pt;
+            GL.pool[i] = pools[l];
+            GL.out[i] = lw[l].stage;
+            GL.n_tok[i] = lw[l].ntok;
+            AL.q[i] = Ly.q;
+            AL.rows[i] = static_cast<const uint8_t *>(lw[l].stage);
+            AL.n_tok[i] = lw[l].ntok;
+            AL.part_o[i] = lw[l].aw.part_o;
+            AL.part_lse[i] = lw[l].aw.part_lse;
+            AL.out[i] = Ly.out;
         }
         e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B, batch->max_ctx,
                                       bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
@@ -714,29 +730,13 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         if (e == hipSuccess)
             e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
                                      cfg->tail_tokens, sc);
+        if (e == hipSuccess)
+            e = launch_gather_layers(GL, nl, batch->ctx_len, B, batch->max_ctx, batch->pt_stride, batch->n_slots, K,
+                                     cfg->budget_tokens, sc);
+        if (e == hipSuccess)
+            e = launch_attention_layers(false, AL, nl, 0, 0, B, 0, cfg->budget_tokens, cfg->sm_scale,
+                                        lw[l0].aw.n_split, sc);
     }
-    if (e == hipSuccess)
-        e = hipEventRecord(ev[0], sc);
-    if (e == hipSuccess)
-        e = hipStreamWaitEvent(sx, ev[0], 0);
-    for (int l = 0; l < n_layers && e == hipSuccess; l++) {
-        if (l >= 2)
-            e = hipStreamWaitEvent(sx, ev[3 * (l - 2) + 2], 0);
-        if (e == hipSuccess)
-            e = gather(l, sx);
-        if (e == hipSuccess)
-            e = hipEventRecord(ev[3 * l + 1], sx);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(sc, ev[3 * l + 1], 0);
-        if (e == hipSuccess)
-            e = attend_staged(l, sc);
-        if (e == hipSuccess)
-            e = hipEventRecord(ev[3 * l + 2], sc);
-    }
-    // The copy stream must not run ahead of this call's last attention into
-    // a later call that reuses the staging buffers.
-    if (e == hipSuccess)
-        e = hipStreamWaitEvent(sx, ev[3 * (n_layers - 1) + 2], 0);
     return hip_status(e);
 }
 

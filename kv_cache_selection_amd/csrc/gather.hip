@@ -20,13 +20,19 @@ constexpr int kBlocksPerWg = 4;                       // 16 rows, 32 KB per work
 constexpr int kRowsPerWg = kBlocksPerWg * kBT;
 constexpr int kPieces = kRowBytes / 16;               // 128 x 16 B per row
 
-__global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restrict__ sel,
-                                                          const int32_t *__restrict__ n_sel,
+// Grid (groups of kBlocksPerWg selection entries, B, layers).
+template <int N>
+__global__ __launch_bounds__(kThreads) void gather_kernel(const GatherLayersT<N> Ls,
                                                           const int32_t *__restrict__ ctx_len, int max_ctx,
-                                                          const int32_t *__restrict__ pt, int64_t pt_stride,
-                                                          int64_t n_slots, const u32x4 *__restrict__ pool, u32x4 *__restrict__ out,
-                                                          int K, int budget_tokens, int32_t *__restrict__ n_tok)
+                                                          int64_t pt_stride, int64_t n_slots, int K,
+                                                          int budget_tokens)
 {
+    const int32_t *__restrict__ sel = Ls.sel[blockIdx.z];
+    const int32_t *__restrict__ n_sel = Ls.n_sel[blockIdx.z];
+    const int32_t *__restrict__ pt = Ls.pt[blockIdx.z];
+    const u32x4 *__restrict__ pool = static_cast<const u32x4 *>(Ls.pool[blockIdx.z]);
+    u32x4 *__restrict__ out = static_cast<u32x4 *>(Ls.out[blockIdx.z]);
+    int32_t *__restrict__ n_tok = Ls.n_tok[blockIdx.z];
     const int b = blockIdx.y;
     const int L = clamp_ctx(ctx_len[b], max_ctx);
     int ns = n_sel[b];
@@ -73,16 +79,42 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const int32_t *__restr
 
 } // namespace
 
+template <int N>
+static void launch_gather_n(const GatherLayersT<N> &L, int n_layers, const int32_t *ctx_len, int batch, int max_ctx,
+                            int64_t pt_stride, int64_t n_slots, int budget_blocks, int budget_tokens, hipStream_t s)
+{
+    dim3 grid((unsigned)((budget_blocks + kBlocksPerWg - 1) / kBlocksPerWg), (unsigned)batch, (unsigned)n_layers);
+    hipLaunchKernelGGL((gather_kernel<N>), grid, dim3(kThreads), 0, s, L, ctx_len, max_ctx, pt_stride, n_slots,
+                       budget_blocks, budget_tokens);
+}
+
+hipError_t launch_gather_layers(const GatherLayers &L, int n_layers, const int32_t *ctx_len, int batch, int max_ctx,
+                                int64_t pt_stride, int64_t n_slots, int budget_blocks, int budget_tokens,
+                                hipStream_t s)
+{
+    if (n_layers < 1 || n_layers > kMaxChainLayers)
+        return hipErrorInvalidValue;
+    if (n_layers > 1) {
+        launch_gather_n(L, n_layers, ctx_len, batch, max_ctx, pt_stride, n_slots, budget_blocks, budget_tokens, s);
+    } else {
+        const GatherLayersT<1> L1 = {{L.sel[0]}, {L.n_sel[0]}, {L.pt[0]}, {L.pool[0]}, {L.out[0]}, {L.n_tok[0]}};
+        launch_gather_n(L1, 1, ctx_len, batch, max_ctx, pt_stride, n_slots, budget_blocks, budget_tokens, s);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
                          const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out,
-                         int budget_blocks,
-                         int budget_tokens, int32_t *n_tok, hipStream_t s)
+                         int budget_blocks, int budget_tokens, int32_t *n_tok, hipStream_t s)
 {
-    dim3 grid((unsigned)((budget_blocks + kBlocksPerWg - 1) / kBlocksPerWg), (unsigned)batch);
-    hipLaunchKernelGGL(gather_kernel, grid, dim3(kThreads), 0, s, sel, n_sel, ctx_len, max_ctx, pt, pt_stride, n_slots,
-                       static_cast<const u32x4 *>(pool), static_cast<u32x4 *>(out), budget_blocks, budget_tokens,
-                       n_tok);
-    return hipGetLastError();
+    GatherLayers L = {};
+    L.sel[0] = sel;
+    L.n_sel[0] = n_sel;
+    L.pt[0] = pt;
+    L.pool[0] = pool;
+    L.out[0] = out;
+    L.n_tok[0] = n_tok;
+    return launch_gather_layers(L, 1, ctx_len, batch, max_ctx, pt_stride, n_slots, budget_blocks, budget_tokens, s);
 }
 
 } // namespace qsa

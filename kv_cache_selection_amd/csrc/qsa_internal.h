@@ -104,6 +104,17 @@ struct ScoreLayersT {
 using ScoreLayers = ScoreLayersT<kMaxChainLayers>;
 
 template <int N>
+struct GatherLayersT {
+    const int32_t *sel[N];                // [B][budget_blocks]
+    const int32_t *n_sel[N];              // [B]
+    const int32_t *pt[N];                 // page table [B][pt_stride]
+    const void *pool[N];                  // [n_slots][kRowBytes], device or mapped pinned host memory
+    void *out[N];                         // staging rows [B][budget_tokens][kRowBytes]
+    int32_t *n_tok[N];                    // [B] or null
+};
+using GatherLayers = GatherLayersT<kMaxChainLayers>;
+
+template <int N>
 struct SelectLayersT {
     const float *bs[N];                   // block scores [B][bs_stride]
     SelectWs ws[N];
@@ -208,6 +219,11 @@ hipError_t launch_select_layers(const SelectLayers &L, int n_layers, int64_t bs_
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
                          const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out, int budget_blocks,
                          int budget_tokens, int32_t *n_tok, hipStream_t s);
+
+// Row gathers of layers 0 .. n_layers - 1 of L in one launch (grid z = layer).
+hipError_t launch_gather_layers(const GatherLayers &L, int n_layers, const int32_t *ctx_len, int batch, int max_ctx,
+                                int64_t pt_stride, int64_t n_slots, int budget_blocks, int budget_tokens,
+                                hipStream_t s);
 
 // Attention over staged rows (kv != nullptr) or through the page table.
 hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int32_t *n_tok, int batch,
