@@ -88,9 +88,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
     float *__restrict__ part_lse = Ls.part_lse[ly];
     __shared__ __attribute__((aligned(16))) float ps[kWaves][kGroup][kWaveTok];  // the wave's probabilities
     __shared__ float sstat[kWaves][kGroup][2];      // per-wave (max, sum) for the workgroup merge
+    __shared__ float swt[kWaves][kGroup];           // per-wave weights exp(m_w - M) of each head
+    __shared__ float sden[kGroup];                  // each head's normaliser
     // V tiles during the token loop, then the per-wave partial outputs
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    float(*so)[kGroup][kDh] = reinterpret_cast<float(*)[kGroup][kDh]>(smem);
 
     const int s = blockIdx.x;
     const int g = blockIdx.y % kHkv;
@@ -276,14 +277,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
         }
     }
 
-    // Workgroup merge of the four waves' states (the V tiles' LDS is reused).
+    // Workgroup merge of the four waves' states (the V tiles' LDS is reused):
+    // each wave's accumulators go to LDS as [dim][head], 16 bytes (4 heads of
+    // one dim) per store; 8 threads then work out each head's wave weights
+    // f_w = exp(m_w - M), normaliser and LSE once, and every thread combines
+    // one dim for the 8 heads.
     __syncthreads();
+    float(*sod)[kDh][kGroup] = reinterpret_cast<float(*)[kDh][kGroup]>(smem);
     if (lane < 32) {
 #pragma unroll
         for (int m = 0; m < kDh / 16; m++)
-#pragma unroll
-            for (int v = 0; v < 4; v++)
-                so[wave][4 * grp + v][16 * m + col] = o[m][v];
+            *reinterpret_cast<f32x4 *>(&sod[wave][16 * m + col][4 * grp]) = o[m];
     }
     if (lane < 32 && (lane & 15) == 0) {
 #pragma unroll
@@ -293,25 +297,42 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
         }
     }
     __syncthreads();
-    for (int d = tid; d < kDh; d += kThreads) {
+    if (tid < kGroup) {
+        const int h = tid;
+        float M = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < kGroup; h++) {
-            float M = -INFINITY;
+        for (int w = 0; w < kWaves; w++)
+            M = fmaxf(M, sstat[w][h][0]);
+        float den = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; w++)
-                M = fmaxf(M, sstat[w][h][0]);
-            float acc = 0.0f, den = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) {
-                const float mw = sstat[w][h][0];
-                const float f = (mw == -INFINITY) ? 0.0f : __expf(mw - M);
-                den += f * sstat[w][h][1];
-                acc = fmaf(f, so[w][h][d], acc);
-            }
-            part_o[(part_base + (int64_t)h * n_split) * kDh + d] = acc / den;
-            if (d == 0)
-                part_lse[part_base + (int64_t)h * n_split] = M + logf(den);
+        for (int w = 0; w < kWaves; w++) {
+            const float mw = sstat[w][h][0];
+            const float f = (mw == -INFINITY) ? 0.0f : __expf(mw - M);
+            swt[w][h] = f;
+            den += f * sstat[w][h][1];
         }
+        sden[h] = den;
+        part_lse[part_base + (int64_t)h * n_split] = M + logf(den);
+    }
+    __syncthreads();
+    for (int d = tid; d < kDh; d += kThreads) {
+        float acc[kGroup];
+#pragma unroll
+        for (int h = 0; h < kGroup; h++)
+            acc[h] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(&sod[w][d][0]);
+            const f32x4 c = *reinterpret_cast<const f32x4 *>(&sod[w][d][4]);
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                acc[h] = fmaf(swt[w][h], a[h], acc[h]);
+                acc[4 + h] = fmaf(swt[w][4 + h], c[h], acc[4 + h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kGroup; h++)
+            part_o[(part_base + (int64_t)h * n_split) * kDh + d] = acc[h] / sden[h];
     }
 }
 
