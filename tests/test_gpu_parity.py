@@ -392,9 +392,10 @@ def test_decode_step_deterministic_and_offload_bit_exact(gpu):
 
 
 def test_decode_step_more_layers_than_one_group(gpu):
-    """With pools in HBM the overlapped schedule selects and attends up to 16
-    layers per launch; 18 layers take two groups (16 + 2), and every
-    schedule must still give the one-stream bits, which match the oracle."""
+    """The overlapped schedules scan, select and attend up to 16 layers per
+    launch; 18 layers take two groups (16 + 2), and every schedule, with the
+    pool in HBM or in pinned host memory, must still give the one-stream
+    bits, which match the oracle."""
     wl = S.Workload("groups-18", 2, (3001, 1800), 18, 256, planted=4, seed=21)
     di = DeviceInputs(wl, gpu)
     sel0, ns0, out0 = _step(di, n_side=0)
@@ -403,6 +404,12 @@ def test_decode_step_more_layers_than_one_group(gpu):
         assert np.array_equal(sel0, sel) and np.array_equal(ns0, ns), n_side
         assert np.array_equal(out0, out), n_side
     _check_step_units(di, sel0, ns0, out0, [(0, 0), (15, 1), (16, 0), (17, 1)])
+    # the pinned-host pool path groups the same way (scan, select, gather, attend)
+    dh = DeviceInputs(wl, gpu, kv_host=True, hi=di.hi)
+    for n_side in (0, 1):
+        sel, ns, out = _step(dh, n_side=n_side)
+        assert np.array_equal(sel0, sel) and np.array_equal(ns0, ns), n_side
+        assert np.array_equal(out0, out), n_side
 
 
 def test_decode_step_page_table_permutation_invariant(gpu):
