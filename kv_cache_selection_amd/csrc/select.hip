@@ -50,22 +50,6 @@ static_assert(kDigitBins + 2 * kThreads <= kWorkWords, "digit histogram and shor
 // (digit histogram and short list, then the output bitmap)
 constexpr size_t kSmemBytes = (size_t)kCandCap * 8 + (size_t)kDefCap * 4 + (size_t)kWorkWords * 4;
 
-// Position of this lane's item in an LDS list: one LDS atomic per wave.
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t *counter)
-{
-    const uint64_t mask = __ballot(pred);
-    uint32_t base = 0;
-    if (mask) {
-        const int lane = threadIdx.x & 63;
-        const int leader = __ffsll((unsigned long long)mask) - 1;
-        if (lane == leader)
-            base = atomicAdd(counter, (uint32_t)__popcll(mask));
-        base = __shfl(base, leader);
-        base += (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-    }
-    return base;
-}
-
 // Walk a histogram of NT * W bins from the top: the bin where the running
 // count first reaches `want`, and the count strictly above it. The histogram
 // is the sum of R copies laid out kHistBins apart.
@@ -153,28 +137,49 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
                                                                            (uint32_t)r, sh_scan, &sh_u[0], &sh_u[1]);
     const uint32_t bstar = sh_u[0];
 
-    // The slot is this workgroup's own: list entries go straight to it, at
-    // positions handed out by the LDS counters (one atomic per wave and list).
+    // The slot is this workgroup's own: list entries go straight to it. A
+    // wave ballots its items first, takes room for all of them with one LDS
+    // atomic per list, and places each item by the popcounts of the ballots.
     const int64_t slot = (int64_t)b * n_slices + slice;
     int32_t *my_def = slot_def + slot * kSliceBlocks;
     uint64_t *my_cand = slot_cand + slot * kSliceBlocks;
+    const int lane = tid & 63;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint64_t md[kCollectPer], mc[kCollectPer];
+    uint32_t key[kCollectPer];
+    uint32_t nd = 0, nc = 0;
 #pragma unroll
     for (int k = 0; k < kCollectPer; k++) {
         const int j = j0 + k * kCollectThreads + tid;
         bool is_def = false, is_cand = false;
-        uint32_t key = 0;
+        key[k] = 0;
         if (j < n && j >= sink_blocks && j < tail_first) {
-            key = order_key(v[k]);
-            const uint32_t bin = key >> kHistShift;
+            key[k] = order_key(v[k]);
+            const uint32_t bin = key[k] >> kHistShift;
             is_def = bin > bstar;
             is_cand = bin == bstar;
         }
-        const uint32_t pd = wave_append(is_def, &sh_u[2]);
-        const uint32_t pc = wave_append(is_cand, &sh_u[3]);
-        if (is_def)
-            my_def[pd] = j;                         // at most kSliceBlocks items per slice
-        if (is_cand)
-            my_cand[pc] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+        md[k] = __ballot(is_def);
+        mc[k] = __ballot(is_cand);
+        nd += (uint32_t)__popcll(md[k]);
+        nc += (uint32_t)__popcll(mc[k]);
+    }
+    uint32_t bd = 0, bc = 0;
+    if (lane == 0) {
+        bd = nd ? atomicAdd(&sh_u[2], nd) : 0u;
+        bc = nc ? atomicAdd(&sh_u[3], nc) : 0u;
+    }
+    bd = __shfl(bd, 0);
+    bc = __shfl(bc, 0);
+#pragma unroll
+    for (int k = 0; k < kCollectPer; k++) {
+        const int j = j0 + k * kCollectThreads + tid;
+        if ((md[k] >> lane) & 1ull)
+            my_def[bd + __popcll(md[k] & lt)] = j;                  // at most kSliceBlocks items per slice
+        if ((mc[k] >> lane) & 1ull)
+            my_cand[bc + __popcll(mc[k] & lt)] = ((uint64_t)key[k] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+        bd += (uint32_t)__popcll(md[k]);
+        bc += (uint32_t)__popcll(mc[k]);
     }
     __syncthreads();
     if (tid == 0) {
