@@ -167,8 +167,9 @@ const void *pool_device_ptr(const void *p, qsa_kv_location_t loc)
     return a.devicePointer;
 }
 
-// Events for the two-stream offload schedule, created once per device and
-// kept for the life of the process.
+// Events that order the streams of the overlapped schedules (fork, join,
+// per-layer scans), created once per device and kept for the life of the
+// process.
 struct EventPool {
     std::mutex mu;
     std::vector<std::vector<hipEvent_t>> per_dev;

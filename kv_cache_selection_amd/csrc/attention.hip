@@ -5,26 +5,27 @@
 //     z_t = sm_scale * (q_h . K_{g,t}),   out_h = sum_t softmax(z)_t V_{g,t}
 // (the attention the article's "fast path" computes, restricted to the
 // gathered set). The tokens are split into chunks of kTPS = 128; a workgroup
-// (sequence b, KV head g, split s) attends the 8 query heads of g over its
-// chunk, one wave per 32 tokens, and writes the normalised partial output and
-// its log-sum-exp; the merge kernel combines the splits exactly:
-// out = sum_s e^{lse_s - LSE} O_s.
+// (split s, KV head g, sequence b, layer of the launch) attends the 8 query
+// heads of g over its chunk, one wave per 32 tokens, and writes the
+// normalised partial output and its log-sum-exp; the merge kernel combines
+// the splits exactly: out = sum_s e^{lse_s - LSE} O_s.
 //
-// Per wave and tile of 16 tokens:
+// Per wave (two tiles of 16 tokens):
+//  - all K and V rows of both tiles are requested before the first multiply;
 //  - QK^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = the 8 query
 //    heads (rows 8..15 zero) and B = 32 dims x 16 tokens read straight from
 //    the KV rows (each lane loads 16 contiguous bytes of one token's K);
-//  - online softmax over the tile in fp32, statistics reduced across the 16
-//    lanes that hold one head's scores;
-//  - PV on the VALU in fp32: each lane owns 4 of the 256 dims for all 8
-//    heads and streams the tile's V rows (8 contiguous bytes per lane and
-//    token), the tile's probabilities broadcast through LDS.
-// The four waves of a workgroup merge their partial states in LDS. All rows
-// of a wave's two tiles are requested before the first multiply.
+//  - one softmax over the wave's 32 tokens in fp32, the statistics reduced
+//    across the 16 lanes that hold one head's scores with DPP row operations;
+//  - PV on the matrix cores as well: the V rows go through LDS, where
+//    ds_read_b64_tr_b16 reads them transposed (k = tokens), and P enters as
+//    an exact bf16 high part plus a bf16 remainder (16 mantissa bits).
+// The four waves of a workgroup then merge their partial states in LDS.
 //
-// Rows come either from the staging area (qsa_sparse_decode, offload path) or
-// straight from the KV pool through the page table (gather fused into the
-// attention when the pool is in HBM).
+// Rows come either from the staging area (qsa_sparse_decode, the pinned-host
+// path) or straight from the KV pool through the page table (the gather is
+// fused into the attention when the pool is in HBM). One launch may cover
+// several layers: their pointers travel in the kernel arguments.
 #include "qsa_internal.h"
 
 namespace qsa {

@@ -22,6 +22,9 @@
 // The VALU only widens codes and runs the ReLU/weight epilogue and the block
 // max, so the kernel stays bound by HBM, not by fp32 FMA throughput.
 //
+// One launch may scan several layers (grid z), their pointers in the kernel
+// arguments, so that the scan streams from one layer into the next.
+//
 // When the sequence has more blocks than the budget, each workgroup also
 // builds an LDS histogram of the top 12 bits of its blocks' order keys
 // (forced blocks excluded) and adds it to the sequence's global histogram:

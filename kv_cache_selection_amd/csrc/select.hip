@@ -11,10 +11,10 @@
 //  1. (fused into scoring, or block_hist_kernel) a per-sequence histogram of
 //     the key's top 12 bits over the non-forced blocks;
 //  2. collect_kernel: one workgroup per slice of 2048 blocks finds the
-//     threshold bin b* from the histogram and compacts, in LDS, the slice's
-//     blocks above b* ("definite") and inside b* ("candidates", as 64-bit
+//     threshold bin b* from the histogram and writes the slice's blocks
+//     above b* ("definite") and inside b* ("candidates", as 64-bit
 //     composites key << 32 | ~index: unique, and ordered like (score desc,
-//     index asc)); it writes them with their counts to the slice's own slot;
+//     index asc)) with their counts to the slice's own slot;
 //  3. finish_kernel: one workgroup per sequence gathers the slots through
 //     prefix offsets, picks the best need = K - |F| - |definite| candidates
 //     exactly with a radix select over the composites' remaining 64 - 12 bits
@@ -25,7 +25,9 @@
 // a few hot addresses (they serialise at the memory side) and no
 // device-scope fences (on gfx950 one writes back and invalidates the XCD's
 // L2). The kernel boundary orders the slots, and the scan of the scores is
-// spread over many CUs.
+// spread over many CUs. One launch may cover several layers (grid z for
+// collect_kernel, y for finish_kernel): their pointers travel in the kernel
+// arguments.
 #include "qsa_internal.h"
 
 namespace qsa {
