@@ -7,7 +7,9 @@
 // rows are moved, over PCIe when the pool lives in pinned host memory).
 // One workgroup copies the rows of kBlocksPerWg selected C4 blocks; every
 // lane moves 16-byte pieces so a row is one contiguous 2 KB burst, which is
-// what both HBM and PCIe reads want.
+// what both HBM and PCIe reads want. One launch may gather several layers
+// (grid z), their pointers in the kernel arguments, so that the PCIe reads
+// of all of them stream without a break.
 #include "qsa_internal.h"
 
 namespace qsa {
