@@ -427,6 +427,42 @@ def test_decode_step_page_table_permutation_invariant(gpu):
     assert np.array_equal(out1, out2)
 
 
+def test_decode_step_per_layer_page_table(gpu):
+    """A layer may bring its own page table (qsa_layer_t.page_table): moving
+    layer 1's rows to other slots of its pool and giving that layer the
+    rewritten table leaves every output bit for bit unchanged, on one stream,
+    in the grouped HBM schedule and on the pinned-host path."""
+    wl = S.WORKLOADS["batch8-short"]
+    di = DeviceInputs(wl, gpu, layers=3)
+    K = wl.budget // 4
+    L = di.n_layers
+    perm = torch.from_numpy(np.random.default_rng(11).permutation(di.n_slots)).to(gpu)
+    pool1 = torch.empty_like(di.pool[1])
+    pool1[perm] = di.pool[1]
+    pt1 = torch.where(di.pt >= 0, perm[di.pt.clamp(min=0).long()].int(), di.pt)
+    for kv_host in (False, True):
+        d = di if not kv_host else DeviceInputs(wl, gpu, layers=3, kv_host=True, hi=di.hi)
+        loc = qsa.QSA_KV_HOST_PINNED if kv_host else qsa.QSA_KV_DEVICE
+        p1 = pool1 if not kv_host else pool1.cpu().pin_memory()
+        for n_side in (0, 1):
+            outs = []
+            for own_table in (False, True):
+                sel = torch.full((L, d.batch, K), -7, dtype=torch.int32, device="cuda")
+                ns = torch.zeros((L, d.batch), dtype=torch.int32, device="cuda")
+                d.out.zero_()
+                layers = [qsa.make_layer(d.keys[l], d.scales[l], d.q_idx[l], d.w_idx[l], d.q[l],
+                                         p1 if (own_table and l == 1) else d.pool[l], d.out[l],
+                                         pt1 if (own_table and l == 1) else None, sel[l], ns[l]) for l in range(L)]
+                cfg = _cfg(wl)
+                ws, nws = _ws(cfg, d.batch, d.max_ctx, L, loc)
+                side = [torch.cuda.Stream() for _ in range(n_side)]
+                qsa.qsa_decode_step(cfg, _batch(d), layers, loc, ws, nws, torch.cuda.current_stream(), side)
+                torch.cuda.synchronize()
+                outs.append((sel.cpu().numpy(), d.out.cpu().numpy()))
+            assert np.array_equal(outs[0][0], outs[1][0]), (kv_host, n_side)
+            assert np.array_equal(outs[0][1], outs[1][1]), (kv_host, n_side)
+
+
 def test_decode_step_budget_covers_context_is_dense(gpu):
     """With the budget above the context every block is selected and the step
     is dense softmax attention over all tokens."""
