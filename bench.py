@@ -505,8 +505,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: the QSA decode step runs on a single MI355X and this build has "
-              "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: libqsa runs the QSA decode step on a single MI355X and has no "
+              "multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.op == "append":
         bench_append(args)
