@@ -233,7 +233,9 @@ __global__ __launch_bounds__(kThreads) void multi_score_kernel(
         else
             score_tile(t0, std::true_type{});
         __syncthreads();
-        // rows of 64 block scores per query
+        // rows of 64 block scores per query, with non-temporal stores (the
+        // writes are as many bytes as the index reads at Q = 64, and ordinary
+        // stores slow the read stream down)
         const int blk0 = t0 / kBT;
 #pragma unroll
         for (int k = 0; k < Q / 4; k++) {
@@ -241,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void multi_score_kernel(
             const int qi = idx >> 6;
             const int blk = blk0 + (idx & 63);
             if (blk < n_blk)
-                out_b[(int64_t)qi * bs_stride + blk] = stage[qi][(idx & 63) ^ (16 * (qi & 1))];
+                __builtin_nontemporal_store(stage[qi][(idx & 63) ^ (16 * (qi & 1))],
+                                            out_b + (int64_t)qi * bs_stride + blk);
         }
     }
 }
