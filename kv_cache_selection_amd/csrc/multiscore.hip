@@ -157,6 +157,13 @@ __global__ __launch_bounds__(kThreads) void multi_score_kernel(
         wv[r] = *reinterpret_cast<const f32x4 *>(w_idx + ((int64_t)b * Q + qi) * kIdxH);
         pq[r] = posq[qi];
     }
+    // Use the operands once here, so the wait for their loads is placed
+    // before the loop. Otherwise the compiler waits for them inside the
+    // scoring pass of every tile, where the same counter also covers the next
+    // tile's prefetch, and that prefetch stops overlapping the pass.
+#pragma unroll
+    for (int r = 0; r < RBW; r++)
+        asm volatile("" ::"v"(qa[r][0]), "v"(qa[r][1]), "v"(wv[r]));
 
     float pinf;
     asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(pinf));
