@@ -111,30 +111,55 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
     // l holds token l & 15 of each tile). On the paged path the row is the
     // page-table slot of the selected token; indices are clamped so that
     // every read stays inside its buffer before the count is known.
+    // The loads are unconditional (selects come after them), so that the
+    // compiler can count them: the selection entries of both tiles and the
+    // query go out together, then the page-table slots of both tiles.
     int nt = n_tok[b];
     int64_t row_k[kTiles];
+    int ptok[kTiles], stok[kTiles];
 #pragma unroll
     for (int i = 0; i < kTiles; i++) {
-        int p = wave_p0 + kTile * i + arow;
-        p = p < budget_tokens ? p : budget_tokens - 1;
-        if (kPaged) {
-            int t = sel[(int64_t)b * budget_blocks + (p >> 2)] * kBT + (p & 3);
-            t = t < max_ctx ? t : max_ctx - 1;
-            row_k[i] = t >= 0 ? safe_slot(pt[(int64_t)b * pt_stride + t], n_slots) : 0;
-        } else {
-            row_k[i] = (int64_t)b * budget_tokens + p;
-        }
+        const int p = min(wave_p0 + kTile * i + arow, budget_tokens - 1);
+        ptok[i] = p;
+        if (kPaged)
+            stok[i] = sel[(int64_t)b * budget_blocks + (p >> 2)];
     }
-    // A operand: lane holds row (lane & 15) = query head of group g (rows 8..15
-    // zero), dims 32kk + 8 (lane >> 4) .. +8 for MFMA kk.
+    // A operand: lane holds row (lane & 15) = query head of group g, dims
+    // 32kk + 8 (lane >> 4) .. +8 for MFMA kk. Rows 8..15 repeat rows 0..7;
+    // their outputs land in lanes 32..63, which carry no head and are never
+    // used.
     bf16x8 qa[kDh / 32];
     {
         const uint16_t *qr = q + ((int64_t)b * kHq + g * kGroup + (arow & 7)) * kDh + kofs;
 #pragma unroll
-        for (int kk = 0; kk < kDh / 32; kk++) {
-            const u32x4 v = arow < kGroup ? *reinterpret_cast<const u32x4 *>(qr + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
-            qa[kk] = __builtin_bit_cast(bf16x8, v);
+        for (int kk = 0; kk < kDh / 32; kk++)
+            qa[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 32 * kk));
+    }
+    if (kPaged) {
+        // token t of the selection; a block index outside the context (only
+        // in entries past the count) reads slot 0. With no context the table
+        // may be empty, so a selection entry is read instead.
+        int32_t slot[kTiles];
+        bool in[kTiles];
+#pragma unroll
+        for (int i = 0; i < kTiles; i++) {
+            const int t = stok[i] * kBT + (ptok[i] & 3);
+            in[i] = t >= 0 && max_ctx > 0;
+            const int tc = min(max(t, 0), max_ctx - 1);
+            const int32_t *src = max_ctx > 0 ? pt + (int64_t)b * pt_stride + tc : sel + (int64_t)b * budget_blocks;
+            slot[i] = *src;
         }
+        // both slots are used here, so both reads are issued before either
+        // is waited for (not moved into the branches of the selects below)
+        static_assert(kTiles == 2, "two tiles per wave");
+        asm volatile("" : "+v"(slot[0]), "+v"(slot[1]));
+#pragma unroll
+        for (int i = 0; i < kTiles; i++)
+            row_k[i] = in[i] ? safe_slot(slot[i], n_slots) : 0;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kTiles; i++)
+            row_k[i] = (int64_t)b * budget_tokens + ptok[i];
     }
 
     nt = nt < 0 ? 0 : (nt > budget_tokens ? budget_tokens : nt);
@@ -143,35 +168,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
         if (tid < kGroup)
             part_lse[part_base + (int64_t)tid * n_split] = -INFINITY;
         return;
-    }
-
-    // Request every row the wave needs before the first multiply. The V rows
-    // of a tile's 16 tokens are the K rows held by lanes 0..15.
-    u32x4 kd[kTiles][kDh / 32];
-    u32x2 vd[kTiles][kTile];
-#pragma unroll
-    for (int i = 0; i < kTiles; i++) {
-        const int pt0 = wave_p0 + kTile * i;
-        if (pt0 + arow < nt) {
-            const uint8_t *rk = rows + row_k[i] * kRowBytes + g * kKBytes + 2 * kofs;
-#pragma unroll
-            for (int kk = 0; kk < kDh / 32; kk++)
-                kd[i][kk] = *reinterpret_cast<const u32x4 *>(rk + 64 * kk);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < kDh / 32; kk++)
-                kd[i][kk] = u32x4{0u, 0u, 0u, 0u};
-        }
-        const uint32_t rlo = (uint32_t)row_k[i], rhi = (uint32_t)(row_k[i] >> 32);
-#pragma unroll
-        for (int t = 0; t < kTile; t++) {
-            // uniform across the wave: token pt0 + t, whose row lane t holds
-            const int64_t r = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(rhi, t) << 32) |
-                                        __builtin_amdgcn_readlane(rlo, t));
-            vd[i][t] = pt0 + t < nt
-                           ? *reinterpret_cast<const u32x2 *>(rows + r * kRowBytes + (kHkv + g) * kKBytes + 8 * lane)
-                           : u32x2{0u, 0u};
-        }
     }
 
     // Softmax state of the wave: lane l holds heads 4 (l >> 4) + v (rows 8..15
@@ -195,12 +191,33 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
             l_run[v] = 0.0f;
         }
     } else {
-        // V rows of both tiles to LDS (row 16 i + t) while QK^T runs.
+        // Request every row the wave needs before the first multiply: the K
+        // rows of both tiles, then their V rows (the V rows of a tile's 16
+        // tokens are the K rows held by lanes 0..15). Every request is made,
+        // also for tokens past the count, whose row indices are clamped to
+        // valid rows and whose scores and V rows are masked below; so the
+        // compiler can count the requests, and QK^T and the softmax start as
+        // soon as the K rows are in, while the V rows still arrive.
+        u32x4 kd[kTiles][kDh / 32];
+        u32x2 vd[kTiles][kTile];
 #pragma unroll
-        for (int i = 0; i < kTiles; i++)
+        for (int i = 0; i < kTiles; i++) {
+            const uint8_t *rk = rows + row_k[i] * kRowBytes + g * kKBytes + 2 * kofs;
 #pragma unroll
-            for (int t = 0; t < kTile; t++)
-                *reinterpret_cast<u32x2 *>(vt + (kTile * i + t) * kVPitch + 8 * lane) = vd[i][t];
+            for (int kk = 0; kk < kDh / 32; kk++)
+                kd[i][kk] = *reinterpret_cast<const u32x4 *>(rk + 64 * kk);
+        }
+#pragma unroll
+        for (int i = 0; i < kTiles; i++) {
+            const uint32_t rlo = (uint32_t)row_k[i], rhi = (uint32_t)(row_k[i] >> 32);
+#pragma unroll
+            for (int t = 0; t < kTile; t++) {
+                // uniform across the wave: token wave_p0 + 16 i + t, whose row lane t holds
+                const int64_t r = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(rhi, t) << 32) |
+                                            __builtin_amdgcn_readlane(rlo, t));
+                vd[i][t] = *reinterpret_cast<const u32x2 *>(rows + r * kRowBytes + (kHkv + g) * kKBytes + 8 * lane);
+            }
+        }
         f32x4 acc[kTiles];
 #pragma unroll
         for (int i = 0; i < kTiles; i++) {
@@ -236,6 +253,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
             l_run[v] = row16_reduce<false>(sum);
             m_run[v] = mx;
         }
+        // V rows of both tiles to LDS (row 16 i + t), zero past the count
+#pragma unroll
+        for (int i = 0; i < kTiles; i++)
+#pragma unroll
+            for (int t = 0; t < kTile; t++)
+                *reinterpret_cast<u32x2 *>(vt + (kTile * i + t) * kVPitch + 8 * lane) =
+                    wave_p0 + kTile * i + t < nt ? vd[i][t] : u32x2{0u, 0u};
         wave_lds_sync();
 
         // PV on the matrix cores, v_mfma_f32_16x16x32_bf16 per 16 dims:
