@@ -53,22 +53,14 @@ static_assert(kDigitBins + 2 * kThreads <= kWorkWords, "digit histogram and shor
 constexpr size_t kSmemBytes = (size_t)kCandCap * 8 + (size_t)kDefCap * 4 + (size_t)kWorkWords * 4;
 
 // Walk a histogram of NT * W bins from the top: the bin where the running
-// count first reaches `want`, and the count strictly above it. The histogram
-// is the sum of R copies laid out kHistBins apart.
-template <int W, int NT, int R = 1>
-__device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
-                              uint32_t *above_out)
+// count first reaches `want`, and the count strictly above it. Thread i
+// holds bins W (NT - 1 - i) .. + W - 1 in hv, so thread 0 holds the top ones.
+template <int W, int NT>
+__device__ void crossing_of(const uint32_t (&hv)[W], uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
+                            uint32_t *above_out)
 {
-    const int tr = NT - 1 - threadIdx.x;               // thread 0 owns the top bins
-    uint32_t hv[W], local = 0;
-#pragma unroll
-    for (int i = 0; i < W; i++)
-        hv[i] = h[W * tr + i];
-#pragma unroll
-    for (int c = 1; c < R; c++)
-#pragma unroll
-        for (int i = 0; i < W; i++)
-            hv[i] += h[c * kHistBins + W * tr + i];
+    const int tr = NT - 1 - threadIdx.x;
+    uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < W; i++)
         local += hv[i];
@@ -83,6 +75,19 @@ __device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_sca
         above += hv[i];
     }
     __syncthreads();
+}
+
+// The same over a histogram in memory.
+template <int W, int NT>
+__device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
+                              uint32_t *above_out)
+{
+    const int tr = NT - 1 - threadIdx.x;
+    uint32_t hv[W];
+#pragma unroll
+    for (int i = 0; i < W; i++)
+        hv[i] = h[W * tr + i];
+    crossing_of<W, NT>(hv, want, sh_scan, bin_out, above_out);
 }
 
 // Number of non-forced blocks to take, or -1 when every block fits.
@@ -120,14 +125,32 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
     if (r <= 0 || j0 >= n)
         return;
 
-    // The slice's scores are requested first; their latency overlaps the
-    // histogram walk.
+    // The histogram copies of the sequence are requested first, then the
+    // slice's scores, whose latency overlaps the histogram walk. The score
+    // reads are unconditional (past the end they repeat the last block,
+    // whose copies are never used): the compiler can then count them, and
+    // since loads are counted in the order they were issued, the walk waits
+    // only for the histogram.
+    constexpr int W = kHistBins / kCollectThreads;
+    const uint32_t *hb = hist + ((int64_t)b * kHistReps * kHistBins + W * (kCollectThreads - 1 - tid));
+    uint32_t hraw[kHistReps][W];
+#pragma unroll
+    for (int c = 0; c < kHistReps; c++)
+#pragma unroll
+        for (int i = 0; i < W; i++)
+            hraw[c][i] = hb[c * kHistBins + i];
     const float *row = block_scores + (int64_t)b * bs_stride;
     float v[kCollectPer];
 #pragma unroll
-    for (int k = 0; k < kCollectPer; k++) {
-        const int j = j0 + k * kCollectThreads + tid;
-        v[k] = j < n ? row[j] : 0.0f;
+    for (int k = 0; k < kCollectPer; k++)
+        v[k] = row[min(j0 + k * kCollectThreads + tid, n - 1)];
+    uint32_t hv[W];
+#pragma unroll
+    for (int i = 0; i < W; i++) {
+        hv[i] = 0;
+#pragma unroll
+        for (int c = 0; c < kHistReps; c++)
+            hv[i] += hraw[c][i];
     }
     if (tid == 0) {
         sh_u[0] = kHistBins;
@@ -135,8 +158,7 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
         sh_u[3] = 0;
     }
     __syncthreads();
-    find_crossing<kHistBins / kCollectThreads, kCollectThreads, kHistReps>(hist + (int64_t)b * kHistReps * kHistBins,
-                                                                           (uint32_t)r, sh_scan, &sh_u[0], &sh_u[1]);
+    crossing_of<W, kCollectThreads>(hv, (uint32_t)r, sh_scan, &sh_u[0], &sh_u[1]);
     const uint32_t bstar = sh_u[0];
 
     // The slot is this workgroup's own: list entries go straight to it. A
