@@ -572,16 +572,45 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return hip_status(e);
     }
 
+    // The per-layer pointer tables of layers l0 .. l0 + nl - 1 (HBM pools).
+    auto hbm_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, AttnLayers &AL) {
+        for (int i = 0; i < nl; i++) {
+            const int l = l0 + i;
+            const qsa_layer_t &Ly = layers[l];
+            CL.keys[i] = Ly.idx_keys;
+            CL.scales[i] = Ly.idx_scales;
+            CL.q_idx[i] = Ly.q_idx;
+            CL.w_idx[i] = Ly.w_idx;
+            CL.block_scores[i] = lw[l].bs;
+            CL.hist[i] = lw[l].sw.hist;
+            SL.bs[i] = lw[l].bs;
+            SL.ws[i] = lw[l].sw;
+            SL.sel[i] = lw[l].sel;
+            SL.n_sel[i] = lw[l].nsel;
+            SL.n_tok[i] = lw[l].ntok;
+            AL.q[i] = Ly.q;
+            AL.rows[i] = static_cast<const uint8_t *>(pools[l]);
+            AL.pt[i] = lw[l].pt;
+            AL.n_slots[i] = batch->n_slots;
+            AL.sel[i] = lw[l].sel;
+            AL.n_tok[i] = lw[l].ntok;
+            AL.part_o[i] = lw[l].aw.part_o;
+            AL.part_lse[i] = lw[l].aw.part_lse;
+            AL.out[i] = Ly.out;
+        }
+    };
+
     if (!offload && !hot) {
         // Pools in HBM. The layers go in groups of up to kMaxChainLayers: one
         // launch scans the whole group's index (the layer is a grid
         // coordinate, so the scan streams without a break between layers),
-        // then one launch each of collect, finish, attention and merge
-        // selects and attends the whole group. A group costs one latency
-        // chain instead of one per layer, and its attention is a single wide
-        // launch; running the chains during the scans instead only takes CUs
-        // and bandwidth from the scans. With one group everything runs on
-        // the compute stream. With several, the chains run on side 0, so a
+        // then one launch each of the selection, attention and merge kernels
+        // covers the whole group. A group costs one latency chain instead of
+        // one per layer, and its attention is a single wide launch; running
+        // the chains during the scans instead only takes CUs and bandwidth
+        // from the scans, and every dependency between streams adds 6-13 us
+        // before the waiting kernel starts. With one group everything runs
+        // on the compute stream. With several, the chains run on side 0, so a
         // group's chain overlaps the next group's scan. The first layer's
         // score events of a group time that group's scan.
         const hipStream_t cs = n_layers > kMaxChainLayers ? (hipStream_t)side[0] : sc;
@@ -596,30 +625,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             ScoreLayers CL = {};
             SelectLayers SL = {};
             AttnLayers AL = {};
-            for (int i = 0; i < nl; i++) {
-                const int l = l0 + i;
-                const qsa_layer_t &Ly = layers[l];
-                CL.keys[i] = Ly.idx_keys;
-                CL.scales[i] = Ly.idx_scales;
-                CL.q_idx[i] = Ly.q_idx;
-                CL.w_idx[i] = Ly.w_idx;
-                CL.block_scores[i] = lw[l].bs;
-                CL.hist[i] = lw[l].sw.hist;
-                SL.bs[i] = lw[l].bs;
-                SL.ws[i] = lw[l].sw;
-                SL.sel[i] = lw[l].sel;
-                SL.n_sel[i] = lw[l].nsel;
-                SL.n_tok[i] = lw[l].ntok;
-                AL.q[i] = Ly.q;
-                AL.rows[i] = static_cast<const uint8_t *>(pools[l]);
-                AL.pt[i] = lw[l].pt;
-                AL.n_slots[i] = batch->n_slots;
-                AL.sel[i] = lw[l].sel;
-                AL.n_tok[i] = lw[l].ntok;
-                AL.part_o[i] = lw[l].aw.part_o;
-                AL.part_lse[i] = lw[l].aw.part_lse;
-                AL.out[i] = Ly.out;
-            }
+            hbm_tables(l0, nl, CL, SL, AL);
             e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B,
                                           batch->max_ctx, bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
                                           (hipEvent_t)layers[l0].score_events[0],

@@ -21,6 +21,10 @@
 //     (11-bit digits, finishing by direct ranking once few are left), and
 //     writes the union in ascending order through an LDS bitmap, so the
 //     output needs no sort.
+// Sequences of up to 16,384 blocks (65,536 tokens) skip steps 2 and 3:
+// select_one_kernel holds all of a sequence's scores in one workgroup's
+// registers and selects in one launch (radix passes over the registers, and
+// an equal-key bitmap for the ties of the last key).
 // Nothing is shared between workgroups inside a kernel: no global atomics on
 // a few hot addresses (they serialise at the memory side) and no
 // device-scope fences (on gfx950 one writes back and invalidates the XCD's
@@ -57,7 +61,7 @@ constexpr size_t kSmemBytes = (size_t)kCandCap * 8 + (size_t)kDefCap * 4 + (size
 // holds bins W (NT - 1 - i) .. + W - 1 in hv, so thread 0 holds the top ones.
 template <int W, int NT>
 __device__ void crossing_of(const uint32_t (&hv)[W], uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
-                            uint32_t *above_out)
+                            uint32_t *above_out, uint32_t *in_bin_out = nullptr)
 {
     const int tr = NT - 1 - threadIdx.x;
     uint32_t local = 0;
@@ -71,6 +75,8 @@ __device__ void crossing_of(const uint32_t (&hv)[W], uint32_t want, uint32_t *sh
         if (above < want && above + hv[i] >= want) {
             *bin_out = W * tr + i;
             *above_out = above;
+            if (in_bin_out)
+                *in_bin_out = hv[i];
         }
         above += hv[i];
     }
@@ -452,6 +458,244 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(const SelectLayersT<N>
     }
 }
 
+// One workgroup of kOneThreads per (sequence, layer): grid (B, layers). For
+// sequences of at most kOneThreads * PER blocks the whole selection runs in
+// one kernel, with every block score of the sequence held in registers
+// (thread t holds blocks t + kOneThreads * i, i < PER):
+//  1. the histogram copies and all block scores are requested together, the
+//     scores clamped to the largest context, so one round trip brings both;
+//  2. the 12-bit histogram gives the threshold bin; radix passes over the
+//     scores still inside the threshold prefix (11-bit digits of the order
+//     key, LDS histograms) refine it until the crossing bin holds exactly
+//     the blocks still wanted, or the key is complete;
+//  3. if the key is complete and only m of the blocks sharing it are wanted,
+//     the m with the lowest indices are taken: their ranks come from a
+//     bitmap of the equal keys and its per-word prefix counts;
+//  4. the forced and chosen blocks form a bitmap (one ballot per wave gives
+//     64 consecutive bits), written out in ascending order by an ordered
+//     compaction.
+// The result is the same set as collect_kernel + finish_kernel give.
+constexpr int kOneThreads = 1024;
+// Longest sequence of the one-kernel route: kOneThreads * kOneMaxPer blocks
+// (65,536 tokens). Past that one CU cannot bring the scores in fast enough:
+// at 65,536 blocks (256 KB of scores) the kernel took 26.7 us per layer,
+// against 13.7 us for collect_kernel + finish_kernel.
+constexpr int kOneMaxPer = 16;
+
+template <int N, int PER>
+__global__ __launch_bounds__(kOneThreads) void select_one_kernel(const SelectLayersT<N> Ls, int64_t bs_stride,
+                                                                 const int32_t *__restrict__ ctx_len, int max_ctx,
+                                                                 int K, int sink_blocks, int tail_tokens)
+{
+    static_assert(PER >= 1 && PER <= 64 && (PER & (PER - 1)) == 0, "a power of two up to 64");
+    constexpr int kWords = kOneThreads * PER / 32;  // bitmap words over the sequence's blocks
+    constexpr int WPT = PER >= 32 ? PER / 32 : 1;   // words per thread in the ordered compaction
+    const bool owns_words = WPT * threadIdx.x < kWords;   // threads past the bitmap own none
+    static_assert(kWords <= kDigitBins, "word prefixes reuse the digit histogram");
+    const float *__restrict__ block_scores = Ls.bs[blockIdx.y];
+    const uint32_t *__restrict__ hist = Ls.ws[blockIdx.y].hist;
+    int32_t *__restrict__ sel = Ls.sel[blockIdx.y];
+    int32_t *__restrict__ n_sel = Ls.n_sel[blockIdx.y];
+    int32_t *__restrict__ n_tok = Ls.n_tok[blockIdx.y];
+    __shared__ __attribute__((aligned(16))) uint32_t bm[kWords];   // equal-key bitmap, then the selection
+    __shared__ uint32_t dh[kDigitBins];             // digit histogram, then per-word prefix counts
+    __shared__ uint32_t sh_scan[kOneThreads / 64];
+    __shared__ uint32_t sh_u[4];                    // crossing bin / count above / count in the bin
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nmax = (max_ctx + kBT - 1) / kBT;     // > K >= 1 (host), and <= bs_stride
+
+    // One round of loads: the length, the histogram copies, every score.
+    const int32_t Lraw = ctx_len[b];
+    constexpr int W = kHistBins / kOneThreads;
+    const uint32_t *hb = hist + ((int64_t)b * kHistReps * kHistBins + W * (kOneThreads - 1 - tid));
+    uint32_t hraw[kHistReps][W];
+#pragma unroll
+    for (int c = 0; c < kHistReps; c++)
+#pragma unroll
+        for (int i = 0; i < W; i++)
+            hraw[c][i] = hb[c * kHistBins + i];
+    const float *row = block_scores + (int64_t)b * bs_stride;
+    uint32_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+        key[i] = __float_as_uint(row[min(tid + kOneThreads * i, nmax - 1)]);
+
+    const int L = clamp_ctx(Lraw, max_ctx);
+    const int n = (L + kBT - 1) / kBT;
+    int32_t *sel_b = sel + (int64_t)b * K;
+    int tail_first = n;
+    const int r = rest_to_take(L, n, K, sink_blocks, tail_tokens, &tail_first);
+    if (r < 0) {
+        // Every block fits in the budget.
+        for (int j = tid; j < K; j += kOneThreads)
+            sel_b[j] = j < n ? j : -1;
+        if (tid == 0) {
+            n_sel[b] = n;
+            if (n_tok)
+                n_tok[b] = L;
+        }
+        return;
+    }
+
+    // Blocks outside [first_el, end_el) are forced or past the sequence. A
+    // block that is not eligible gets key 0, which never matches a threshold
+    // prefix: keys below 2^20 (histogram bin 0) are NaN codes, so for scores
+    // that are numbers the threshold bin, and with it pfx, is above 0.
+    const int first_el = min(sink_blocks, n);
+    const int end_el = max(tail_first, first_el);
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int j = tid + kOneThreads * i;
+        const bool el = j >= first_el && j < end_el;
+        key[i] = el ? order_key(__uint_as_float(key[i])) : 0u;
+    }
+
+    // ---- the threshold: chosen <=> key's prefix above pfx, or equal to it
+    //      (and, on a complete key with ties, among the m lowest indices) ----
+    uint32_t pfx = 0xFFFFFFFFu, pmask = 0xFFFFFFFFu;
+    bool pick = r > 0;                              // some non-forced blocks are taken
+    bool tie = false;
+    uint32_t m = 0;
+    if (r > 0) {
+        uint32_t hv[W];
+#pragma unroll
+        for (int i = 0; i < W; i++) {
+            hv[i] = 0;
+#pragma unroll
+            for (int c = 0; c < kHistReps; c++)
+                hv[i] += hraw[c][i];
+        }
+        if (tid == 0) {
+            sh_u[0] = kHistBins;                    // no crossing: nothing is chosen
+            sh_u[1] = 0;
+            sh_u[2] = 0;
+        }
+        __syncthreads();
+        crossing_of<W, kOneThreads>(hv, (uint32_t)r, sh_scan, &sh_u[0], &sh_u[1], &sh_u[2]);
+        uint32_t want = (uint32_t)r - sh_u[1];
+        uint32_t in_bin = sh_u[2];
+        pfx = sh_u[0] << kHistShift;
+        pmask = ~0u << kHistShift;
+        int shift = kHistShift;
+        if (sh_u[0] >= (uint32_t)kHistBins) {       // histogram inconsistent with the lengths: take none
+            pick = false;
+            in_bin = 0;
+            want = 0;
+        }
+        __syncthreads();
+        while (in_bin != want && shift > 0) {       // uniform
+            const int bits = shift >= kDigitBits ? kDigitBits : shift;
+            shift -= bits;
+            const uint32_t dmask = (1u << bits) - 1u;
+            for (int i = tid; i < kDigitBins; i += kOneThreads)
+                dh[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < PER; i++)
+                if ((key[i] & pmask) == pfx)
+                    atomicAdd(&dh[(key[i] >> shift) & dmask], 1u);
+            __syncthreads();
+            find_crossing<kDigitBins / kOneThreads, kOneThreads>(dh, want, sh_scan, &sh_u[0], &sh_u[1]);
+            const uint32_t digit = sh_u[0];
+            in_bin = dh[digit];
+            want -= sh_u[1];
+            pfx |= digit << shift;
+            pmask |= dmask << shift;
+            __syncthreads();
+        }
+        tie = in_bin != want;                       // complete key, only `want` of its blocks taken
+        m = want;
+    }
+
+    if (tie) {
+        // Equal keys in ascending block order: bitmap, per-word prefix, rank.
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const uint64_t bal = __ballot(key[i] == pfx);
+            if (lane == 0)
+                *reinterpret_cast<uint64_t *>(&bm[(kOneThreads * i + 64 * wave) >> 5]) = bal;
+        }
+        __syncthreads();
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int w = 0; w < WPT; w++)
+            cnt += owns_words ? __popc(bm[WPT * tid + w]) : 0u;
+        uint32_t total;
+        uint32_t pos = block_inclusive_scan<kOneThreads>(cnt, sh_scan, &total) - cnt;
+        if (owns_words) {
+#pragma unroll
+            for (int w = 0; w < WPT; w++) {
+                dh[WPT * tid + w] = pos;
+                pos += __popc(bm[WPT * tid + w]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- the selection bitmap: forced blocks and chosen ones ----------------
+    // A wave's ballot of round i covers words 32 i + 2 wave and + 1, which
+    // hold only this wave's blocks of that round: the equal-key bits read
+    // for them are never read again, so each round overwrites its own words.
+    if (!pick) {                                    // uniform: only this keeps key-0 blocks out
+        pfx = 0xFFFFFFFFu;
+        pmask = 0u;
+    }
+    uint32_t last_taken = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int j = tid + kOneThreads * i;
+        const uint32_t kp = key[i] & pmask;
+        bool take = kp > pfx || (kp == pfx && !tie);
+        if (tie) {                                  // uniform
+            const uint32_t wd = (uint32_t)j >> 5;
+            const uint32_t rank = dh[wd] + __popc(bm[wd] & ((1u << (j & 31)) - 1u));
+            take = take || (kp == pfx && rank < m);
+        }
+        take = j < n && (take || j < first_el || j >= end_el);
+        last_taken = j == n - 1 ? (uint32_t)take : last_taken;
+        const uint64_t bal = __ballot(take);
+        if (lane == 0)
+            *reinterpret_cast<uint64_t *>(&bm[(kOneThreads * i + 64 * wave) >> 5]) = bal;
+    }
+    __syncthreads();
+
+    // ---- ordered compaction: thread t owns words [WPT t, WPT t + WPT) -------
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int w = 0; w < WPT; w++)
+        cnt += owns_words ? __popc(bm[WPT * tid + w]) : 0u;
+    uint32_t total;
+    uint32_t pos = block_inclusive_scan<kOneThreads>(cnt, sh_scan, &total) - cnt;
+#pragma unroll
+    for (int w = 0; w < WPT; w++) {
+        uint32_t mw = owns_words ? bm[WPT * tid + w] : 0u;
+        while (mw) {
+            const int bit = __ffs(mw) - 1;
+            mw &= mw - 1;
+            if (pos < (uint32_t)K)
+                sel_b[pos] = 32 * (WPT * tid + w) + bit;
+            pos++;
+        }
+    }
+    for (int p = (int)total + tid; p < K; p += kOneThreads)
+        sel_b[p] = -1;
+    if (tid == (n - 1) % kOneThreads) {
+        const int nsel = (int)min(total, (uint32_t)K);
+        n_sel[b] = nsel;
+        if (n_tok) {
+            int nt = nsel * kBT;
+            const int last_len = L - (n - 1) * kBT;
+            if (last_len < kBT && last_taken)
+                nt -= kBT - last_len;               // the partial last block is selected
+            n_tok[b] = nt;
+        }
+    }
+}
+
 } // namespace
 
 template <int N>
@@ -461,6 +705,17 @@ static hipError_t launch_select_n(const SelectLayersT<N> &L, int n_layers, int64
 {
     const int n_blk_max = (max_ctx + kBT - 1) / kBT;
     const int n_slices = n_blk_max > 0 ? (n_blk_max + kSliceBlocks - 1) / kSliceBlocks : 1;
+    if (n_blk_max > budget_blocks && n_blk_max <= kOneThreads * kOneMaxPer) {
+        // the whole selection in one kernel, one workgroup per (sequence, layer)
+        dim3 grid((unsigned)batch, (unsigned)n_layers);
+        if (n_blk_max <= kOneThreads * 2)
+            hipLaunchKernelGGL((select_one_kernel<N, 2>), grid, dim3(kOneThreads), 0, s, L, bs_stride, ctx_len,
+                               max_ctx, budget_blocks, sink_blocks, tail_tokens);
+        else
+            hipLaunchKernelGGL((select_one_kernel<N, kOneMaxPer>), grid, dim3(kOneThreads), 0, s, L, bs_stride,
+                               ctx_len, max_ctx, budget_blocks, sink_blocks, tail_tokens);
+        return hipGetLastError();
+    }
     if (n_blk_max > budget_blocks) {
         dim3 grid((unsigned)n_slices, (unsigned)batch, (unsigned)n_layers);
         hipLaunchKernelGGL((collect_kernel<N>), grid, dim3(kCollectThreads), 0, s, L, bs_stride, ctx_len, max_ctx,

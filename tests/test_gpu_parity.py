@@ -214,10 +214,16 @@ def _check_topk_exact(bs_rows, lens, budget, sink=0, tail=0):
         assert nt[b] == len(toks)
 
 
-def test_topk_exact_random_and_ties(gpu):
-    rng = np.random.default_rng(5)
+# Longest context of the case picks the route: the one-kernel selection with 2
+# or 16 scores per thread (up to 8,192 and 65,536 tokens), and the collect +
+# finish kernels past that (one and several selection slices per workgroup
+# of the scan).
+@pytest.mark.parametrize("max_len", [8000, 40000, 65536 + 1, 262144, 262144 + 4 * 2048 + 1])
+def test_topk_exact_random_and_ties(gpu, max_len):
+    rng = np.random.default_rng(5 + max_len)
     for trial in range(6):
-        lens = rng.integers(1, 40000, size=5)
+        lens = rng.integers(1, max_len, size=5)
+        lens[4] = max_len
         lens[0] = 4 * 512 + 3          # just over the budget, ragged
         lens[1] = 2048                 # exactly the budget: everything fits
         n_max = (lens.max() + 3) // 4
@@ -229,10 +235,11 @@ def test_topk_exact_random_and_ties(gpu):
         _check_topk_exact(bs, lens, 2048, sink=trial % 3, tail=64 if trial >= 3 else 0)
 
 
-def test_topk_exact_degenerate_constant_scores(gpu):
+@pytest.mark.parametrize("max_len", [6000, 60000, 262144, 280000])
+def test_topk_exact_degenerate_constant_scores(gpu, max_len):
     """All scores equal: every block lands in one histogram bin, the candidate
     list is the whole sequence (radix path), and ties break by index."""
-    lens = [280000, 9000, 4 * 512 + 1]
+    lens = [max_len, 9000, 4 * 512 + 1]
     n_max = (max(lens) + 3) // 4
     bs = np.full((3, n_max), 3.5, np.float32)
     _check_topk_exact(bs, lens, 2048, sink=1)
