@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of libqsa: host-side validation, workspace carving and
 // the per-layer launch sequence of the decode step.
 #include <math.h>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -15,7 +16,7 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int n_split_of(int budget_tokens) { return (budget_tokens + kTPS - 1) / kTPS; }
+int n_split_of(int budget_tokens) { return (budget_tokens + kTPSMin - 1) / kTPSMin; }
 
 // Byte offsets of the workspace pieces. The histograms of every layer come
 // first, contiguous, so one fill kernel clears them all.
@@ -103,12 +104,34 @@ SelectWs select_ws(void *ws, const WsLayout &w, int l)
     return s;
 }
 
+// CUs of the current device (read once per device).
+int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The attention's split size for a call over w.B sequences and w.n_layers
+// layers: kTPS tokens when the call's splits give every CU two workgroups,
+// else kTPSMin. It depends on the call, not on how a schedule groups its
+// launches, so that every schedule gives the same bits.
 AttnWs attn_ws(void *ws, const WsLayout &w, int l)
 {
     AttnWs a;
     a.part_o = at<float>(ws, w.po + w.per_po * l);
     a.part_lse = at<float>(ws, w.plse + w.per_plse * l);
-    a.n_split = w.n_split;
+    const int64_t big_splits = (int64_t)((w.budget + kTPS - 1) / kTPS) * w.B * w.n_layers;
+    a.tps = big_splits >= 2 * (int64_t)device_cus() ? kTPS : kTPSMin;
+    a.n_split = (w.budget + a.tps - 1) / a.tps;
     return a;
 }
 
@@ -640,7 +663,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                          cfg->tail_tokens, cs);
             if (e == hipSuccess)
                 e = launch_attention_layers(true, AL, nl, batch->pt_stride, batch->max_ctx, B, K,
-                                            cfg->budget_tokens, cfg->sm_scale, lw[l0].aw.n_split, cs);
+                                            cfg->budget_tokens, cfg->sm_scale, lw[l0].aw.tps, cs);
         }
         // The caller synchronises on the compute stream: join the side stream.
         if (e == hipSuccess && n_used) {
@@ -742,7 +765,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                      cfg->budget_tokens, sc);
         if (e == hipSuccess)
             e = launch_attention_layers(false, AL, nl, 0, 0, B, 0, cfg->budget_tokens, cfg->sm_scale,
-                                        lw[l0].aw.n_split, sc);
+                                        lw[l0].aw.tps, sc);
     }
     return hip_status(e);
 }

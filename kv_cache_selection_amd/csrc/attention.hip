@@ -4,22 +4,29 @@
 // For query head h with KV head g = h / 8 and the selected tokens T:
 //     z_t = sm_scale * (q_h . K_{g,t}),   out_h = sum_t softmax(z)_t V_{g,t}
 // (the attention the article's "fast path" computes, restricted to the
-// gathered set). The tokens are split into chunks of kTPS = 128; a workgroup
-// (split s, KV head g, sequence b, layer of the launch) attends the 8 query
-// heads of g over its chunk, one wave per 32 tokens, and writes the
-// normalised partial output and its log-sum-exp; the merge kernel combines
-// the splits exactly: out = sum_s e^{lse_s - LSE} O_s.
+// gathered set). The tokens are split into chunks of 64 or 128 (kTPSMin or
+// kTPS, whichever gives the launch enough workgroups); a workgroup (split s,
+// sequence b, layer of the launch) attends all 16 query heads over its chunk,
+// each wave over 16 or 32 tokens, and writes the normalised partial outputs
+// and their log-sum-exp; the merge kernel combines the splits exactly:
+// out = sum_s e^{lse_s - LSE} O_s. One workgroup reads each token's whole
+// 2 KB row (K and V of both KV heads).
 //
-// Per wave (two tiles of 16 tokens):
-//  - all K and V rows of both tiles are requested before the first multiply;
-//  - QK^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = the 8 query
-//    heads (rows 8..15 zero) and B = 32 dims x 16 tokens read straight from
-//    the KV rows (each lane loads 16 contiguous bytes of one token's K);
-//  - one softmax over the wave's 32 tokens in fp32, the statistics reduced
-//    across the 16 lanes that hold one head's scores with DPP row operations;
-//  - PV on the matrix cores as well: the V rows go through LDS, where
-//    ds_read_b64_tr_b16 reads them transposed (k = tokens), and P enters as
-//    an exact bf16 high part plus a bf16 remainder (16 mantissa bits).
+// Per wave, for each chunk of 16 tokens:
+//  - all K and V rows of the chunk are requested before the first multiply;
+//  - QK^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = the 16 query
+//    heads (rows 0..7 the heads of KV head 0, rows 8..15 those of KV head 1)
+//    and B = 32 dims x 16 tokens of K_g read straight from the rows (each
+//    lane loads 16 contiguous bytes of one token's K), one chain per KV head;
+//    of each chain's output the rows of its own heads are kept;
+//  - the softmax in fp32, the statistics reduced across the 16 lanes that
+//    hold one head's scores with DPP row operations, and rescaled online
+//    between the chunks;
+//  - PV on the matrix cores as well (v_mfma_f32_16x16x16_bf16 per KV head):
+//    the V rows go through LDS, where ds_read_b64_tr_b16 reads them
+//    transposed (k = tokens), and P enters as an exact bf16 high part plus a
+//    bf16 remainder (16 mantissa bits), with the other KV head's rows zero,
+//    so both heads accumulate into the same 16-row output tiles.
 // The four waves of a workgroup then merge their partial states in LDS.
 //
 // Rows come either from the staging area (qsa_sparse_decode, the pinned-host
@@ -39,16 +46,16 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 16;                          // tokens per MFMA tile
-constexpr int kTiles = 2;                          // tiles per wave
-constexpr int kWaveTok = kTile * kTiles;           // 32
-static_assert(kWaves * kWaveTok == kTPS, "tokens per split");
+constexpr int kTile = 16;                          // tokens per MFMA tile (one chunk of a wave)
+static_assert(kWaves * kTile * 2 == kTPS && kWaves * kTile == kTPSMin, "tokens per split: 1 or 2 chunks a wave");
 constexpr int kKBytes = kDh * 2;                   // 512 bytes of K (or V) per head per row
-// A wave's V tile in LDS: 16 token rows of 512 bytes, 32 bytes of padding
-// between rows so that the transposing reads of 16 rows hit distinct banks.
-constexpr int kVPitch = kKBytes + 32;
-constexpr int kVTileBytes = kWaveTok * kVPitch;    // a wave's 32 rows: 17408
-constexpr int kOBytes = kWaves * kGroup * kDh * 4; // per-wave partial outputs for the merge (32 KB)
+constexpr int kVBytes = kHkv * kKBytes;            // a token's V: both heads, 1 KB
+// A wave's V tile in LDS: 16 token rows of 1 KB (V of head 0, then head 1),
+// 32 bytes of padding between rows so that the transposing reads of 4 rows
+// hit distinct banks.
+constexpr int kVPitch = kVBytes + 32;
+constexpr int kVTileBytes = kTile * kVPitch;       // 16,896
+constexpr int kOBytes = kWaves * kHq * kDh * 4;    // per-wave partial outputs for the merge (64 KB)
 constexpr int kSmemBytes = kWaves * kVTileBytes > kOBytes ? kWaves * kVTileBytes : kOBytes;
 
 // Max / sum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15): swaps
@@ -71,14 +78,29 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Grid (n_split, kHkv * layers, B): workgroup (split s, KV head g of layer ly,
-// sequence b) with blockIdx.y = g + kHkv * ly.
-template <bool kPaged, int N>
+// The exact split of p into a bf16 high part and a bf16 remainder, as the
+// halves of two packed pairs (elements e, e+1 of each).
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi, uint32_t &lo)
+{
+    const uint32_t h0 = __float_as_uint(p0) & 0xFFFF0000u;
+    const uint32_t h1 = __float_as_uint(p1) & 0xFFFF0000u;
+    const uint32_t l0 = __float_as_uint(p0 - __uint_as_float(h0)) >> 16;
+    const uint32_t l1 = __float_as_uint(p1 - __uint_as_float(h1)) & 0xFFFF0000u;
+    hi = (h0 >> 16) | h1;
+    lo = l0 | l1;
+}
+
+// Grid (n_split, layers, B): workgroup (split s, layer ly, sequence b)
+// attends all 16 query heads over the split's 64 kChunks tokens, so that each
+// token's whole 2 KB row is read by one wave (whole rows stream about 13 %
+// faster than the four 512-byte pieces of two workgroups). Each wave takes
+// kChunks chunks of 16 tokens, one after the other.
+template <bool kPaged, int N, int kChunks>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx,
                                                               int budget_blocks, int budget_tokens, float sm_scale,
                                                               int n_split)
 {
-    const int ly = blockIdx.y / kHkv;
+    const int ly = blockIdx.y;
     const uint16_t *__restrict__ q = Ls.q[ly];
     const uint8_t *__restrict__ rows = Ls.rows[ly];
     const int32_t *__restrict__ pt = Ls.pt[ly];
@@ -87,50 +109,49 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
     const int32_t *__restrict__ n_tok = Ls.n_tok[ly];
     float *__restrict__ part_o = Ls.part_o[ly];
     float *__restrict__ part_lse = Ls.part_lse[ly];
-    __shared__ __attribute__((aligned(16))) float ps[kWaves][kGroup][kWaveTok];  // the wave's probabilities
-    __shared__ float sstat[kWaves][kGroup][2];      // per-wave (max, sum) for the workgroup merge
-    __shared__ float swt[kWaves][kGroup];           // per-wave weights exp(m_w - M) of each head
-    __shared__ float sden[kGroup];                  // each head's normaliser
+    __shared__ __attribute__((aligned(16))) float ps[kWaves][kHq][kTile];  // the chunk's probabilities
+    __shared__ float sstat[kWaves][kHq][2];         // per-wave (max, sum) for the workgroup merge
+    __shared__ float swt[kWaves][kHq];              // per-wave weights exp(m_w - M) of each head
+    __shared__ float sden[kHq];                     // each head's normaliser
     // V tiles during the token loop, then the per-wave partial outputs
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
 
     const int s = blockIdx.x;
-    const int g = blockIdx.y % kHkv;
     const int b = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4;
+    const int col = lane & 15;
 
-    const int split_p0 = s * kTPS;
+    constexpr int kWaveTok = kTile * kChunks;
+    const int split_p0 = s * kWaves * kWaveTok;
     const int wave_p0 = split_p0 + wave * kWaveTok;
-    const int arow = lane & 15;
-    const int kofs = 8 * (lane >> 4);
 
     // Everything that does not depend on the token count is requested at
     // once: the count, the query, and each lane's row for its K token (lane
-    // l holds token l & 15 of each tile). On the paged path the row is the
+    // l holds token l & 15 of each chunk). On the paged path the row is the
     // page-table slot of the selected token; indices are clamped so that
     // every read stays inside its buffer before the count is known.
     // The loads are unconditional (selects come after them), so that the
-    // compiler can count them: the selection entries of both tiles and the
-    // query go out together, then the page-table slots of both tiles.
+    // compiler can count them: the selection entries of both chunks and the
+    // query go out together, then the page-table slots of both chunks.
     int nt = n_tok[b];
-    int64_t row_k[kTiles];
-    int ptok[kTiles], stok[kTiles];
+    int64_t row_k[kChunks];
+    int ptok[kChunks], stok[kChunks];
 #pragma unroll
-    for (int i = 0; i < kTiles; i++) {
-        const int p = min(wave_p0 + kTile * i + arow, budget_tokens - 1);
-        ptok[i] = p;
+    for (int c = 0; c < kChunks; c++) {
+        const int p = min(wave_p0 + kTile * c + col, budget_tokens - 1);
+        ptok[c] = p;
         if (kPaged)
-            stok[i] = sel[(int64_t)b * budget_blocks + (p >> 2)];
+            stok[c] = sel[(int64_t)b * budget_blocks + (p >> 2)];
     }
-    // A operand: lane holds row (lane & 15) = query head of group g, dims
-    // 32kk + 8 (lane >> 4) .. +8 for MFMA kk. Rows 8..15 repeat rows 0..7;
-    // their outputs land in lanes 32..63, which carry no head and are never
-    // used.
+    // A operand of QK^T: lane holds query head (lane & 15), dims
+    // 32 kk + 8 (lane >> 4) .. +8 for MFMA kk. Rows 0..7 are the heads of KV
+    // head 0, rows 8..15 those of KV head 1.
     bf16x8 qa[kDh / 32];
     {
-        const uint16_t *qr = q + ((int64_t)b * kHq + g * kGroup + (arow & 7)) * kDh + kofs;
+        const uint16_t *qr = q + ((int64_t)b * kHq + col) * kDh + 8 * grp;
 #pragma unroll
         for (int kk = 0; kk < kDh / 32; kk++)
             qa[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 32 * kk));
@@ -139,41 +160,47 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
         // token t of the selection; a block index outside the context (only
         // in entries past the count) reads slot 0. With no context the table
         // may be empty, so a selection entry is read instead.
-        int32_t slot[kTiles];
-        bool in[kTiles];
+        int32_t slot[kChunks];
+        bool in[kChunks];
 #pragma unroll
-        for (int i = 0; i < kTiles; i++) {
-            const int t = stok[i] * kBT + (ptok[i] & 3);
-            in[i] = t >= 0 && max_ctx > 0;
+        for (int c = 0; c < kChunks; c++) {
+            const int t = stok[c] * kBT + (ptok[c] & 3);
+            in[c] = t >= 0 && max_ctx > 0;
             const int tc = min(max(t, 0), max_ctx - 1);
             const int32_t *src = max_ctx > 0 ? pt + (int64_t)b * pt_stride + tc : sel + (int64_t)b * budget_blocks;
-            slot[i] = *src;
+            slot[c] = *src;
         }
-        // both slots are used here, so both reads are issued before either
+        // every slot is used here, so all the reads are issued before any
         // is waited for (not moved into the branches of the selects below)
-        static_assert(kTiles == 2, "two tiles per wave");
-        asm volatile("" : "+v"(slot[0]), "+v"(slot[1]));
 #pragma unroll
-        for (int i = 0; i < kTiles; i++)
-            row_k[i] = in[i] ? safe_slot(slot[i], n_slots) : 0;
+        for (int c = 0; c < kChunks; c++)
+            asm volatile("" : "+v"(slot[c]));
+#pragma unroll
+        for (int c = 0; c < kChunks; c++)
+            row_k[c] = in[c] ? safe_slot(slot[c], n_slots) : 0;
     } else {
 #pragma unroll
-        for (int i = 0; i < kTiles; i++)
-            row_k[i] = (int64_t)b * budget_tokens + ptok[i];
+        for (int c = 0; c < kChunks; c++)
+            row_k[c] = (int64_t)b * budget_tokens + ptok[c];
     }
 
     nt = nt < 0 ? 0 : (nt > budget_tokens ? budget_tokens : nt);
-    const int64_t part_base = ((int64_t)b * kHq + g * kGroup) * n_split + s;   // head g*8, split s
+    const int64_t part_base = (int64_t)b * kHq * n_split + s;   // head 0, split s
     if (split_p0 >= nt) {
-        if (tid < kGroup)
+        if (tid < kHq)
             part_lse[part_base + (int64_t)tid * n_split] = -INFINITY;
         return;
     }
 
-    // Softmax state of the wave: lane l holds heads 4 (l >> 4) + v (rows 8..15
-    // of the MFMA tiles are padding, so lanes 32..63 carry no head). The
-    // wave's 32 tokens are normalised together, so no running rescale.
+    // Softmax state of the wave: lane l holds heads 4 (l >> 4) + v, the rows
+    // of the C tiles it holds, for QK^T and PV alike; the state runs over
+    // the wave's two chunks (online rescale).
     float m_run[4], l_run[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        m_run[v] = -INFINITY;
+        l_run[v] = 0.0f;
+    }
     // Output accumulators, the C tiles of PV: o[m][v] = head 4 (l >> 4) + v,
     // dim 16 m + (l & 15).
     f32x4 o[kDh / 16];
@@ -181,148 +208,128 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
     for (int m = 0; m < kDh / 16; m++)
         o[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     uint8_t *vt = smem + wave * kVTileBytes;
-    const int grp = lane >> 4;
-    const int col = lane & 15;
 
-    if (wave_p0 >= nt) {                            // uniform: no valid token in this wave
+    if (wave_p0 < nt) {                             // uniform: the wave has valid tokens
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            m_run[v] = -INFINITY;
-            l_run[v] = 0.0f;
-        }
-    } else {
-        // Request every row the wave needs before the first multiply: the K
-        // rows of both tiles, then their V rows (the V rows of a tile's 16
-        // tokens are the K rows held by lanes 0..15). Every request is made,
-        // also for tokens past the count, whose row indices are clamped to
-        // valid rows and whose scores and V rows are masked below; so the
-        // compiler can count the requests, and QK^T and the softmax start as
-        // soon as the K rows are in, while the V rows still arrive.
-        u32x4 kd[kTiles][kDh / 32];
-        u32x2 vd[kTiles][kTile];
+        for (int c = 0; c < kChunks; c++) {
+            const int c_p0 = wave_p0 + kTile * c;
+            // The chunk's rows: K of both heads (lane: 16 B of each of 16
+            // pieces of its token's K), then V of both heads (one token's
+            // 1 KB per load, lane: 16 B). Every request is made, also for
+            // tokens past the count (rows clamped to valid ones, masked
+            // below), so the compiler can count them; QK^T waits for the K
+            // rows only.
+            u32x4 kd[kHkv][kDh / 32];
+            u32x4 vd[kTile];
+            const uint8_t *rk = rows + row_k[c] * kRowBytes + 16 * grp;
 #pragma unroll
-        for (int i = 0; i < kTiles; i++) {
-            const uint8_t *rk = rows + row_k[i] * kRowBytes + g * kKBytes + 2 * kofs;
+            for (int g = 0; g < kHkv; g++)
 #pragma unroll
-            for (int kk = 0; kk < kDh / 32; kk++)
-                kd[i][kk] = *reinterpret_cast<const u32x4 *>(rk + 64 * kk);
-        }
-#pragma unroll
-        for (int i = 0; i < kTiles; i++) {
-            const uint32_t rlo = (uint32_t)row_k[i], rhi = (uint32_t)(row_k[i] >> 32);
+                for (int kk = 0; kk < kDh / 32; kk++)
+                    kd[g][kk] = *reinterpret_cast<const u32x4 *>(rk + g * kKBytes + 64 * kk);
+            const uint32_t rlo = (uint32_t)row_k[c], rhi = (uint32_t)(row_k[c] >> 32);
 #pragma unroll
             for (int t = 0; t < kTile; t++) {
-                // uniform across the wave: token wave_p0 + 16 i + t, whose row lane t holds
+                // uniform across the wave: token c_p0 + t, whose row lane t holds
                 const int64_t r = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(rhi, t) << 32) |
                                             __builtin_amdgcn_readlane(rlo, t));
-                vd[i][t] = *reinterpret_cast<const u32x2 *>(rows + r * kRowBytes + (kHkv + g) * kKBytes + 8 * lane);
+                vd[t] = *reinterpret_cast<const u32x4 *>(rows + r * kRowBytes + kHkv * kKBytes + 16 * lane);
             }
-        }
-        f32x4 acc[kTiles];
+            // QK^T: acc[g] rows 8 g .. 8 g + 7 are the heads of KV head g.
+            f32x4 acc[kHkv];
 #pragma unroll
-        for (int i = 0; i < kTiles; i++) {
-            acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int g = 0; g < kHkv; g++) {
+                acc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kk = 0; kk < kDh / 32; kk++)
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8, kd[i][kk]),
-                                                                 acc[i], 0, 0, 0);
-        }
-        // acc[i][v] = q_{4 (lane>>4) + v} . K_{token 16 i + (lane & 15)}.
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            float z[kTiles], mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < kTiles; i++) {
-                z[i] = wave_p0 + kTile * i + col < nt ? acc[i][v] * sm_scale : -INFINITY;
-                mx = fmaxf(mx, z[i]);
+                for (int kk = 0; kk < kDh / 32; kk++)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8, kd[g][kk]),
+                                                                     acc[g], 0, 0, 0);
             }
-            mx = row16_reduce<true>(mx);
-            float sum = 0.0f;
+            // Lane l: heads 4 (l >> 4) + v (group l >> 5), token c_p0 + (l & 15).
+            const bool valid = c_p0 + col < nt;
 #pragma unroll
-            for (int i = 0; i < kTiles; i++) {
-                float e = (z[i] == -INFINITY) ? 0.0f : __expf(z[i] - mx);
+            for (int v = 0; v < 4; v++) {
+                const float z = valid ? (lane < 32 ? acc[0][v] : acc[1][v]) * sm_scale : -INFINITY;
+                const float mx = fmaxf(m_run[v], row16_reduce<true>(z));   // finite: token c_p0 is valid
+                const float r = __expf(m_run[v] - mx);                     // 0 on the first chunk
+                float e = valid ? __expf(z - mx) : 0.0f;
                 // Keep 16 mantissa bits (a bf16 head plus a bf16 remainder),
                 // the precision PV uses, so that numerator and normaliser agree.
                 const uint32_t hb = __float_as_uint(e) & 0xFFFF0000u;
                 const uint32_t lb = __float_as_uint(e - __uint_as_float(hb)) & 0xFFFF0000u;
                 e = __uint_as_float(hb) + __uint_as_float(lb);
-                sum += e;
-                if (lane < 32)
-                    ps[wave][4 * grp + v][kTile * i + col] = e;
-            }
-            l_run[v] = row16_reduce<false>(sum);
-            m_run[v] = mx;
-        }
-        // V rows of both tiles to LDS (row 16 i + t), zero past the count
+                l_run[v] = l_run[v] * r + row16_reduce<false>(e);
+                m_run[v] = mx;
 #pragma unroll
-        for (int i = 0; i < kTiles; i++)
+                for (int m = 0; m < kDh / 16; m++)
+                    o[m][v] *= r;
+                ps[wave][4 * grp + v][col] = e;
+            }
+            // V rows to LDS (row t), zero past the count
 #pragma unroll
             for (int t = 0; t < kTile; t++)
-                *reinterpret_cast<u32x2 *>(vt + (kTile * i + t) * kVPitch + 8 * lane) =
-                    wave_p0 + kTile * i + t < nt ? vd[i][t] : u32x2{0u, 0u};
-        wave_lds_sync();
+                *reinterpret_cast<u32x4 *>(vt + t * kVPitch + 16 * lane) =
+                    c_p0 + t < nt ? vd[t] : u32x4{0u, 0u, 0u, 0u};
+            wave_lds_sync();
 
-        // PV on the matrix cores, v_mfma_f32_16x16x32_bf16 per 16 dims:
-        //  A = P (row = head `col`, k = tokens 8 grp .. +7) as its exact split
-        //      into a bf16 high part and a bf16 remainder;
-        //  B = V (k = tokens 8 grp .. +7, column = dim), read transposed from
-        //      the rows in LDS, four tokens per read: in each group of 16
-        //      lanes, lane j supplies the address of token row base + (j >> 2),
-        //      dims 4 (j & 3) .. +3, and lane c receives dim c of the four rows.
-        bf16x8 a_hi, a_lo;
-        {
-            uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
-            if (col < kGroup) {
-                const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&ps[wave][col][8 * grp]);
-                const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&ps[wave][col][8 * grp + 4]);
-                const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            // PV on the matrix cores, v_mfma_f32_16x16x16_bf16 per 16 dims
+            // and KV head g:
+            //  A = P (row = head `col`, k = tokens 4 grp .. +3) as its exact
+            //      split into a bf16 high part and a bf16 remainder, with the
+            //      rows of the other KV head's query heads zero;
+            //  B = V_g (k = tokens 4 grp .. +3, column = dim), read transposed
+            //      from the rows in LDS: in each group of 16 lanes, lane j
+            //      supplies the address of token row 4 grp + (j >> 2), dims
+            //      4 (j & 3) .. +3, and lane c receives dim c of the four rows.
+            s16x4 a_hi[kHkv], a_lo[kHkv];
+            {
+                const f32x4 p = *reinterpret_cast<const f32x4 *>(&ps[wave][col][4 * grp]);
+                uint32_t hi[2], lo[2];
+                split_pair(p[0], p[1], hi[0], lo[0]);
+                split_pair(p[2], p[3], hi[1], lo[1]);
+                const s16x4 h = __builtin_bit_cast(s16x4, u32x2{hi[0], hi[1]});
+                const s16x4 l = __builtin_bit_cast(s16x4, u32x2{lo[0], lo[1]});
+                const s16x4 z = {0, 0, 0, 0};
+                a_hi[0] = col < kGroup ? h : z;
+                a_lo[0] = col < kGroup ? l : z;
+                a_hi[1] = col < kGroup ? z : h;
+                a_lo[1] = col < kGroup ? z : l;
+            }
+            const uint8_t *vrd = vt + (4 * grp + (col >> 2)) * kVPitch + 8 * (col & 3);
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t h0 = __float_as_uint(pv[e]) & 0xFFFF0000u;
-                    const uint32_t h1 = __float_as_uint(pv[e + 1]) & 0xFFFF0000u;
-                    const uint32_t l0 = __float_as_uint(pv[e] - __uint_as_float(h0)) >> 16;
-                    const uint32_t l1 = __float_as_uint(pv[e + 1] - __uint_as_float(h1)) & 0xFFFF0000u;
-                    hi[e >> 1] = (h0 >> 16) | h1;
-                    lo[e >> 1] = l0 | l1;
+            for (int m = 0; m < kDh / 16; m++) {
+#pragma unroll
+                for (int g = 0; g < kHkv; g++) {
+                    const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(vrd + g * kKBytes + 32 * m));
+                    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi[g], bv, o[m], 0, 0, 0);
+                    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo[g], bv, o[m], 0, 0, 0);
                 }
             }
-            a_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-            a_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
-        }
-        const uint8_t *vrd = vt + (8 * grp + (col >> 2)) * kVPitch + 8 * (col & 3);
-#pragma unroll
-        for (int m = 0; m < kDh / 16; m++) {
-            const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(vrd + 32 * m));
-            const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(vrd + 4 * kVPitch + 32 * m));
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bv, o[m], 0, 0, 0);
-            o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bv, o[m], 0, 0, 0);
+            // the next chunk's V overwrites this chunk's tile
+            wave_lds_sync();
         }
     }
 
     // Workgroup merge of the four waves' states (the V tiles' LDS is reused):
     // each wave's accumulators go to LDS as [dim][head], 16 bytes (4 heads of
-    // one dim) per store; 8 threads then work out each head's wave weights
+    // one dim) per store; 16 threads then work out each head's wave weights
     // f_w = exp(m_w - M), normaliser and LSE once, and every thread combines
-    // one dim for the 8 heads.
+    // one dim for the 16 heads.
     __syncthreads();
-    float(*sod)[kDh][kGroup] = reinterpret_cast<float(*)[kDh][kGroup]>(smem);
-    if (lane < 32) {
+    float(*sod)[kDh][kHq] = reinterpret_cast<float(*)[kDh][kHq]>(smem);
 #pragma unroll
-        for (int m = 0; m < kDh / 16; m++)
-            *reinterpret_cast<f32x4 *>(&sod[wave][16 * m + col][4 * grp]) = o[m];
-    }
-    if (lane < 32 && (lane & 15) == 0) {
+    for (int m = 0; m < kDh / 16; m++)
+        *reinterpret_cast<f32x4 *>(&sod[wave][16 * m + col][4 * grp]) = o[m];
+    if (col == 0) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            sstat[wave][4 * (lane >> 4) + v][0] = m_run[v];
-            sstat[wave][4 * (lane >> 4) + v][1] = l_run[v];
+            sstat[wave][4 * grp + v][0] = m_run[v];
+            sstat[wave][4 * grp + v][1] = l_run[v];
         }
     }
     __syncthreads();
-    if (tid < kGroup) {
+    if (tid < kHq) {
         const int h = tid;
         float M = -INFINITY;
 #pragma unroll
@@ -341,22 +348,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
     }
     __syncthreads();
     for (int d = tid; d < kDh; d += kThreads) {
-        float acc[kGroup];
+        float acc[kHq];
 #pragma unroll
-        for (int h = 0; h < kGroup; h++)
+        for (int h = 0; h < kHq; h++)
             acc[h] = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(&sod[w][d][0]);
-            const f32x4 c = *reinterpret_cast<const f32x4 *>(&sod[w][d][4]);
 #pragma unroll
-            for (int h = 0; h < 4; h++) {
-                acc[h] = fmaf(swt[w][h], a[h], acc[h]);
-                acc[4 + h] = fmaf(swt[w][4 + h], c[h], acc[4 + h]);
+            for (int h4 = 0; h4 < kHq; h4 += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sod[w][d][h4]);
+#pragma unroll
+                for (int h = 0; h < 4; h++)
+                    acc[h4 + h] = fmaf(swt[w][h4 + h], a[h], acc[h4 + h]);
             }
         }
 #pragma unroll
-        for (int h = 0; h < kGroup; h++)
+        for (int h = 0; h < kHq; h++)
             part_o[(part_base + (int64_t)h * n_split) * kDh + d] = acc[h] / sden[h];
     }
 }
@@ -414,14 +421,24 @@ __global__ __launch_bounds__(kDh) void merge_kernel(const AttnLayersT<N> Ls, int
 template <int N>
 static hipError_t launch_attention_n(bool paged, const AttnLayersT<N> &L, int n_layers, int64_t pt_stride,
                                      int max_ctx, int batch, int budget_blocks, int budget_tokens, float sm_scale,
-                                     int n_split, hipStream_t s)
+                                     int tps, hipStream_t s)
 {
-    dim3 grid((unsigned)n_split, (unsigned)(kHkv * n_layers), (unsigned)batch);
-    if (paged)
-        hipLaunchKernelGGL((attn_split_kernel<true, N>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
+    if (tps != kTPS && tps != kTPSMin)
+        return hipErrorInvalidValue;
+    const bool big = tps == kTPS;
+    const int n_split = (budget_tokens + tps - 1) / tps;
+    dim3 grid((unsigned)n_split, (unsigned)n_layers, (unsigned)batch);
+    if (paged && big)
+        hipLaunchKernelGGL((attn_split_kernel<true, N, 2>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
+                           budget_blocks, budget_tokens, sm_scale, n_split);
+    else if (paged)
+        hipLaunchKernelGGL((attn_split_kernel<true, N, 1>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
+                           budget_blocks, budget_tokens, sm_scale, n_split);
+    else if (big)
+        hipLaunchKernelGGL((attn_split_kernel<false, N, 2>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
                            budget_blocks, budget_tokens, sm_scale, n_split);
     else
-        hipLaunchKernelGGL((attn_split_kernel<false, N>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
+        hipLaunchKernelGGL((attn_split_kernel<false, N, 1>), grid, dim3(kThreads), 0, s, L, pt_stride, max_ctx,
                            budget_blocks, budget_tokens, sm_scale, n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -432,18 +449,18 @@ static hipError_t launch_attention_n(bool paged, const AttnLayersT<N> &L, int n_
 }
 
 hipError_t launch_attention_layers(bool paged, const AttnLayers &L, int n_layers, int64_t pt_stride, int max_ctx,
-                                   int batch, int budget_blocks, int budget_tokens, float sm_scale, int n_split,
+                                   int batch, int budget_blocks, int budget_tokens, float sm_scale, int tps,
                                    hipStream_t s)
 {
     if (n_layers < 1 || n_layers > kMaxChainLayers)
         return hipErrorInvalidValue;
     if (n_layers > 1)
         return launch_attention_n(paged, L, n_layers, pt_stride, max_ctx, batch, budget_blocks, budget_tokens,
-                                  sm_scale, n_split, s);
+                                  sm_scale, tps, s);
     const AttnLayersT<1> L1 = {{L.q[0]},     {L.rows[0]},   {L.pt[0]},       {L.n_slots[0]}, {L.sel[0]},
                                {L.n_tok[0]}, {L.part_o[0]}, {L.part_lse[0]}, {L.out[0]}};
     return launch_attention_n(paged, L1, 1, pt_stride, max_ctx, batch, budget_blocks, budget_tokens, sm_scale,
-                              n_split, s);
+                              tps, s);
 }
 
 hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int32_t *n_tok, int batch,
@@ -456,7 +473,7 @@ hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int3
     L.part_o[0] = ws.part_o;
     L.part_lse[0] = ws.part_lse;
     L.out[0] = out;
-    return launch_attention_layers(false, L, 1, 0, 0, batch, 0, budget_tokens, sm_scale, ws.n_split, s);
+    return launch_attention_layers(false, L, 1, 0, 0, batch, 0, budget_tokens, sm_scale, ws.tps, s);
 }
 
 hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int32_t *pt, int64_t pt_stride,
@@ -476,7 +493,7 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
     L.part_lse[0] = ws.part_lse;
     L.out[0] = out;
     return launch_attention_layers(true, L, 1, pt_stride, max_ctx, batch, budget_blocks, budget_tokens, sm_scale,
-                                   ws.n_split, s);
+                                   ws.tps, s);
 }
 
 } // namespace qsa

@@ -30,8 +30,12 @@ constexpr int kHistShift = 32 - kHistBits;
 // sequence's workgroups queue up on the same counter. Readers sum the copies.
 constexpr int kHistReps = 2;
 
-// Attention: tokens per split.
+// Attention: tokens per split. A launch with enough splits to give every CU
+// two workgroups uses splits of kTPS tokens; smaller launches use kTPSMin, so
+// that they still spread over the CUs. The workspace holds the partial
+// outputs of kTPSMin-token splits.
 constexpr int kTPS = 128;
+constexpr int kTPSMin = 64;
 
 // Monotone map of a float to uint32: a < b  <=>  key(a) < key(b); -0.0 maps
 // to the key of +0.0 so that the two compare equal, as floats do.
@@ -78,9 +82,10 @@ struct SelectWs {
 };
 
 struct AttnWs {
-    float *part_o;       // [B][kHq][n_split][kDh]
+    float *part_o;       // [B][kHq][n_split][kDh]; room for splits of kTPSMin tokens
     float *part_lse;     // [B][kHq][n_split]
-    int n_split;
+    int tps;             // tokens per split of this call: kTPS or kTPSMin
+    int n_split;         // splits per sequence: budget / tps, rounded up
 };
 
 // One launch of the selection or attention kernels may cover several layers
@@ -239,7 +244,7 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
 // Attention (split kernel + merge) of layers 0 .. n_layers - 1 of L, through
 // the page tables (paged) or over staged rows.
 hipError_t launch_attention_layers(bool paged, const AttnLayers &L, int n_layers, int64_t pt_stride, int max_ctx,
-                                   int batch, int budget_blocks, int budget_tokens, float sm_scale, int n_split,
+                                   int batch, int budget_blocks, int budget_tokens, float sm_scale, int tps,
                                    hipStream_t s);
 
 // Several queries per sequence (multiscore.hip); n_queries in {4, 8, 16, 32, 64}.
