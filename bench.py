@@ -252,10 +252,78 @@ def cpu_baseline(wl, hi, seconds):
             times.append((t1 - t0) + (t3 - t2))
             units.append((l, b))
     mean = sum(times) / len(times)
-    return {"value": 1.0 / (wl.batch * mean), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
-            "sample": "%d (layer, sequence) units of %s (layers %d-%d, %.1f s of oracle time), single-threaded "
-                      "C oracle in fp64: %.3f s per unit, and a layer-step is %d units; input generation excluded"
-                      % (len(units), wl.name, units[0][0], units[-1][0], sum(times), mean, wl.batch)}
+    single = {"value": 1.0 / (wl.batch * mean), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+              "sample": "%d (layer, sequence) units of %s (layers %d-%d, %.1f s of oracle time), single-threaded "
+                        "C oracle in fp64: %.3f s per unit, and a layer-step is %d units; input generation excluded"
+                        % (len(units), wl.name, units[0][0], units[-1][0], sum(times), mean, wl.batch)}
+
+    # All host cores (at most 16, one GPU's share of the box): one thread per
+    # core, each running the oracle on its own (layer, sequence) unit over and
+    # over for about seconds / 2. The C oracle and the generator release the
+    # GIL, so the threads run in parallel; inputs are generated before timing.
+    import threading
+    n_thr = max(1, min(16, len(os.sched_getaffinity(0))))
+    all_units = [(l, b) for l in range(wl.layers) for b in range(wl.batch)]
+    picked = [all_units[i % len(all_units)] for i in range(n_thr)]
+    inputs = []
+    for (l, b) in picked:
+        L = int(hi.lay.ctx[b])
+        keys, sig = SH.index_keys(wl.seed, l, b, 0, L, hi.lay.planted[(l, b)], hi.u[l, b])
+        inputs.append((l, b, L, keys, sig))
+    done = [0] * n_thr
+    t_start = [0.0]
+    ready = threading.Barrier(n_thr + 1)
+    go = threading.Barrier(n_thr + 1)
+
+    def work(i):
+        try:
+            run(i)
+        except BaseException:
+            ready.abort()                           # no thread waits forever on a failed one
+            go.abort()
+            raise
+
+    def run(i):
+        l, b, L, keys, sig = inputs[i]
+
+        def select():
+            ts = oracle.token_scores(keys, sig, hi.q_idx[l, b], hi.w[l, b])
+            bs = oracle.block_scores(ts, g.block_tokens)
+            sel = oracle.select_blocks(bs, K, oracle.forced_mask(L, g.block_tokens, wl.sink_blocks, wl.tail_tokens))
+            return oracle.tokens_of_blocks(L, sel.blocks, g.block_tokens)
+
+        # untimed: the unit's rows (its selection is the same every time)
+        rows = SH.kv_rows(wl.seed, l, hi.lay.pt[b, select()])
+        ready.wait()
+        go.wait()
+        while time.perf_counter() < t_start[0] + seconds / 2:
+            toks = select()
+            oracle.attention(np.arange(len(toks)), None, rows, hi.q[l, b], g.n_kv_heads, g.sm_scale)
+            done[i] += 1
+
+    thr = [threading.Thread(target=work, args=(i,)) for i in range(n_thr)]
+    for t in thr:
+        t.start()
+    try:
+        ready.wait()
+        t_start[0] = time.perf_counter()
+        go.wait()
+    except threading.BrokenBarrierError:
+        pass
+    for t in thr:
+        t.join()
+    if ready.broken or go.broken:
+        return single
+    wall = time.perf_counter() - t_start[0]
+    n_done = sum(done)
+    if n_done == 0:
+        return single
+    return {"value": n_done / wall / wl.batch, "unit": "layer-steps/s", "cores": n_thr, "kind": "oracle",
+            "sample": "%d threads (one per host core, at most 16), each running the C oracle (fp64) on its own "
+                      "(layer, sequence) unit of %s over and over: %d units in %.1f s of wall time, and a "
+                      "layer-step is %d units; input generation excluded" % (n_thr, wl.name, n_done, wall,
+                                                                            wl.batch),
+            "single_core": single}
 
 
 def bench_append(args):
