@@ -22,11 +22,12 @@
 //  - the softmax in fp32, the statistics reduced across the 16 lanes that
 //    hold one head's scores with DPP row operations, and rescaled online
 //    between the chunks;
-//  - PV on the matrix cores as well (v_mfma_f32_16x16x16_bf16 per KV head):
+//  - PV on the matrix cores as well (v_mfma_f32_16x16x32_bf16, the two KV
+//    heads stacked along k: 16 tokens under V_0, then the same 16 under V_1):
 //    the V rows go through LDS, where ds_read_b64_tr_b16 reads them
 //    transposed (k = tokens), and P enters as an exact bf16 high part plus a
-//    bf16 remainder (16 mantissa bits), with the other KV head's rows zero,
-//    so both heads accumulate into the same 16-row output tiles.
+//    bf16 remainder (16 mantissa bits), zero outside its own KV head's k
+//    range, so both heads accumulate into the same 16-row output tiles.
 // The four waves of a workgroup then merge their partial states in LDS.
 //
 // Rows come either from the staging area (qsa_sparse_decode, the pinned-host
@@ -95,8 +96,9 @@ __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi, uin
 // token's whole 2 KB row is read by one wave (whole rows stream about 13 %
 // faster than the four 512-byte pieces of two workgroups). Each wave takes
 // kChunks chunks of 16 tokens, one after the other.
+// Two waves per SIMD (two workgroups per CU): a register budget of 256.
 template <bool kPaged, int N, int kChunks>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx,
                                                               int budget_blocks, int budget_tokens, float sm_scale,
                                                               int n_split)
 {
@@ -272,39 +274,45 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const AttnLayersT<
                     c_p0 + t < nt ? vd[t] : u32x4{0u, 0u, 0u, 0u};
             wave_lds_sync();
 
-            // PV on the matrix cores, v_mfma_f32_16x16x16_bf16 per 16 dims
-            // and KV head g:
-            //  A = P (row = head `col`, k = tokens 4 grp .. +3) as its exact
-            //      split into a bf16 high part and a bf16 remainder, with the
-            //      rows of the other KV head's query heads zero;
-            //  B = V_g (k = tokens 4 grp .. +3, column = dim), read transposed
-            //      from the rows in LDS: in each group of 16 lanes, lane j
-            //      supplies the address of token row 4 grp + (j >> 2), dims
-            //      4 (j & 3) .. +3, and lane c receives dim c of the four rows.
-            s16x4 a_hi[kHkv], a_lo[kHkv];
+            // PV on the matrix cores, v_mfma_f32_16x16x32_bf16 per 16 dims,
+            // with both KV heads stacked along k: k = 0..15 are the chunk's
+            // tokens under V_0, k = 16..31 the same tokens under V_1.
+            //  A = P: lane l holds row (head) `col`, k = 8 (l >> 4) .. +7, i.e.
+            //      tokens 8 ((l >> 4) & 1) .. +7 of KV head g = l >> 5; zero
+            //      unless head `col` belongs to g (then the product picks
+            //      V_g for the heads of g only). P enters as its exact split
+            //      into a bf16 high part and a bf16 remainder.
+            //  B = V: lane l holds k = 8 (l >> 4) .. +7 and column (dim)
+            //      16 m + col, read transposed from the rows in LDS, four
+            //      tokens per read: in each group of 16 lanes, lane j supplies
+            //      the address of token row base + (j >> 2), dims 4 (j & 3)
+            //      .. +3 of V_g, and lane c receives dim c of the four rows.
+            const int g_k = lane >> 5;                  // the KV head of this lane's k range
+            const int tok0 = 8 * (grp & 1);             // its first token
+            bf16x8 a_hi, a_lo;
             {
-                const f32x4 p = *reinterpret_cast<const f32x4 *>(&ps[wave][col][4 * grp]);
-                uint32_t hi[2], lo[2];
-                split_pair(p[0], p[1], hi[0], lo[0]);
-                split_pair(p[2], p[3], hi[1], lo[1]);
-                const s16x4 h = __builtin_bit_cast(s16x4, u32x2{hi[0], hi[1]});
-                const s16x4 l = __builtin_bit_cast(s16x4, u32x2{lo[0], lo[1]});
-                const s16x4 z = {0, 0, 0, 0};
-                a_hi[0] = col < kGroup ? h : z;
-                a_lo[0] = col < kGroup ? l : z;
-                a_hi[1] = col < kGroup ? z : h;
-                a_lo[1] = col < kGroup ? z : l;
+                uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+                if ((col >> 3) == g_k) {
+                    const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&ps[wave][col][tok0]);
+                    const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&ps[wave][col][tok0 + 4]);
+                    split_pair(p0[0], p0[1], hi[0], lo[0]);
+                    split_pair(p0[2], p0[3], hi[1], lo[1]);
+                    split_pair(p1[0], p1[1], hi[2], lo[2]);
+                    split_pair(p1[2], p1[3], hi[3], lo[3]);
+                }
+                a_hi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+                a_lo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
             }
-            const uint8_t *vrd = vt + (4 * grp + (col >> 2)) * kVPitch + 8 * (col & 3);
+            const uint8_t *vrd = vt + (tok0 + (col >> 2)) * kVPitch + g_k * kKBytes + 8 * (col & 3);
 #pragma unroll
             for (int m = 0; m < kDh / 16; m++) {
-#pragma unroll
-                for (int g = 0; g < kHkv; g++) {
-                    const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(vrd + g * kKBytes + 32 * m));
-                    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi[g], bv, o[m], 0, 0, 0);
-                    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo[g], bv, o[m], 0, 0, 0);
-                }
+                const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(vrd + 32 * m));
+                const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(vrd + 4 * kVPitch + 32 * m));
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bv, o[m], 0, 0, 0);
+                o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bv, o[m], 0, 0, 0);
             }
             // the next chunk's V overwrites this chunk's tile
             wave_lds_sync();
