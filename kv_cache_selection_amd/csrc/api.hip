@@ -121,8 +121,8 @@ int device_cus()
 }
 
 // The attention's split size for a call over w.B sequences and w.n_layers
-// layers: kTPS tokens when the call's splits give every CU two workgroups,
-// else kTPSMin. It depends on the call, not on how a schedule groups its
+// layers: kTPS tokens when the call has at least half as many kTPS-token
+// splits as the device has CUs, else kTPSMin. It depends on the call, not on how a schedule groups its
 // launches, so that every schedule gives the same bits.
 AttnWs attn_ws(void *ws, const WsLayout &w, int l)
 {
@@ -130,7 +130,7 @@ AttnWs attn_ws(void *ws, const WsLayout &w, int l)
     a.part_o = at<float>(ws, w.po + w.per_po * l);
     a.part_lse = at<float>(ws, w.plse + w.per_plse * l);
     const int64_t big_splits = (int64_t)((w.budget + kTPS - 1) / kTPS) * w.B * w.n_layers;
-    a.tps = big_splits >= 2 * (int64_t)device_cus() ? kTPS : kTPSMin;
+    a.tps = 2 * big_splits >= (int64_t)device_cus() ? kTPS : kTPSMin;
     a.n_split = (w.budget + a.tps - 1) / a.tps;
     return a;
 }
