@@ -215,10 +215,9 @@ def _check_topk_exact(bs_rows, lens, budget, sink=0, tail=0):
 
 
 # Longest context of the case picks the route: the one-kernel selection with 2
-# or 16 scores per thread (up to 8,192 and 65,536 tokens), and the collect +
-# finish kernels past that (one and several selection slices per workgroup
-# of the scan).
-@pytest.mark.parametrize("max_len", [8000, 40000, 65536 + 1, 262144, 262144 + 4 * 2048 + 1])
+# or 16 scores per thread (up to 8,192 and 65,536 tokens, both ends of the
+# second), and the collect + finish kernels past that.
+@pytest.mark.parametrize("max_len", [8000, 40000, 65536, 65536 + 1, 262144, 262144 + 4 * 2048 + 1])
 def test_topk_exact_random_and_ties(gpu, max_len):
     rng = np.random.default_rng(5 + max_len)
     for trial in range(6):
