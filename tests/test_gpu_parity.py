@@ -367,6 +367,32 @@ def _check_step_units(di, sel, ns, out, units):
     return excused
 
 
+# The longest context picks the selection route: the one-kernel selection
+# (65,536 tokens) or collect + finish (70,001).
+@pytest.mark.parametrize("longest", [65536, 70001])
+def test_decode_step_edge_lengths(gpu, longest):
+    """A batch of edge lengths through the whole step: an empty sequence, one
+    and three tokens (a partial first block, forced as the sink), exactly the
+    budget (everything fits), just over it with partial last blocks (L mod 4
+    = 1 and 3), a mid length and the longest; with a sink block and a 64-token
+    tail ring. Every schedule and the pinned-host pool give the same bits, and
+    every (layer, sequence) matches the oracle; the empty sequence attends to
+    nothing and returns zeros."""
+    wl = S.Workload("edge-lengths", 8, (0, 1, 3, 2048, 2049, 2051, 9000, longest), 2, 2048, sink_blocks=1,
+                    tail_tokens=64, planted=8, seed=11)
+    di = DeviceInputs(wl, gpu)
+    sel, ns, out = _step(di, n_side=0)
+    for n_side in (1, 2):
+        sel2, ns2, out2 = _step(di, n_side=n_side)
+        assert np.array_equal(sel, sel2) and np.array_equal(ns, ns2) and np.array_equal(out, out2), n_side
+    dh = DeviceInputs(wl, gpu, kv_host=True, hi=di.hi)
+    sel3, ns3, out3 = _step(dh, n_side=1)
+    assert np.array_equal(sel, sel3) and np.array_equal(out, out3)
+    assert np.all(ns[:, 0] == 0) and np.all(out[:, 0] == 0.0)
+    assert np.all(ns[:, 3] == 512)                  # 2048 tokens: all 512 blocks fit
+    _check_step_units(di, sel, ns, out, [(l, b) for l in range(wl.layers) for b in range(wl.batch)])
+
+
 @pytest.mark.parametrize("name,layers", [("tiny-4k", 1), ("batch8-short", 3), ("single-38k", 2)])
 def test_decode_step_parity(gpu, name, layers):
     di = DeviceInputs(S.WORKLOADS[name], gpu, layers=layers)
