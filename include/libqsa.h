@@ -160,6 +160,11 @@ qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, co
  *   q   bf16 bits [B][n_q_heads][head_dim];  kv [B][budget_tokens][row_bytes]
  *   n_tok i32 [B] rows used per sequence (0 gives a zero output)
  *   out f32 [B][n_q_heads][head_dim]
+ * The tokens are split in 128-token pieces when the call has at least half
+ * as many of them as the device has CUs (budget/128 x B x layers >= CUs/2),
+ * else in 64-token pieces; the two splittings round differently (within the
+ * same tolerance), so results depend in their last bits on the call's batch
+ * and layer count and on the device.
  * Workspace: qsa_workspace_size(cfg, B, 0, 1, QSA_KV_DEVICE) bytes. */
 qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uint16_t *q, const void *kv,
                                const int32_t *n_tok, float *out, void *workspace, size_t workspace_bytes,
@@ -231,7 +236,9 @@ typedef struct {
  *     the layers' staging buffers, and attends them, all on `compute` (side
  *     streams are not used).
  * The call leaves `compute` ordered after all of its work, so a sync on
- * `compute` covers the step. Results are bit-identical for every schedule.
+ * `compute` covers the step. Results are bit-identical for every schedule
+ * of a call (the attention's split size is chosen once per call, as for
+ * qsa_sparse_decode with B x n_layers).
  * The overlapped schedules record events owned by the library (one set per
  * device): do not run them concurrently from several host threads on one
  * device. n_side is at most QSA_MAX_SIDE_STREAMS.
