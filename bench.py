@@ -168,6 +168,17 @@ def read_traffic(workload, grouped):
     return int(kv[key])
 
 
+def stream_ceiling(step_gbs, scan_gbs):
+    """A streaming-read ceiling measured on the same GPU: a plain read of a
+    buffer the size of the 12-layer index (1.66 GB), 256 KB per workgroup with
+    eight 16-byte loads in flight per lane. The step's and the scan's
+    algorithmic GB/s are given as fractions of it."""
+    from qsa_synth import fill
+    gbs = fill.stream_read_gbs()
+    return {"achieved": round(gbs, 1), "unit": "GB/s", "kind": "plain streaming read of 1.66 GB",
+            "step_frac": round(step_gbs / gbs, 4), "scan_frac": round(scan_gbs / gbs, 4)}
+
+
 def copy_calibration():
     import torch
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -762,6 +773,8 @@ def main():
                                    "rows_fetched_per_step": round(fetched, 1),
                                    "rows_selected_per_step": int(ntok.sum()),
                                    "hit_rate": round(1.0 - fetched / max(int(ntok.sum()), 1), 4)}
+    if not di.kv_host:
+        result["stream_ceiling"] = stream_ceiling(step_gbs, achieved)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, di.hi, args.cpu_seconds)
     print(json.dumps(result), flush=True)
