@@ -168,6 +168,24 @@ def read_traffic(workload, grouped):
     return int(kv[key])
 
 
+def h2d_copy_gbs(n_bytes=1 << 28, reps=10):
+    """The PCIe reference measured on the same box: a plain copy of a pinned
+    host buffer to the GPU (the DMA engines), GB/s over `reps` copies."""
+    import torch
+    src = torch.empty(n_bytes, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return n_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def stream_ceiling(step_gbs, scan_gbs):
     """A streaming-read ceiling measured on the same GPU: a plain read of a
     buffer the size of the 12-layer index (1.66 GB), 256 KB per workgroup with
@@ -766,8 +784,10 @@ def main():
         # every gathered row crosses PCIe once per step (with a hot cache: the misses only)
         pcie_bytes = int(ntok.sum()) * g.row_bytes if fetched is None else int(round(fetched)) * g.row_bytes
         pcie_gbs = pcie_bytes / (ms_step * 1e-3) / 1e9
+        h2d = h2d_copy_gbs()
         result["pcie"] = {"achieved": round(pcie_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "bytes_per_step": pcie_bytes}
+                          "frac": round(pcie_gbs / PCIE_PEAK_GBS, 4), "bytes_per_step": pcie_bytes,
+                          "h2d_copy": round(h2d, 2), "frac_of_h2d_copy": round(pcie_gbs / h2d, 4)}
         if fetched is not None:
             result["hot_cache"] = {"rows_per_layer": wl.hot_slots, "drift": wl.drift, "query_variants": NV,
                                    "rows_fetched_per_step": round(fetched, 1),
