@@ -122,8 +122,9 @@ int device_cus()
 
 // The attention's split size for a call over w.B sequences and w.n_layers
 // layers: kTPS tokens when the call has at least half as many kTPS-token
-// splits as the device has CUs, else kTPSMin. It depends on the call, not on how a schedule groups its
-// launches, so that every schedule gives the same bits.
+// splits as the device has CUs, else kTPSMin. It depends on the call, not on
+// how a schedule groups its launches, so that every schedule gives the same
+// bits.
 AttnWs attn_ws(void *ws, const WsLayout &w, int l)
 {
     AttnWs a;

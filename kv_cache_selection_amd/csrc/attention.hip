@@ -98,9 +98,9 @@ __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi, uin
 // kChunks chunks of 16 tokens, one after the other.
 // Two waves per SIMD (two workgroups per CU): a register budget of 256.
 template <bool kPaged, int N, int kChunks>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx,
-                                                              int budget_blocks, int budget_tokens, float sm_scale,
-                                                              int n_split)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx, int budget_blocks, int budget_tokens,
+                       float sm_scale, int n_split)
 {
     const int ly = blockIdx.y;
     const uint16_t *__restrict__ q = Ls.q[ly];
