@@ -700,6 +700,30 @@ def main():
         torch.cuda.synchronize()
         ms_serial = e0.elapsed_time(e1) / args.steps
 
+    # Timed region 2b: a step as a model with dependent layers runs it, one
+    # call per layer (n_layers = 1, one stream), each call with the
+    # workspace a one-layer call needs.
+    ms_per_layer_calls = None
+    if not hot:
+        nws1 = qsa.qsa_workspace_size(cfg, di.batch, di.max_ctx, 1, loc)
+        ws1 = torch.empty(nws1, dtype=torch.uint8, device=dev)
+
+        def step_per_layer():
+            lys = plain[n_done[0] % NV]
+            for ly in lys:
+                qsa.qsa_decode_step(cfg, bt, [ly], loc, ws1, nws1, stream, None)
+            n_done[0] += 1
+
+        step_per_layer()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step_per_layer()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_layer_calls = e0.elapsed_time(e1) / args.steps
+        del ws1
+
     # Timed region 3: the headline schedule again, with HIP events around
     # the scoring launches. With side streams and no hot cache one launch
     # scans all the layers (up to 16), and the first layer's events time it;
@@ -775,6 +799,9 @@ def main():
                              "frac": round(achieved1 / HBM_PEAK_GBS, 4), "bytes_per_launch": idx_bytes_layer,
                              "avg_launch_us": round(score1_ms * 1e3, 2),
                              "traffic": read_traffic(wl.name, False)},
+        "per_layer_calls": None if ms_per_layer_calls is None else {
+            "ms_per_step": round(ms_per_layer_calls, 4), "value": round(NL / (ms_per_layer_calls * 1e-3), 2),
+            "note": "one qsa_decode_step call per layer (n_layers = 1), one stream"},
         "one_stream": {"ms_per_step": round(ms_serial if ms_serial is not None else ms_step, 4),
                        "value": round(NL / ((ms_serial if ms_serial is not None else ms_step) * 1e-3), 2)},
         "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

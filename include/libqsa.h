@@ -160,9 +160,9 @@ qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, co
  *   q   bf16 bits [B][n_q_heads][head_dim];  kv [B][budget_tokens][row_bytes]
  *   n_tok i32 [B] rows used per sequence (0 gives a zero output)
  *   out f32 [B][n_q_heads][head_dim]
- * The tokens are split in 128-token pieces when the call has at least half
- * as many of them as the device has CUs (budget/128 x B x layers >= CUs/2),
- * else in 64-token pieces; the two splittings round differently (within the
+ * The tokens are split in 128-token pieces when the call has at least three
+ * quarters as many of them as the device has CUs (budget/128 x B x layers >=
+ * 3/4 CUs), else in 64-token pieces; the two splittings round differently (within the
  * same tolerance), so results depend in their last bits on the call's batch
  * and layer count and on the device.
  * Workspace: qsa_workspace_size(cfg, B, 0, 1, QSA_KV_DEVICE) bytes. */

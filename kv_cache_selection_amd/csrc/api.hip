@@ -121,17 +121,17 @@ int device_cus()
 }
 
 // The attention's split size for a call over w.B sequences and w.n_layers
-// layers: kTPS tokens when the call has at least half as many kTPS-token
-// splits as the device has CUs, else kTPSMin. It depends on the call, not on
-// how a schedule groups its launches, so that every schedule gives the same
-// bits.
+// layers: kTPS tokens when the call's kTPS-token splits number at least
+// three quarters of the device's CUs, else kTPSMin. It depends on the call,
+// not on how a schedule groups its launches, so that every schedule gives the
+// same bits.
 AttnWs attn_ws(void *ws, const WsLayout &w, int l)
 {
     AttnWs a;
     a.part_o = at<float>(ws, w.po + w.per_po * l);
     a.part_lse = at<float>(ws, w.plse + w.per_plse * l);
     const int64_t big_splits = (int64_t)((w.budget + kTPS - 1) / kTPS) * w.B * w.n_layers;
-    a.tps = 2 * big_splits >= (int64_t)device_cus() ? kTPS : kTPSMin;
+    a.tps = 4 * big_splits >= 3 * (int64_t)device_cus() ? kTPS : kTPSMin;
     a.n_split = (w.budget + a.tps - 1) / a.tps;
     return a;
 }

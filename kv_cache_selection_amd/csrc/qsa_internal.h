@@ -30,9 +30,9 @@ constexpr int kHistShift = 32 - kHistBits;
 // sequence's workgroups queue up on the same counter. Readers sum the copies.
 constexpr int kHistReps = 2;
 
-// Attention: tokens per split. A call with at least half as many kTPS-token
-// splits as the device has CUs uses splits of kTPS tokens; smaller calls use
-// kTPSMin, so that they still spread over the CUs. The workspace holds the partial
+// Attention: tokens per split. A call whose kTPS-token splits number at
+// least three quarters of the device's CUs uses splits of kTPS tokens;
+// smaller calls use kTPSMin, so that they still spread over the CUs. The workspace holds the partial
 // outputs of kTPSMin-token splits.
 constexpr int kTPS = 128;
 constexpr int kTPSMin = 64;
