@@ -643,6 +643,7 @@ def main():
     if args.side_streams is None:
         args.side_streams = 3 if di.kv_host else 1
     side = [torch.cuda.Stream() for _ in range(args.side_streams)]
+    events = qsa.StepEvents(NL, len(side)) if side else None
 
     # Workloads that run many decode steps cycle through step_variants query
     # sets (drifting indexer queries); the others repeat one step.
@@ -672,7 +673,8 @@ def main():
     n_done = [0]
 
     def step(lys, streams=True):
-        qsa.qsa_decode_step(cfg, bt, lys[n_done[0] % NV], loc, ws, nws, stream, side if streams else None)
+        qsa.qsa_decode_step(cfg, bt, lys[n_done[0] % NV], loc, ws, nws, stream, side if streams else None,
+                            events if streams else None)
         n_done[0] += 1
 
     for _ in range(args.warmup):

@@ -24,17 +24,22 @@
  *   - All pointers are device pointers unless stated otherwise; "host-pinned"
  *     pointers are host allocations made with hipHostMalloc (or torch
  *     pin_memory), read by the GPU directly over PCIe.
- *   - The caller owns every buffer, including the workspace. The library never
- *     allocates, frees or synchronises inside these calls; work is enqueued on
- *     the given stream(s) and runs asynchronously. NULL stream = the default
- *     stream. Calls are thread-safe when their workspaces differ.
+ *   - The caller owns every buffer, including the workspace, and every HIP
+ *     object the calls use (streams, and the event set of the overlapped
+ *     schedules, qsa_step_events_create). The library never allocates, frees,
+ *     creates HIP objects or synchronises inside the calls of the decode path;
+ *     work is enqueued on the given stream(s) and runs asynchronously. NULL
+ *     stream = the default stream. Calls are thread-safe when their
+ *     workspaces and event sets differ.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error nothing is enqueued. Values that live only on the device
  *     (ctx_len, idx_row0, page-table entries, selections) are the caller's
  *     contract. The kernels never read outside the buffers described here:
  *     ctx_len is clamped to [0, max_ctx]; a sequence whose index rows fall
  *     outside [0, n_idx_rows) is treated as empty; a page-table entry outside
- *     [0, n_slots) is read as slot 0 (the result is then unspecified).
+ *     [0, n_slots) is read as slot 0 (the result is then unspecified). Calls
+ *     that take a workspace report each of these events in a flags word kept
+ *     in the workspace (QSA_FLAG_*, read with qsa_read_flags).
  *   - Launch failures return QSA_ERR_HIP; faults surface at the next sync.
  *
  * Data layouts
@@ -42,6 +47,14 @@
  *     E4M3FN: bias 7, max 448, no infinities) and idx_scales u16 [rows] (IEEE
  *     fp16 bits, sigma_t >= 0), in logical token order; sequence b occupies
  *     rows [idx_row0[b], idx_row0[b] + ctx_len[b]). 66 bytes per token.
+ *     The pages give the index row's size only (66 bytes per token per
+ *     layer: 64 fp8 codes and one fp16 scale). This library takes the row as
+ *     two arrays, codes then scales, rather than one packed 66-byte record:
+ *     the same bytes, but every 64-lane load of codes is an aligned, fully
+ *     used 1 KB piece, where packed rows would leave 2-byte tails on every
+ *     row. The article's memory-ledger section says the index, its
+ *     quantisation scales and the page layout were re-aligned against each
+ *     other, which this split follows.
  *   - KV pool of one layer: [n_slots][row_bytes], row_bytes = 2 * n_kv_heads *
  *     head_dim * 2 = 2048; a row holds K of KV head 0..n_kv-1, then V of KV
  *     head 0..n_kv-1, each head_dim bf16 values.
@@ -112,9 +125,12 @@ typedef struct {
 } qsa_batch_t;
 
 /* Step 1 + 2 (indexer scoring and C4 reduce).
- *   idx_keys     u8  [rows][idx_dim], 16-byte aligned
- *   idx_scales   u16 [rows] fp16 bits
- *   q_idx        bf16 bits [B][idx_heads][idx_dim];  w_idx f32 [B][idx_heads]
+ *   idx_keys     u8  [rows][idx_dim], 16-byte aligned (the 64 codes of each
+ *                66-byte index row; the layout note above says why the row's
+ *                two parts come as two arrays)
+ *   idx_scales   u16 [rows] fp16 bits (the row's last 2 bytes)
+ *   q_idx        bf16 bits [B][idx_heads][idx_dim], 16-byte aligned;
+ *   w_idx        f32 [B][idx_heads]
  *   token_scores f32 [rows] (same row index as the keys) or NULL
  *   block_scores f32 [B][bs_stride], bs_stride >= ceil(max_ctx / block_tokens);
  *                entries past ceil(ctx_len[b] / block_tokens) are not written. */
@@ -138,8 +154,9 @@ qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, 
  * formula, causally -- query i sees tokens t <= q_pos[b][i] -- and gets C4
  * block scores: the max over the block's visible tokens, -inf for a block it
  * does not see. Dense [4 Q x 64] x [64 x L] contraction on the matrix cores.
- *   q_idx bf16 [B][Q][idx_heads][idx_dim], w_idx f32 [B][Q][idx_heads],
- *   q_pos int32 [B][Q]; block_scores f32 [B][Q][bs_stride], written for
+ *   q_idx bf16 [B][Q][idx_heads][idx_dim] and w_idx f32 [B][Q][idx_heads],
+ *   both 16-byte aligned; q_pos int32 [B][Q]; block_scores f32
+ *   [B][Q][bs_stride], written for
  *   blocks j < ceil(ctx_len[b] / 4). n_queries in {4, 8, 16, 32, 64}.
  * Each (b, i) row can go to qsa_topk_blocks as a sequence of its own with
  * length q_pos[b][i] + 1. */
@@ -157,7 +174,8 @@ qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, co
                            void *kv_out, int32_t *n_tok, qsa_stream_t stream);
 
 /* Step 5 (split-K GQA decode attention + log-sum-exp merge) over staged rows.
- *   q   bf16 bits [B][n_q_heads][head_dim];  kv [B][budget_tokens][row_bytes]
+ *   q   bf16 bits [B][n_q_heads][head_dim], 16-byte aligned;
+ *   kv  [B][budget_tokens][row_bytes], 16-byte aligned
  *   n_tok i32 [B] rows used per sequence (0 gives a zero output)
  *   out f32 [B][n_q_heads][head_dim]
  * The tokens are split in 128-token pieces when the call has at least three
@@ -194,12 +212,12 @@ typedef struct qsa_hot_cache {
 } qsa_hot_cache_t;
 
 typedef struct {
-    const uint8_t *idx_keys;    /* [rows][idx_dim] */
+    const uint8_t *idx_keys;    /* [rows][idx_dim], 16-byte aligned */
     const uint16_t *idx_scales; /* [rows] */
-    const uint16_t *q_idx;      /* [B][idx_heads][idx_dim] */
+    const uint16_t *q_idx;      /* [B][idx_heads][idx_dim], 16-byte aligned */
     const float *w_idx;         /* [B][idx_heads] */
-    const uint16_t *q;          /* [B][n_q_heads][head_dim] */
-    const void *kv_pool;        /* [n_slots][row_bytes], device or host-pinned */
+    const uint16_t *q;          /* [B][n_q_heads][head_dim], 16-byte aligned */
+    const void *kv_pool;        /* [n_slots][row_bytes], device or host-pinned, 16-byte aligned */
     const int32_t *page_table;  /* this layer's table, or NULL for batch->page_table */
     float *out;                 /* [B][n_q_heads][head_dim] */
     int32_t *sel_blocks;        /* optional [B][K] copy of the selection, or NULL */
@@ -239,15 +257,50 @@ typedef struct {
  * `compute` covers the step. Results are bit-identical for every schedule
  * of a call (the attention's split size is chosen once per call, as for
  * qsa_sparse_decode with B x n_layers).
- * The overlapped schedules record events owned by the library (one set per
- * device): do not run them concurrently from several host threads on one
- * device. n_side is at most QSA_MAX_SIDE_STREAMS.
- * Workspace: qsa_workspace_size(cfg, B, max_ctx, n_layers, kv_location). */
+ * Events: the schedules that order several streams (side streams with a hot
+ * cache, or with more than 16 layers on HBM pools) record and wait on the
+ * events of `events`, a set the caller created with qsa_step_events_create
+ * on the current device for at least n_layers layers and n_side side
+ * streams; the other schedules need none, and `events` may then be NULL.
+ * A set serves one call at a time: calls issued one after another on the
+ * same streams may share it, calls from different host threads may not.
+ * QSA_ERR_INVALID_ARGUMENT when the schedule needs events and `events` is
+ * NULL, too small or made on another device. n_side is at most
+ * QSA_MAX_SIDE_STREAMS, n_layers at most QSA_MAX_LAYERS.
+ * Workspace: qsa_workspace_size(cfg, B, max_ctx, n_layers, kv_location).
+ * The workspace's flags word (qsa_read_flags) is cleared at the start of
+ * the call and collects the QSA_FLAG_* events of its kernels. */
 #define QSA_MAX_SIDE_STREAMS 8
+#define QSA_MAX_LAYERS 64
+typedef struct qsa_step_events qsa_step_events_t;
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
                              size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
-                             int32_t n_side);
+                             int32_t n_side, qsa_step_events_t *events);
+
+/* The HIP events that order the streams of qsa_decode_step's overlapped
+ * schedules, created here (outside any hot path) on the current device, for
+ * calls of up to max_layers layers and max_side side streams. Not itself
+ * thread-safe: one set per host thread that issues overlapped steps.
+ * QSA_ERR_HIP if HIP cannot create the events (nothing is then kept). */
+qsa_status_t qsa_step_events_create(int32_t max_layers, int32_t max_side, qsa_step_events_t **events);
+void qsa_step_events_destroy(qsa_step_events_t *events);
+
+/* Flags a call's kernels raise when device-side values break the contract
+ * (each such value is clamped so every read stays in bounds, as described
+ * under the conventions above). Kept in a 32-bit word in the workspace. */
+#define QSA_FLAG_BAD_SLOT 1u       /* a selected token's page-table entry was outside [0, n_slots)
+                                      (its row was read from slot 0) */
+#define QSA_FLAG_BAD_INDEX_ROWS 2u /* a sequence's index rows fell outside [0, n_idx_rows)
+                                      (it was scored as empty) */
+#define QSA_FLAG_BAD_CTX_LEN 4u    /* a ctx_len[b] was outside [0, max_ctx] (it was clamped) */
+#define QSA_FLAG_BAD_N_TOK 8u      /* qsa_sparse_decode: an n_tok[b] was outside [0, budget_tokens] */
+
+/* Enqueues a copy of the flags word of `workspace` (a workspace passed to
+ * qsa_decode_step, qsa_topk_blocks or qsa_sparse_decode; the word covers the
+ * last call that used it, once that call has run) to flags_out (device, one
+ * uint32), on `stream`. */
+qsa_status_t qsa_read_flags(const void *workspace, uint32_t *flags_out, qsa_stream_t stream);
 
 /* Empties a hot cache: map[b][0..pt_stride) and owner[b][0..hot_slots) = -1
  * for every sequence of the batch. */

@@ -21,10 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE_TOO_SMALL, QSA_ERR_HIP, QSA_ERR_OUT_OF_SLOTS = range(6)
 QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1
+QSA_FLAG_BAD_SLOT, QSA_FLAG_BAD_INDEX_ROWS, QSA_FLAG_BAD_CTX_LEN, QSA_FLAG_BAD_N_TOK = 1, 2, 4, 8
+QSA_MAX_SIDE_STREAMS = 8
 
 # Every symbol include/libqsa.h declares.
 EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-           "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi",
+           "qsa_step_events_create", "qsa_step_events_destroy", "qsa_read_flags", "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi",
            "qsa_pool_create", "qsa_pool_destroy", "qsa_pool_open", "qsa_pool_next", "qsa_pool_close",
            "qsa_pool_free_slots", "qsa_pool_generations",
            "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
@@ -97,8 +99,13 @@ def _load():
     lib.qsa_pool_generations.argtypes = [P, P]
     lib.qsa_hot_reset.argtypes = [BP, ctypes.POINTER(HotCache), P]
     lib.qsa_decode_step.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P, sz, P,
-                                    ctypes.POINTER(ctypes.c_void_p), i32]
+                                    ctypes.POINTER(ctypes.c_void_p), i32, P]
+    lib.qsa_step_events_create.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.qsa_step_events_destroy.argtypes = [P]
+    lib.qsa_step_events_destroy.restype = None
+    lib.qsa_read_flags.argtypes = [P, P, P]
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
+              "qsa_step_events_create", "qsa_read_flags",
               "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi", "qsa_pool_create",
               "qsa_pool_open", "qsa_pool_next", "qsa_pool_close", "qsa_pool_generations"):
         getattr(lib, f).restype = i32
@@ -215,20 +222,59 @@ def qsa_hot_reset(batch, hot, stream=None):
     _check("qsa_hot_reset", lib.qsa_hot_reset(ctypes.byref(batch), ctypes.byref(hot), _stream(stream)))
 
 
-def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, side=None):
-    """`side`: None, one stream, or a sequence of streams (the side streams of
-    the overlapped schedules); None or an empty sequence serialises the step
-    on `compute`."""
-    # the array copies the structs; `layers` keeps the tensors they point to alive
-    arr = (Layer * len(layers))(*layers)
+class StepEvents:
+    """The caller-owned event set of the overlapped schedules
+    (qsa_step_events_create / _destroy), made on the current device."""
+
+    def __init__(self, max_layers: int, max_side: int):
+        h = ctypes.c_void_p()
+        _check("qsa_step_events_create", lib.qsa_step_events_create(int(max_layers), int(max_side), ctypes.byref(h)))
+        self._h = h
+        self.max_layers, self.max_side = int(max_layers), int(max_side)
+
+    @property
+    def handle(self):
+        return self._h.value
+
+    def destroy(self):
+        if self._h:
+            lib.qsa_step_events_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def _side_array(side):
     if side is None:
         side = ()
     elif not isinstance(side, (list, tuple)):
         side = (side,)
     sarr = (ctypes.c_void_p * max(len(side), 1))(*[_stream(x) for x in side])
+    return (sarr if side else None), len(side)
+
+
+def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes, compute=None, side=None,
+                    events=None):
+    """`side`: None, one stream, or a sequence of streams (the side streams of
+    the overlapped schedules); None or an empty sequence serialises the step
+    on `compute`. `events`: a StepEvents (needed by the schedules that order
+    several streams), or None."""
+    # the array copies the structs; `layers` keeps the tensors they point to alive
+    arr = (Layer * len(layers))(*layers)
+    sarr, n_side = _side_array(side)
     _check("qsa_decode_step", lib.qsa_decode_step(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
                                                   kv_location, _p(workspace), workspace_bytes, _stream(compute),
-                                                  sarr if side else None, len(side)))
+                                                  sarr, n_side, events.handle if events is not None else None))
+
+
+def qsa_read_flags(workspace, flags_out, stream=None):
+    """Enqueue a copy of the workspace's flags word (QSA_FLAG_*) into the
+    one-element int32/uint32 device tensor flags_out."""
+    _check("qsa_read_flags", lib.qsa_read_flags(_p(workspace), _p(flags_out), _stream(stream)))
 
 
 def make_append_layer(new_idx_key, new_kv_row, idx_keys, idx_scales, kv_pool) -> AppendLayer:

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <atomic>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "../../include/libqsa.h"
@@ -18,11 +19,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int n_split_of(int budget_tokens) { return (budget_tokens + kTPSMin - 1) / kTPSMin; }
 
-// Byte offsets of the workspace pieces. The histograms of every layer come
-// first, contiguous, so one fill kernel clears them all.
+// Byte offsets of the workspace pieces. The flags word and the histograms of
+// every layer come first, contiguous, so one fill kernel clears them all.
 struct WsLayout {
     int B = 0, K = 0, n_blk_max = 0, n_slices = 0, n_layers = 0, n_split = 0, budget = 0;
-    size_t hist = 0, zero_bytes = 0;
+    size_t flags = 0, hist = 0, zero_bytes = 0;
     size_t cnt = 0, sdef = 0, scand = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0,
            fetch = 0, nfetch = 0;
     size_t per_hist = 0, per_cnt = 0, per_sdef = 0, per_scand = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
@@ -57,6 +58,8 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.per_fetch = (loc == QSA_KV_HOST_PINNED) ? align_up((size_t)batch * w.budget * 8) : 0;
     w.per_nfetch = (loc == QSA_KV_HOST_PINNED) ? align_up((size_t)batch * 4) : 0;
     size_t off = 0;
+    w.flags = off;            // one uint32 (QSA_FLAG_*), in its own 256-byte piece
+    off += kAlign;
     w.hist = off;
     off += w.per_hist * n_layers;
     w.zero_bytes = off;
@@ -101,6 +104,9 @@ SelectWs select_ws(void *ws, const WsLayout &w, int l)
     s.slot_cand = at<uint64_t>(ws, w.scand + w.per_scand * l);
     s.spill = at<uint64_t>(ws, w.cand + w.per_cand * l);
     s.spill_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
+    s.flags = at<uint32_t>(ws, w.flags);
+    s.row0 = nullptr;
+    s.n_rows = 0;
     return s;
 }
 
@@ -133,6 +139,7 @@ AttnWs attn_ws(void *ws, const WsLayout &w, int l)
     const int64_t big_splits = (int64_t)((w.budget + kTPS - 1) / kTPS) * w.B * w.n_layers;
     a.tps = 4 * big_splits >= 3 * (int64_t)device_cus() ? kTPS : kTPSMin;
     a.n_split = (w.budget + a.tps - 1) / a.tps;
+    a.flags = at<uint32_t>(ws, w.flags);
     return a;
 }
 
@@ -191,43 +198,65 @@ const void *pool_device_ptr(const void *p, qsa_kv_location_t loc)
     return a.devicePointer;
 }
 
-// Events that order the streams of the overlapped schedules (fork, join,
-// per-layer scans), created once per device and kept for the life of the
-// process.
-struct EventPool {
-    std::mutex mu;
-    std::vector<std::vector<hipEvent_t>> per_dev;
-};
-
-EventPool &event_pool()
-{
-    static EventPool p;
-    return p;
-}
-
-qsa_status_t get_events(int n, std::vector<hipEvent_t> &out)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return QSA_ERR_HIP;
-    EventPool &p = event_pool();
-    std::lock_guard<std::mutex> g(p.mu);
-    if ((int)p.per_dev.size() <= dev)
-        p.per_dev.resize(dev + 1);
-    std::vector<hipEvent_t> &v = p.per_dev[dev];
-    while ((int)v.size() < n) {
-        hipEvent_t e;
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-            return QSA_ERR_HIP;
-        v.push_back(e);
-    }
-    out.assign(v.begin(), v.begin() + n);
-    return QSA_OK;
-}
+// The number of events a schedule of qsa_decode_step records: fork and join
+// events plus one per layer (the scans of the hot-cache schedule, the layer
+// groups of the HBM schedule).
+int events_needed(int n_layers, int n_side) { return 3 * n_layers + n_side + 1; }
 
 } // namespace
 
+// The caller's event set (qsa_step_events_create).
+struct qsa_step_events {
+    int device;
+    int max_layers, max_side;
+    std::vector<hipEvent_t> ev;
+};
+
 extern "C" {
+
+qsa_status_t qsa_step_events_create(int32_t max_layers, int32_t max_side, qsa_step_events_t **events)
+{
+    if (!events || max_layers < 1 || max_side < 0 || max_side > QSA_MAX_SIDE_STREAMS)
+        return QSA_ERR_INVALID_ARGUMENT;
+    *events = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return QSA_ERR_HIP;
+    qsa_step_events *e = new (std::nothrow) qsa_step_events;
+    if (!e)
+        return QSA_ERR_HIP;
+    e->device = dev;
+    e->max_layers = max_layers;
+    e->max_side = max_side;
+    const int n = events_needed(max_layers, max_side);
+    e->ev.reserve((size_t)n);
+    for (int i = 0; i < n; i++) {
+        hipEvent_t h;
+        if (hipEventCreateWithFlags(&h, hipEventDisableTiming) != hipSuccess) {
+            qsa_step_events_destroy(e);
+            return QSA_ERR_HIP;
+        }
+        e->ev.push_back(h);
+    }
+    *events = e;
+    return QSA_OK;
+}
+
+void qsa_step_events_destroy(qsa_step_events_t *events)
+{
+    if (!events)
+        return;
+    for (hipEvent_t h : events->ev)
+        (void)hipEventDestroy(h);
+    delete events;
+}
+
+qsa_status_t qsa_read_flags(const void *workspace, uint32_t *flags_out, qsa_stream_t stream)
+{
+    if (!workspace || !flags_out || !aligned(workspace, kAlign) || !aligned(flags_out, 4))
+        return QSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_copy_u32(static_cast<const uint32_t *>(workspace), flags_out, 1, (hipStream_t)stream));
+}
 
 size_t qsa_workspace_size(const qsa_config_t *cfg, int32_t batch, int32_t max_ctx, int32_t n_layers,
                           qsa_kv_location_t kv_location)
@@ -276,11 +305,12 @@ qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     if ((st = check_batch(batch, true, false)) != QSA_OK)
         return st;
     if (!idx_keys || !idx_scales || !q_idx || !w_idx || !block_scores || !aligned(idx_keys, 16) ||
-        !aligned(q_idx, 8) || bs_stride < (batch->max_ctx + kBT - 1) / kBT)
+        !aligned(idx_scales, 2) || !aligned(q_idx, 16) || !aligned(w_idx, 4) ||
+        bs_stride < (batch->max_ctx + kBT - 1) / kBT)
         return QSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_index_score(idx_keys, idx_scales, q_idx, w_idx, batch->ctx_len, batch->idx_row0,
                                          batch->n_idx_rows, batch->batch, batch->max_ctx, token_scores, block_scores, bs_stride,
-                                         nullptr, 0, 0, 0, (hipStream_t)stream));
+                                         nullptr, 0, 0, 0, nullptr, (hipStream_t)stream));
 }
 
 qsa_status_t qsa_index_score_multi(const qsa_config_t *cfg, const qsa_batch_t *batch, int32_t n_queries,
@@ -296,7 +326,8 @@ qsa_status_t qsa_index_score_multi(const qsa_config_t *cfg, const qsa_batch_t *b
     if (!(n_queries == 4 || n_queries == 8 || n_queries == 16 || n_queries == 32 || n_queries == 64))
         return QSA_ERR_UNSUPPORTED;
     if (!idx_keys || !idx_scales || !q_idx || !w_idx || !q_pos || !block_scores || !aligned(idx_keys, 16) ||
-        !aligned(q_idx, 16) || !aligned(w_idx, 4) || bs_stride < (batch->max_ctx + kBT - 1) / kBT)
+        !aligned(idx_scales, 2) || !aligned(q_idx, 16) || !aligned(w_idx, 16) || !aligned(q_pos, 4) ||
+        bs_stride < (batch->max_ctx + kBT - 1) / kBT)
         return QSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_multi_score(n_queries, idx_keys, idx_scales, q_idx, w_idx, q_pos, batch->ctx_len,
                                          batch->idx_row0, batch->n_idx_rows, batch->batch, batch->max_ctx,
@@ -347,7 +378,8 @@ qsa_status_t qsa_gather_kv(const qsa_config_t *cfg, const qsa_batch_t *batch, co
         return QSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_gather(sel_blocks, n_sel, batch->ctx_len, batch->batch, batch->max_ctx,
                                     batch->page_table, batch->pt_stride, batch->n_slots, pool, kv_out,
-                                    cfg->budget_tokens / kBT, cfg->budget_tokens, n_tok, (hipStream_t)stream));
+                                    cfg->budget_tokens / kBT, cfg->budget_tokens, n_tok, nullptr,
+                                    (hipStream_t)stream));
 }
 
 qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uint16_t *q, const void *kv,
@@ -357,14 +389,17 @@ qsa_status_t qsa_sparse_decode(const qsa_config_t *cfg, int32_t batch, const uin
     qsa_status_t st = check_config(cfg);
     if (st != QSA_OK)
         return st;
-    if (batch < 1 || !q || !kv || !n_tok || !out || !workspace || !aligned(kv, 16) ||
-        !aligned(workspace, kAlign))
+    if (batch < 1 || !q || !kv || !n_tok || !out || !workspace || !aligned(q, 16) || !aligned(kv, 16) ||
+        !aligned(n_tok, 4) || !aligned(out, 4) || !aligned(workspace, kAlign))
         return QSA_ERR_INVALID_ARGUMENT;
     const WsLayout w = make_layout(cfg, batch, 0, 1, QSA_KV_DEVICE);
     if (workspace_bytes < w.total)
         return QSA_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(launch_attention_staged(q, kv, n_tok, batch, cfg->budget_tokens, cfg->sm_scale,
-                                              attn_ws(workspace, w, 0), out, (hipStream_t)stream));
+    hipError_t e = launch_zero_u32(at<uint32_t>(workspace, w.flags), 1, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = launch_attention_staged(q, kv, n_tok, batch, cfg->budget_tokens, cfg->sm_scale, attn_ws(workspace, w, 0),
+                                    out, (hipStream_t)stream);
+    return hip_status(e);
 }
 
 qsa_status_t qsa_hot_reset(const qsa_batch_t *batch, const qsa_hot_cache_t *hot, qsa_stream_t stream)
@@ -447,21 +482,23 @@ qsa_status_t qsa_check_generations(const qsa_batch_t *batch, const int32_t *page
 qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
                              int32_t n_layers, qsa_kv_location_t kv_location, void *workspace,
                              size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
-                             int32_t n_side)
+                             int32_t n_side, qsa_step_events_t *events)
 {
     qsa_status_t st = check_config(cfg);
     if (st != QSA_OK)
         return st;
     if ((st = check_batch(batch, true, true)) != QSA_OK)
         return st;
-    if (!layers || n_layers < 1 || !workspace || !aligned(workspace, kAlign) ||
+    if (!layers || n_layers < 1 || n_layers > QSA_MAX_LAYERS || !workspace || !aligned(workspace, kAlign) ||
         (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
         return QSA_ERR_INVALID_ARGUMENT;
     int n_hot = 0;
     for (int l = 0; l < n_layers; l++) {
         const qsa_layer_t &L = layers[l];
         if (!L.idx_keys || !L.idx_scales || !L.q_idx || !L.w_idx || !L.q || !L.kv_pool || !L.out ||
-            !aligned(L.idx_keys, 16) || !aligned(L.q_idx, 8) || !aligned(L.kv_pool, 16))
+            !aligned(L.idx_keys, 16) || !aligned(L.idx_scales, 2) || !aligned(L.q_idx, 16) || !aligned(L.w_idx, 4) ||
+            !aligned(L.q, 16) || !aligned(L.kv_pool, 16) || !aligned(L.out, 4) ||
+            (L.page_table && !aligned(L.page_table, 4)))
             return QSA_ERR_INVALID_ARGUMENT;
         if (L.hot) {
             const qsa_hot_cache_t &H = *L.hot;
@@ -484,10 +521,29 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             if (side[k] == side[k2])
                 return QSA_ERR_INVALID_ARGUMENT;
     }
+    // The schedules that order several streams take their events from the
+    // caller's set: the hot-cache schedule, and HBM pools with more layers
+    // than one group. Side streams that a schedule does not use are ignored.
+    const bool offload = kv_location == QSA_KV_HOST_PINNED;
+    const bool two_streams = n_side > 0;
+    const int NS = (offload && !hot) ? 0 : n_side;
+    const bool needs_events = two_streams && (hot || (!offload && n_layers > kMaxChainLayers));
+    const hipEvent_t *ev = nullptr;
+    if (needs_events) {
+        if (!events || events->max_layers < n_layers || events->max_side < NS ||
+            (int)events->ev.size() < events_needed(n_layers, NS))
+            return QSA_ERR_INVALID_ARGUMENT;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return QSA_ERR_HIP;
+        if (events->device != dev)
+            return QSA_ERR_INVALID_ARGUMENT;
+        ev = events->ev.data();
+    }
     const WsLayout w = make_layout(cfg, batch->batch, batch->max_ctx, n_layers, kv_location);
     if (workspace_bytes < w.total)
         return QSA_ERR_WORKSPACE_TOO_SMALL;
-    std::vector<const void *> pools((size_t)n_layers);
+    const void *pools[QSA_MAX_LAYERS];
     for (int l = 0; l < n_layers; l++) {
         pools[l] = pool_device_ptr(layers[l].kv_pool, kv_location);
         if (!pools[l])
@@ -495,16 +551,6 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     }
 
     hipStream_t sc = (hipStream_t)compute;
-    const bool offload = kv_location == QSA_KV_HOST_PINNED;
-    const bool two_streams = n_side > 0;
-    // side streams the overlapped schedules use: none for pinned-host pools
-    // without a hot cache (one stream), side[0] for HBM pools with more layers
-    // than one group, all of them for hot-cached pools
-    const int NS = (offload && !hot) ? 0 : n_side;
-    std::vector<hipEvent_t> ev;
-    if (two_streams && NS > 0 && (st = get_events(3 * n_layers + NS + 1, ev)) != QSA_OK)
-        return st;
-
     const int B = batch->batch;
     const int K = w.K;
     const int64_t bs_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
@@ -520,7 +566,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         int2 *fetch;
         int32_t *nfetch;
     };
-    std::vector<Lw> lw((size_t)n_layers);
+    Lw lw[QSA_MAX_LAYERS];
     for (int l = 0; l < n_layers; l++) {
         const qsa_layer_t &Ly = layers[l];
         Lw &x = lw[l];
@@ -530,16 +576,19 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         x.nsel = Ly.n_sel ? Ly.n_sel : at<int32_t>(workspace, w.nsel + w.per_nsel * l);
         x.ntok = at<int32_t>(workspace, w.ntok + w.per_ntok * l);
         x.sw = select_ws(workspace, w, l);
+        x.sw.row0 = batch->idx_row0;
+        x.sw.n_rows = batch->n_idx_rows;
         x.aw = attn_ws(workspace, w, l);
         x.stage = offload ? at<void>(workspace, w.stage + w.per_stage * l) : nullptr;
         x.fetch = offload ? at<int2>(workspace, w.fetch + w.per_fetch * l) : nullptr;
         x.nfetch = offload ? at<int32_t>(workspace, w.nfetch + w.per_nfetch * l) : nullptr;
     }
+    uint32_t *const flags = at<uint32_t>(workspace, w.flags);
     auto score = [&](int l, hipStream_t s) {
         const qsa_layer_t &Ly = layers[l];
         return launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
                                   batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.hist, K,
-                                  cfg->sink_blocks, cfg->tail_tokens, s, (hipEvent_t)Ly.score_events[0],
+                                  cfg->sink_blocks, cfg->tail_tokens, flags, s, (hipEvent_t)Ly.score_events[0],
                                   (hipEvent_t)Ly.score_events[1]);
     };
     auto select = [&](int l, hipStream_t s) {
@@ -555,7 +604,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                          s);
         if (r == hipSuccess)
             r = launch_hot_fetch(lw[l].fetch, lw[l].nfetch, B, cfg->budget_tokens, lw[l].pt, batch->pt_stride,
-                                 batch->n_slots, batch->max_ctx, pools[l], H.rows, H.hot_slots, s);
+                                 batch->n_slots, batch->max_ctx, pools[l], H.rows, H.hot_slots, flags, s);
         if (r == hipSuccess)
             r = launch_attention_paged(layers[l].q, H.rows, H.map, batch->pt_stride, (int64_t)B * H.hot_slots,
                                        lw[l].sel, lw[l].ntok, batch->ctx_len, batch->max_ctx, B, K,
@@ -571,7 +620,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     };
     auto gather = [&](int l, hipStream_t s) {
         return launch_gather(lw[l].sel, lw[l].nsel, batch->ctx_len, B, batch->max_ctx, lw[l].pt, batch->pt_stride,
-                             batch->n_slots, pools[l], lw[l].stage, K, cfg->budget_tokens, lw[l].ntok, s);
+                             batch->n_slots, pools[l], lw[l].stage, K, cfg->budget_tokens, lw[l].ntok, flags, s);
     };
     auto attend_staged = [&](int l, hipStream_t s) {
         return launch_attention_staged(layers[l].q, lw[l].stage, lw[l].ntok, B, cfg->budget_tokens, cfg->sm_scale,
@@ -598,6 +647,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
 
     // The per-layer pointer tables of layers l0 .. l0 + nl - 1 (HBM pools).
     auto hbm_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, AttnLayers &AL) {
+        CL.flags = flags;
+        AL.flags = flags;
         for (int i = 0; i < nl; i++) {
             const int l = l0 + i;
             const qsa_layer_t &Ly = layers[l];
@@ -728,6 +779,9 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         SelectLayers SL = {};
         GatherLayers GL = {};
         AttnLayers AL = {};
+        CL.flags = flags;
+        GL.flags = flags;
+        AL.flags = flags;
         for (int i = 0; i < nl; i++) {
             const int l = l0 + i;
             const qsa_layer_t &Ly = layers[l];

@@ -178,14 +178,20 @@ void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx, 
         for (int c = 0; c < kChunks; c++)
             asm volatile("" : "+v"(slot[c]));
 #pragma unroll
-        for (int c = 0; c < kChunks; c++)
+        for (int c = 0; c < kChunks; c++) {
             row_k[c] = in[c] ? safe_slot(slot[c], n_slots) : 0;
+            // a selected token (p < n_tok) whose entry is outside the pool
+            if (in[c] && row_k[c] != slot[c] && ptok[c] < nt && grp == 0)
+                raise_flag(Ls.flags, QSA_FLAG_BAD_SLOT);
+        }
     } else {
 #pragma unroll
         for (int c = 0; c < kChunks; c++)
             row_k[c] = (int64_t)b * budget_tokens + ptok[c];
     }
 
+    if (!kPaged && s == 0 && tid == 0 && (nt < 0 || nt > budget_tokens))
+        raise_flag(Ls.flags, QSA_FLAG_BAD_N_TOK);
     nt = nt < 0 ? 0 : (nt > budget_tokens ? budget_tokens : nt);
     const int64_t part_base = (int64_t)b * kHq * n_split + s;   // head 0, split s
     if (split_p0 >= nt) {
@@ -466,7 +472,7 @@ hipError_t launch_attention_layers(bool paged, const AttnLayers &L, int n_layers
         return launch_attention_n(paged, L, n_layers, pt_stride, max_ctx, batch, budget_blocks, budget_tokens,
                                   sm_scale, tps, s);
     const AttnLayersT<1> L1 = {{L.q[0]},     {L.rows[0]},   {L.pt[0]},       {L.n_slots[0]}, {L.sel[0]},
-                               {L.n_tok[0]}, {L.part_o[0]}, {L.part_lse[0]}, {L.out[0]}};
+                               {L.n_tok[0]}, {L.part_o[0]}, {L.part_lse[0]}, {L.out[0]},     L.flags};
     return launch_attention_n(paged, L1, 1, pt_stride, max_ctx, batch, budget_blocks, budget_tokens, sm_scale,
                               tps, s);
 }
@@ -475,6 +481,7 @@ hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int3
                                    int budget_tokens, float sm_scale, const AttnWs &ws, float *out, hipStream_t s)
 {
     AttnLayers L = {};
+    L.flags = ws.flags;
     L.q[0] = q;
     L.rows[0] = static_cast<const uint8_t *>(kv);
     L.n_tok[0] = n_tok;
@@ -491,6 +498,7 @@ hipError_t launch_attention_paged(const uint16_t *q, const void *pool, const int
 {
     (void)ctx_len;
     AttnLayers L = {};
+    L.flags = ws.flags;
     L.q[0] = q;
     L.rows[0] = static_cast<const uint8_t *>(pool);
     L.pt[0] = pt;

@@ -66,7 +66,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherLayersT<N>
             const int j = sel[(int64_t)b * K + i];
             const int t = j * kBT + (r % kBT);
             if (j >= 0 && t < L) {
-                const int64_t slot = safe_slot(pt[(int64_t)b * pt_stride + t], n_slots);
+                const int32_t raw = pt[(int64_t)b * pt_stride + t];
+                const int64_t slot = safe_slot(raw, n_slots);
+                if (piece == 0 && slot != raw)
+                    raise_flag(Ls.flags, QSA_FLAG_BAD_SLOT);
                 v[k] = __builtin_nontemporal_load(pool + slot * kPieces + piece);
                 const int p = i * kBT + (r % kBT);
                 dst[k] = ((int64_t)b * budget_tokens + p) * kPieces + piece;
@@ -99,7 +102,8 @@ hipError_t launch_gather_layers(const GatherLayers &L, int n_layers, const int32
     if (n_layers > 1) {
         launch_gather_n(L, n_layers, ctx_len, batch, max_ctx, pt_stride, n_slots, budget_blocks, budget_tokens, s);
     } else {
-        const GatherLayersT<1> L1 = {{L.sel[0]}, {L.n_sel[0]}, {L.pt[0]}, {L.pool[0]}, {L.out[0]}, {L.n_tok[0]}};
+        const GatherLayersT<1> L1 = {{L.sel[0]}, {L.n_sel[0]}, {L.pt[0]}, {L.pool[0]},
+                                     {L.out[0]}, {L.n_tok[0]}, L.flags};
         launch_gather_n(L1, 1, ctx_len, batch, max_ctx, pt_stride, n_slots, budget_blocks, budget_tokens, s);
     }
     return hipGetLastError();
@@ -107,9 +111,10 @@ hipError_t launch_gather_layers(const GatherLayers &L, int n_layers, const int32
 
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
                          const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out,
-                         int budget_blocks, int budget_tokens, int32_t *n_tok, hipStream_t s)
+                         int budget_blocks, int budget_tokens, int32_t *n_tok, uint32_t *flags, hipStream_t s)
 {
     GatherLayers L = {};
+    L.flags = flags;
     L.sel[0] = sel;
     L.n_sel[0] = n_sel;
     L.pt[0] = pt;

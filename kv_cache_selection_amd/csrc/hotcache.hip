@@ -137,7 +137,7 @@ constexpr int kPieces = kRowBytes / 16;
 __global__ __launch_bounds__(kFetchThreads) void hot_fetch_kernel(
     const int2 *__restrict__ fetch, const int32_t *__restrict__ n_fetch, int budget_tokens,
     const int32_t *__restrict__ pt, int64_t pt_stride, int64_t n_slots, int max_ctx, const u32x4 *__restrict__ pool,
-    u32x4 *__restrict__ rows, int H)
+    u32x4 *__restrict__ rows, int H, uint32_t *flags)
 {
     const int b = blockIdx.y;
     int nf = n_fetch[b];
@@ -157,7 +157,10 @@ __global__ __launch_bounds__(kFetchThreads) void hot_fetch_kernel(
         if (i < nf) {
             const int2 f = fetch[(int64_t)b * budget_tokens + i];
             if (f.x >= 0 && f.x < max_ctx && f.y >= 0 && f.y < H) {
-                const int64_t slot = safe_slot(pt[(int64_t)b * pt_stride + f.x], n_slots);
+                const int32_t raw = pt[(int64_t)b * pt_stride + f.x];
+                const int64_t slot = safe_slot(raw, n_slots);
+                if (piece == 0 && slot != raw)
+                    raise_flag(flags, QSA_FLAG_BAD_SLOT);
                 v[k] = __builtin_nontemporal_load(pool + slot * kPieces + piece);
                 dst[k] = ((int64_t)b * H + f.y) * kPieces + piece;
             }
@@ -189,11 +192,12 @@ hipError_t launch_hot_update(const int32_t *sel, const int32_t *n_tok, int batch
 
 hipError_t launch_hot_fetch(const int2 *fetch, const int32_t *n_fetch, int batch, int budget_tokens,
                             const int32_t *pt, int64_t pt_stride, int64_t n_slots, int max_ctx, const void *pool,
-                            void *rows, int H, hipStream_t s)
+                            void *rows, int H, uint32_t *flags, hipStream_t s)
 {
     dim3 grid((unsigned)((budget_tokens + kFetchPerWg - 1) / kFetchPerWg), (unsigned)batch);
     hipLaunchKernelGGL(hot_fetch_kernel, grid, dim3(kFetchThreads), 0, s, fetch, n_fetch, budget_tokens, pt,
-                       pt_stride, n_slots, max_ctx, static_cast<const u32x4 *>(pool), static_cast<u32x4 *>(rows), H);
+                       pt_stride, n_slots, max_ctx, static_cast<const u32x4 *>(pool), static_cast<u32x4 *>(rows), H,
+                       flags);
     return hipGetLastError();
 }
 

@@ -71,8 +71,16 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
 
     const int b = blockIdx.y;
     const int64_t r0 = row0[b];
-    int L = clamp_ctx(ctx_len[b], max_ctx);
-    if (r0 < 0 || r0 + L > n_rows)
+    const int32_t L_raw = ctx_len[b];
+    int L = clamp_ctx(L_raw, max_ctx);
+    const bool bad_rows = r0 < 0 || r0 + L > n_rows;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (L != L_raw)
+            raise_flag(Ls.flags, QSA_FLAG_BAD_CTX_LEN);
+        if (bad_rows && L > 0)
+            raise_flag(Ls.flags, QSA_FLAG_BAD_INDEX_ROWS);
+    }
+    if (bad_rows)
         L = 0;                                    // rows outside the index buffer: empty
     const int t_begin = blockIdx.x * chunk_tokens;
     if (t_begin >= L)
@@ -235,6 +243,13 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n)
         p[i] = 0;
 }
 
+__global__ void copy_u32_kernel(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst, int64_t n)
+{
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src[i];
+}
+
 } // namespace
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)
@@ -245,6 +260,17 @@ hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)
     if (blocks > 2048)
         blocks = 2048;
     hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_u32(const uint32_t *src, uint32_t *dst, int64_t n, hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 2048)
+        blocks = 2048;
+    hipLaunchKernelGGL(copy_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
     return hipGetLastError();
 }
 
@@ -302,7 +328,7 @@ hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const i
         return launch_score_n(L, n_layers, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks,
                               sink_blocks, tail_tokens, s, ev0, ev1);
     const ScoreLayersT<1> L1 = {{L.keys[0]},         {L.scales[0]},       {L.q_idx[0]}, {L.w_idx[0]},
-                                {L.token_scores[0]}, {L.block_scores[0]}, {L.hist[0]}};
+                                {L.token_scores[0]}, {L.block_scores[0]}, {L.hist[0]},  L.flags};
     return launch_score_n(L1, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks, sink_blocks,
                           tail_tokens, s, ev0, ev1);
 }
@@ -310,10 +336,11 @@ hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const i
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
-                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s,
-                              hipEvent_t ev0, hipEvent_t ev1)
+                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, uint32_t *flags,
+                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
 {
     ScoreLayers L = {};
+    L.flags = flags;
     L.keys[0] = keys;
     L.scales[0] = scales;
     L.q_idx[0] = q_idx;

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/libqsa.h"
+
 namespace qsa {
 
 // Compiled geometry.
@@ -52,6 +54,14 @@ __device__ __forceinline__ int clamp_ctx(int32_t L, int max_ctx)
     return L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
 }
 
+// Records a contract violation (QSA_FLAG_*) in the call's flags word, if it
+// has one. Only the lanes that found one execute the atomic.
+__device__ __forceinline__ void raise_flag(uint32_t *flags, uint32_t bit)
+{
+    if (flags)
+        atomicOr(flags, bit);
+}
+
 // Block j is forced when it is one of the first sink blocks or holds one of
 // the last tail tokens.
 __device__ __forceinline__ int tail_first_block(int L, int tail_tokens, int n_blk)
@@ -79,13 +89,28 @@ struct SelectWs {
     uint64_t *slot_cand;   // [B][n_slices][kSliceBlocks] blocks inside the threshold bin
     uint64_t *spill;       // [B][spill_stride] candidates past the finish kernel's LDS
     int64_t spill_stride;
+    uint32_t *flags;       // the call's flags word (QSA_FLAG_*), or null
+    // The index rows of the batch (qsa_decode_step): a sequence whose rows
+    // [row0[b], row0[b] + L) fall outside [0, n_rows) was scored as empty, and
+    // the selection takes it as empty too. Null when there is no index.
+    const int64_t *row0;
+    int64_t n_rows;
 };
+
+// The length the selection works with: ctx_len clamped to [0, max_ctx], or 0
+// for a sequence whose index rows fall outside the index buffer.
+__device__ __forceinline__ int select_len(int32_t L_raw, int64_t r0, int max_ctx, const SelectWs &ws)
+{
+    const int L = clamp_ctx(L_raw, max_ctx);
+    return (ws.row0 && (r0 < 0 || r0 + L > ws.n_rows)) ? 0 : L;
+}
 
 struct AttnWs {
     float *part_o;       // [B][kHq][n_split][kDh]; room for splits of kTPSMin tokens
     float *part_lse;     // [B][kHq][n_split]
     int tps;             // tokens per split of this call: kTPS or kTPSMin
     int n_split;         // splits per sequence: budget / tps, rounded up
+    uint32_t *flags;     // the call's flags word, or null
 };
 
 // One launch of the selection or attention kernels may cover several layers
@@ -105,6 +130,7 @@ struct ScoreLayersT {
     float *token_scores[N];               // [rows] or null
     float *block_scores[N];               // [B][bs_stride]
     uint32_t *hist[N];                    // [B][kHistReps][kHistBins] or null
+    uint32_t *flags;                      // the call's flags word, or null
 };
 using ScoreLayers = ScoreLayersT<kMaxChainLayers>;
 
@@ -116,6 +142,7 @@ struct GatherLayersT {
     const void *pool[N];                  // [n_slots][kRowBytes], device or mapped pinned host memory
     void *out[N];                         // staging rows [B][budget_tokens][kRowBytes]
     int32_t *n_tok[N];                    // [B] or null
+    uint32_t *flags;                      // the call's flags word, or null
 };
 using GatherLayers = GatherLayersT<kMaxChainLayers>;
 
@@ -140,6 +167,7 @@ struct AttnLayersT {
     float *part_o[N];
     float *part_lse[N];
     float *out[N];                        // [B][kHq][kDh] fp32
+    uint32_t *flags;                      // the call's flags word, or null
 };
 using AttnLayers = AttnLayersT<kMaxChainLayers>;
 
@@ -194,11 +222,12 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1)
 
 // Kernel launchers (one translation unit each).
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_copy_u32(const uint32_t *src, uint32_t *dst, int64_t n, hipStream_t s);
 
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
-                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
+                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, uint32_t *flags,
                               hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Index scoring of layers 0 .. n_layers - 1 of L in one launch (grid z =
@@ -223,7 +252,7 @@ hipError_t launch_select_layers(const SelectLayers &L, int n_layers, int64_t bs_
 
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
                          const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out, int budget_blocks,
-                         int budget_tokens, int32_t *n_tok, hipStream_t s);
+                         int budget_tokens, int32_t *n_tok, uint32_t *flags, hipStream_t s);
 
 // Row gathers of layers 0 .. n_layers - 1 of L in one launch (grid z = layer).
 hipError_t launch_gather_layers(const GatherLayers &L, int n_layers, const int32_t *ctx_len, int batch, int max_ctx,
@@ -260,7 +289,7 @@ hipError_t launch_hot_update(const int32_t *sel, const int32_t *n_tok, int batch
                              int2 *fetch, int32_t *n_fetch, int32_t *n_miss_out, hipStream_t s);
 hipError_t launch_hot_fetch(const int2 *fetch, const int32_t *n_fetch, int batch, int budget_tokens,
                             const int32_t *pt, int64_t pt_stride, int64_t n_slots, int max_ctx, const void *pool,
-                            void *rows, int H, hipStream_t s);
+                            void *rows, int H, uint32_t *flags, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 
 // Per-layer pointers of the append step, passed by value.

@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kCollectThreads) void collect_kernel(const SelectLa
     const int b = blockIdx.y;
     const int slice = blockIdx.x;
     const int tid = threadIdx.x;
-    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    const SelectWs &ws = Ls.ws[blockIdx.z];
+    const int L = select_len(ctx_len[b], ws.row0 ? ws.row0[b] : 0, max_ctx, ws);
     const int n = (L + kBT - 1) / kBT;
     const int j0 = slice * kSliceBlocks;
     int tail_first = n;
@@ -257,11 +258,15 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(const SelectLayersT<N>
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int L = clamp_ctx(ctx_len[b], max_ctx);
+    const int32_t L_raw = ctx_len[b];
+    const int64_t r0 = ws.row0 ? ws.row0[b] : 0;
+    const int L = select_len(L_raw, r0, max_ctx, ws);
     const int n = (L + kBT - 1) / kBT;
     int32_t *sel_b = sel + (int64_t)b * K;
     int tail_first = n;
     const int r = rest_to_take(L, n, K, sink_blocks, tail_tokens, &tail_first);
+    if (tid == 0 && clamp_ctx(L_raw, max_ctx) != L_raw)
+        raise_flag(ws.flags, QSA_FLAG_BAD_CTX_LEN);
 
     if (r < 0) {
         // Every block fits in the budget.
@@ -508,8 +513,11 @@ __global__ __launch_bounds__(kOneThreads) void select_one_kernel(const SelectLay
     const int wave = tid >> 6;
     const int nmax = (max_ctx + kBT - 1) / kBT;     // > K >= 1 (host), and <= bs_stride
 
-    // One round of loads: the length, the histogram copies, every score.
+    // One round of loads: the length, the index row offset, the histogram
+    // copies, every score.
+    const SelectWs &ws = Ls.ws[blockIdx.y];
     const int32_t Lraw = ctx_len[b];
+    const int64_t r0 = ws.row0 ? ws.row0[b] : 0;
     constexpr int W = kHistBins / kOneThreads;
     const uint32_t *hb = hist + ((int64_t)b * kHistReps * kHistBins + W * (kOneThreads - 1 - tid));
     uint32_t hraw[kHistReps][W];
@@ -524,9 +532,11 @@ __global__ __launch_bounds__(kOneThreads) void select_one_kernel(const SelectLay
     for (int i = 0; i < PER; i++)
         key[i] = __float_as_uint(row[min(tid + kOneThreads * i, nmax - 1)]);
 
-    const int L = clamp_ctx(Lraw, max_ctx);
+    const int L = select_len(Lraw, r0, max_ctx, ws);
     const int n = (L + kBT - 1) / kBT;
     int32_t *sel_b = sel + (int64_t)b * K;
+    if (tid == 0 && clamp_ctx(Lraw, max_ctx) != Lraw)
+        raise_flag(ws.flags, QSA_FLAG_BAD_CTX_LEN);
     int tail_first = n;
     const int r = rest_to_take(L, n, K, sink_blocks, tail_tokens, &tail_first);
     if (r < 0) {

@@ -19,3 +19,19 @@ def gpu():
     import torch
     assert torch.cuda.is_available(), "GPU test collected on a machine without a GPU"
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With QSA_STATS_OUT set, write the plain relative errors the score
+    checks recorded (qsa_testlib.SCORE_STATS) to that file as JSON lines."""
+    path = os.environ.get("QSA_STATS_OUT")
+    if not path:
+        return
+    import json
+    lib = sys.modules.get("qsa_testlib")
+    if lib is None:
+        return
+    with open(path, "w") as f:
+        for what, n, rel_max, share, zero_ref_nonzero in lib.SCORE_STATS:
+            f.write(json.dumps({"what": what, "scores": n, "max_rel_err": rel_max, "share_within_1e-5": share,
+                                "nonzero_where_ref_is_zero": zero_ref_nonzero}) + "\n")

@@ -113,11 +113,47 @@ def test_bad_arguments_rejected_before_launch():
                                     0, FAKE, 1 << 30, 4096, [8192, 8192]),                       # repeated side
         lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)],
                                     0, FAKE, 1 << 30, 4096, list(range(8192, 8192 + 9))),        # too many
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)] * 65,
+                                    0, FAKE, 1 << 30),                                           # > 64 layers
+        # the kernels read 16-byte pieces of the queries and 4-byte words of the weights
+        lambda: qsa.qsa_index_score(cfg, _batch(), FAKE, FAKE, FAKE + 8, FAKE, None, FAKE, 25),  # q_idx at 8
+        lambda: qsa.qsa_index_score(cfg, _batch(), FAKE, FAKE + 1, FAKE, FAKE, None, FAKE, 25),  # odd scales
+        lambda: qsa.qsa_index_score(cfg, _batch(), FAKE, FAKE, FAKE, FAKE + 2, None, FAKE, 25),  # w_idx at 2
+        lambda: qsa.qsa_index_score_multi(cfg, _batch(), 4, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 25),
+        lambda: qsa.qsa_index_score_multi(cfg, _batch(), 4, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, 25),
+        lambda: qsa.qsa_sparse_decode(cfg, 1, FAKE + 8, FAKE, FAKE, FAKE, FAKE, 1 << 30),       # q at 8
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE)],
+                                    0, FAKE, 1 << 30),                                           # q_idx at 8
+        lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE)],
+                                    0, FAKE, 1 << 30),                                           # q at 8
+        lambda: qsa.qsa_read_flags(None, FAKE),
+        lambda: qsa.qsa_read_flags(FAKE + 4, FAKE),                                              # ws not 256-aligned
+        lambda: qsa.qsa_read_flags(FAKE, FAKE + 2),
     ]
     for i, c in enumerate(cases):
         with pytest.raises(qsa.QsaError) as ei:
             c()
         assert ei.value.status == E, i
+
+
+def test_step_events_required_and_validated():
+    """The schedules that order several streams (a hot cache with side
+    streams, or more than 16 layers on HBM pools with side streams) need a
+    caller-made event set; the library creates no HIP object inside a call."""
+    cfg = qsa.make_config(256)
+    hc = qsa.make_hot_cache(FAKE, FAKE, FAKE, 256)
+    lay_hot = qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, hot=hc)
+    lay = qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for layers, loc in [([lay_hot] * 2, qsa.QSA_KV_HOST_PINNED), ([lay] * 17, qsa.QSA_KV_DEVICE)]:
+        with pytest.raises(qsa.QsaError) as ei:
+            qsa.qsa_decode_step(cfg, _batch(), layers, loc, FAKE, 1 << 34, 4096, [8192])
+        assert ei.value.status == qsa.QSA_ERR_INVALID_ARGUMENT
+    for bad in ((0, 1), (4, -1), (4, qsa.QSA_MAX_SIDE_STREAMS + 1)):
+        with pytest.raises(qsa.QsaError) as ei:
+            qsa.StepEvents(*bad)
+        assert ei.value.status == qsa.QSA_ERR_INVALID_ARGUMENT
+    assert qsa.lib.qsa_step_events_create(4, 1, None) == qsa.QSA_ERR_INVALID_ARGUMENT
+    qsa.lib.qsa_step_events_destroy(None)          # a no-op
 
 
 def test_workspace_too_small_rejected():

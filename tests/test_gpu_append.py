@@ -8,6 +8,8 @@ import torch
 import oracle
 import qsa_synth as S
 
+from qsa_testlib import check_attention
+
 pytestmark = pytest.mark.gpu
 
 qsa = pytest.importorskip("kv_cache_selection_amd")
@@ -179,4 +181,4 @@ def test_append_then_decode_attends_the_new_tokens(gpu):
     assert np.all(np.abs(bs[diff].astype(np.float64) - ref.kth_score) <= 1e-5 * abs(ref.kth_score)), diff
     toks = oracle.tokens_of_blocks(L, got)
     want = oracle.attention(toks, st.pt[0], st.pools[0], q[0], G.n_kv_heads, G.sm_scale)
-    assert np.abs(out[0].cpu().numpy() - want).max() <= 2e-3
+    check_attention(out[0].cpu().numpy(), want, "append-then-decode")

@@ -11,7 +11,7 @@ import oracle
 import qsa_synth as S
 from qsa_synth.device import DeviceInputs
 
-from qsa_testlib import check_selection, oracle_attention_on, oracle_unit
+from qsa_testlib import check_attention, check_selection, oracle_attention_on, oracle_unit
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,7 @@ def test_hot_cache_steps(gpu, n_side):
     ref_own = [np.full((B, H), -1, np.int64) for _ in range(NL)]
     rng = np.random.default_rng(71)
     side = [torch.cuda.Stream() for _ in range(n_side)]
+    ev = qsa.StepEvents(NL, n_side) if n_side else None
     base_q_idx = hi.q_idx.copy()
     n_fetched = []
     for step in range(4):
@@ -65,10 +66,11 @@ def test_hot_cache_steps(gpu, n_side):
         mk = lambda out, hot: [qsa.make_layer(di.keys[l], di.scales[l], d_qi[l], di.w_idx[l], d_q[l], di.pool[l],
                                               out[l], None, sel[l], ns[l], hot=hot[l] if hot else None)
                                for l in range(NL)]
-        qsa.qsa_decode_step(cfg, bt, mk(out_hot, caches), loc, ws, nws, torch.cuda.current_stream(), side)
+        qsa.qsa_decode_step(cfg, bt, mk(out_hot, caches), loc, ws, nws, torch.cuda.current_stream(), side, events=ev)
         torch.cuda.synchronize()
         sel_h, ns_h = sel.cpu().numpy().copy(), ns.cpu().numpy().copy()
-        qsa.qsa_decode_step(cfg, bt, mk(out_plain, None), loc, ws, nws, torch.cuda.current_stream(), side)
+        qsa.qsa_decode_step(cfg, bt, mk(out_plain, None), loc, ws, nws, torch.cuda.current_stream(), side,
+                            events=ev)
         torch.cuda.synchronize()
         assert np.array_equal(sel.cpu().numpy(), sel_h)
         assert np.array_equal(out_hot.cpu().numpy(), out_plain.cpu().numpy())      # the cache is transparent
@@ -96,7 +98,7 @@ def test_hot_cache_steps(gpu, n_side):
                 assert np.array_equal(grows[b, owned], host_rows), (step, l, b)
                 hi.q[l, b] = q[l, b]
                 want = oracle_attention_on(hi, l, b, toks)
-                assert np.abs(out_hot[l, b].cpu().numpy() - want).max() <= 2e-3
+                check_attention(out_hot[l, b].cpu().numpy(), want, "hot l%d b%d" % (l, b))
         hi.q_idx[:] = base_q_idx
         n_fetched.append(step_fetches)
     # the first step fetches every selected row; later steps reuse the cache
