@@ -299,8 +299,27 @@ void qsa_step_events_destroy(qsa_step_events_t *events);
 /* Enqueues a copy of the flags word of `workspace` (a workspace passed to
  * qsa_decode_step, qsa_topk_blocks or qsa_sparse_decode; the word covers the
  * last call that used it, once that call has run) to flags_out (device, one
- * uint32), on `stream`. */
+ * uint32), on `stream`. workspace NULL reads the flags word of
+ * qsa_decode_step_static's scratch on the current device. */
 qsa_status_t qsa_read_flags(const void *workspace, uint32_t *flags_out, qsa_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid allocation): qsa_decode_step with the
+ * workspace taken from a static device array of QSA_STATIC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ * The call allocates nothing; the caller still passes every input and output
+ * (and, for the schedules that need them, the event set). Its workspace need
+ * (qsa_workspace_size) must fit the array, else QSA_ERR_WORKSPACE_TOO_SMALL
+ * and nothing is enqueued. Every call on a GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (several host threads, or streams
+ * not ordered after each other) race and give undefined results. The first
+ * call on a device looks up that device's copy of the array (with the device
+ * current) and keeps its address. Results are bit-identical to
+ * qsa_decode_step's. */
+#define QSA_STATIC_SCRATCH_BYTES (64u << 20)
+qsa_status_t qsa_decode_step_static(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
+                                    int32_t n_layers, qsa_kv_location_t kv_location, qsa_stream_t compute,
+                                    const qsa_stream_t *side, int32_t n_side, qsa_step_events_t *events);
 
 /* Empties a hot cache: map[b][0..pt_stride) and owner[b][0..hot_slots) = -1
  * for every sequence of the batch. */

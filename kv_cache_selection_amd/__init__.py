@@ -26,7 +26,8 @@ QSA_MAX_SIDE_STREAMS = 8
 
 # Every symbol include/libqsa.h declares.
 EXPORTS = ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-           "qsa_step_events_create", "qsa_step_events_destroy", "qsa_read_flags", "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi",
+           "qsa_step_events_create", "qsa_step_events_destroy", "qsa_read_flags", "qsa_decode_step_static",
+           "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi",
            "qsa_pool_create", "qsa_pool_destroy", "qsa_pool_open", "qsa_pool_next", "qsa_pool_close",
            "qsa_pool_free_slots", "qsa_pool_generations",
            "qsa_workspace_size", "qsa_layer_bytes", "qsa_status_string")
@@ -104,8 +105,10 @@ def _load():
     lib.qsa_step_events_destroy.argtypes = [P]
     lib.qsa_step_events_destroy.restype = None
     lib.qsa_read_flags.argtypes = [P, P, P]
+    lib.qsa_decode_step_static.argtypes = [CP, BP, ctypes.POINTER(Layer), i32, i32, P,
+                                           ctypes.POINTER(ctypes.c_void_p), i32, P]
     for f in ("qsa_index_score", "qsa_topk_blocks", "qsa_gather_kv", "qsa_sparse_decode", "qsa_decode_step",
-              "qsa_step_events_create", "qsa_read_flags",
+              "qsa_step_events_create", "qsa_read_flags", "qsa_decode_step_static",
               "qsa_append_token", "qsa_hot_reset", "qsa_move_tokens", "qsa_check_generations", "qsa_index_score_multi", "qsa_pool_create",
               "qsa_pool_open", "qsa_pool_next", "qsa_pool_close", "qsa_pool_generations"):
         getattr(lib, f).restype = i32
@@ -269,6 +272,19 @@ def qsa_decode_step(cfg, batch, layers, kv_location, workspace, workspace_bytes,
     _check("qsa_decode_step", lib.qsa_decode_step(ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers),
                                                   kv_location, _p(workspace), workspace_bytes, _stream(compute),
                                                   sarr, n_side, events.handle if events is not None else None))
+
+
+QSA_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def qsa_decode_step_static(cfg, batch, layers, kv_location, compute=None, side=None, events=None):
+    """qsa_decode_step with the library's static scratch as the workspace
+    (allocates nothing; up to QSA_STATIC_SCRATCH_BYTES of workspace need)."""
+    arr = (Layer * len(layers))(*layers)
+    sarr, n_side = _side_array(side)
+    _check("qsa_decode_step_static", lib.qsa_decode_step_static(
+        ctypes.byref(cfg), ctypes.byref(batch), arr, len(layers), kv_location, _stream(compute), sarr, n_side,
+        events.handle if events is not None else None))
 
 
 def qsa_read_flags(workspace, flags_out, stream=None):

@@ -205,6 +205,48 @@ int events_needed(int n_layers, int n_side) { return 3 * n_layers + n_side + 1; 
 
 } // namespace
 
+// Scratch of qsa_decode_step_static: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends. In host code its name
+// is only a stand-in for the symbol: the device address of each GPU's copy is
+// fetched once per device with hipGetSymbolAddress, and only that address is
+// ever passed to kernels or fills.
+static __device__ __align__(256) uint8_t scratch[QSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up on the first call on
+// each device (with that device current); nullptr with *err set on failure.
+void *static_scratch(qsa_status_t *err)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = QSA_ERR_HIP;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+            (void)hipGetLastError();
+            *err = QSA_ERR_HIP;
+            return nullptr;
+        }
+        p = q;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+} // namespace
+
 // The caller's event set (qsa_step_events_create).
 struct qsa_step_events {
     int device;
@@ -253,8 +295,13 @@ void qsa_step_events_destroy(qsa_step_events_t *events)
 
 qsa_status_t qsa_read_flags(const void *workspace, uint32_t *flags_out, qsa_stream_t stream)
 {
-    if (!workspace || !flags_out || !aligned(workspace, kAlign) || !aligned(flags_out, 4))
+    if (!flags_out || !aligned(flags_out, 4) || (workspace && !aligned(workspace, kAlign)))
         return QSA_ERR_INVALID_ARGUMENT;
+    if (!workspace) {
+        qsa_status_t err = QSA_OK;
+        if (!(workspace = static_scratch(&err)))
+            return err;
+    }
     return hip_status(launch_copy_u32(static_cast<const uint32_t *>(workspace), flags_out, 1, (hipStream_t)stream));
 }
 
@@ -823,6 +870,27 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                         lw[l0].aw.tps, sc);
     }
     return hip_status(e);
+}
+
+qsa_status_t qsa_decode_step_static(const qsa_config_t *cfg, const qsa_batch_t *batch, const qsa_layer_t *layers,
+                                    int32_t n_layers, qsa_kv_location_t kv_location, qsa_stream_t compute,
+                                    const qsa_stream_t *side, int32_t n_side, qsa_step_events_t *events)
+{
+    qsa_status_t st = check_config(cfg);
+    if (st != QSA_OK)
+        return st;
+    if ((st = check_batch(batch, true, true)) != QSA_OK)
+        return st;
+    if (n_layers < 1 || n_layers > QSA_MAX_LAYERS ||
+        (kv_location != QSA_KV_DEVICE && kv_location != QSA_KV_HOST_PINNED))
+        return QSA_ERR_INVALID_ARGUMENT;
+    if (make_layout(cfg, batch->batch, batch->max_ctx, n_layers, kv_location).total > QSA_STATIC_SCRATCH_BYTES)
+        return QSA_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = static_scratch(&st);
+    if (!ws)
+        return st;
+    return qsa_decode_step(cfg, batch, layers, n_layers, kv_location, ws, QSA_STATIC_SCRATCH_BYTES, compute, side,
+                           n_side, events);
 }
 
 } // extern "C"

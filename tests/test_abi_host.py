@@ -126,7 +126,7 @@ def test_bad_arguments_rejected_before_launch():
                                     0, FAKE, 1 << 30),                                           # q_idx at 8
         lambda: qsa.qsa_decode_step(cfg, _batch(), [qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE)],
                                     0, FAKE, 1 << 30),                                           # q at 8
-        lambda: qsa.qsa_read_flags(None, FAKE),
+        lambda: qsa.qsa_read_flags(FAKE, None),
         lambda: qsa.qsa_read_flags(FAKE + 4, FAKE),                                              # ws not 256-aligned
         lambda: qsa.qsa_read_flags(FAKE, FAKE + 2),
     ]

@@ -552,8 +552,10 @@ def test_decode_step_reports_bad_entries(gpu):
     neg_pt = di.pt.clone()
     neg_pt[3, L3 - 1] = -3
     assert run(di, hbm, pt=neg_pt)[0] == qsa.QSA_FLAG_BAD_SLOT
+    # the longest sequence claims one token more than max_ctx: clamped back to
+    # its own length, so only the length is reported
     ctx = di.ctx.clone()
-    ctx[0] = di.max_ctx + 1
+    ctx[int(np.argmax(di.hi.lay.ctx))] = di.max_ctx + 1
     assert run(di, hbm, ctx=ctx)[0] == qsa.QSA_FLAG_BAD_CTX_LEN
     f, ns = run(di, hbm, n_rows=di.n_rows - 1)           # the last sequence's rows run past the buffer
     assert f == qsa.QSA_FLAG_BAD_INDEX_ROWS
