@@ -48,9 +48,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+DRIFT = 0.25                  # indexer-query noise of the drifting region
+DRIFT_VARIANTS = 8
 PCIE_PEAK_GBS = 64.0          # PCIe 5.0 x16, one direction
 SCORE_KERNEL = "index_score_kernel"
 SCORE_SOURCES = ("kv_cache_selection_amd/csrc/index_score.hip", "kv_cache_selection_amd/csrc/qsa_internal.h")
+ATTN_KERNEL = "attn_split_kernel"
+ATTN_SOURCES = ("kv_cache_selection_amd/csrc/attention.hip", "kv_cache_selection_amd/csrc/qsa_internal.h")
 COPY_BYTES = 1 << 28
 
 
@@ -58,10 +62,10 @@ def pmc_file(workload):
     return os.path.join(ROOT, "profiles", "%s.%s.pmc.txt" % (SCORE_KERNEL, workload))
 
 
-def score_source_hash():
+def score_source_hash(sources=SCORE_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in SCORE_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -103,11 +107,13 @@ def pmc_summary(paths, workload):
              "factors" % COPY_BYTES,
              "kernel: %s" % SCORE_KERNEL,
              "source_sha256: %s" % score_source_hash(),
+             "attn_source_sha256: %s" % score_source_hash(ATTN_SOURCES),
              "fetch_factor: %.4f" % f_fetch,
              "write_factor: %.4f" % f_write]
     # the scoring kernel comes as a launch over a group of layers (the
     # overlapped step) and as a launch per layer (the one-stream step)
     score = {}
+    attn = {}
     rows = []
     for name in sorted(set(fetch) | set(write)):
         fv, wv = fetch.get(name, []), write.get(name, [])
@@ -117,12 +123,16 @@ def pmc_summary(paths, workload):
         rows.append((byt, name, len(fv), fk, wk))
         if SCORE_KERNEL in name:
             score["layer" if "ScoreLayersT<1>" in name else "group"] = byt
+        if ATTN_KERNEL in name and "AttnLayersT<1>" not in name:
+            attn["group"] = byt
     if not score:
         raise SystemExit("no %s dispatch in the counter files" % SCORE_KERNEL)
     if "group" in score:
         lines.append("traffic_bytes_per_group_launch: %d" % round(score["group"]))
     if "layer" in score:
         lines.append("traffic_bytes_per_layer_launch: %d" % round(score["layer"]))
+    if "group" in attn:
+        lines.append("attn_traffic_bytes_per_group_launch: %d" % round(attn["group"]))
     lines.append("")
     lines.append("%14s %8s %14s %14s  %s" % ("bytes/dispatch", "dispatch", "FETCH KiB", "WRITE KiB", "kernel"))
     for byt, name, n, fk, wk in sorted(rows, reverse=True):
@@ -150,20 +160,34 @@ def stats_summary(path, workload, op="step", bench_args=""):
     return "\n".join(lines) + "\n"
 
 
+def read_pmc_summary(workload):
+    path = pmc_file(workload)
+    kv = {}
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
 def read_traffic(workload, grouped):
     """The scoring kernel's measured HBM bytes per launch (of a group of
     layers, or of one layer), or None when there is no summary for this
     workload or the kernel changed since."""
-    path = pmc_file(workload)
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
+    kv = read_pmc_summary(workload)
     key = "traffic_bytes_per_group_launch" if grouped else "traffic_bytes_per_layer_launch"
     if kv.get("source_sha256") != score_source_hash() or key not in kv:
+        return None
+    return int(kv[key])
+
+
+def read_attn_traffic(workload):
+    """The attention kernel's measured HBM bytes per launch over a group of
+    layers, or None when there is no summary or the kernel changed since."""
+    kv = read_pmc_summary(workload)
+    key = "attn_traffic_bytes_per_group_launch"
+    if kv.get("attn_source_sha256") != score_source_hash(ATTN_SOURCES) or key not in kv:
         return None
     return int(kv[key])
 
@@ -186,15 +210,110 @@ def h2d_copy_gbs(n_bytes=1 << 28, reps=10):
     return n_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+BENCH_STREAM_SRC = os.path.join(ROOT, "bench_stream.hip")
+BENCH_STREAM_LIB = os.path.join(ROOT, "_build", "libqsabench.so")
+
+
+def build_stream_probe():
+    """Compile bench_stream.hip (the streaming-read reference) for gfx950."""
+    import subprocess
+    os.makedirs(os.path.dirname(BENCH_STREAM_LIB), exist_ok=True)
+    tmp = BENCH_STREAM_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", BENCH_STREAM_SRC,
+                           "-o", tmp])
+    os.replace(tmp, BENCH_STREAM_LIB)
+    return BENCH_STREAM_LIB
+
+
+def stream_read_gbs(n_bytes=1660944384 // (1 << 20) * (1 << 20), reps=10):
+    """GB/s of a plain front-to-back read of an n_bytes device buffer (256 KB
+    per workgroup, eight 16-byte loads in flight per lane), timed with events
+    over `reps` reads."""
+    import torch
+    if not os.path.exists(BENCH_STREAM_LIB):
+        raise RuntimeError("libqsabench.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(BENCH_STREAM_LIB)
+    lib.bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.bench_stream_read.restype = ctypes.c_int
+    chunk = 256 * 1024
+    n_wg = n_bytes // chunk
+    buf = torch.empty(n_wg * chunk, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.empty(n_wg * 256, dtype=torch.int32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        if lib.bench_stream_read(ctypes.c_void_p(buf.data_ptr()), n_wg, chunk, ctypes.c_void_p(out.data_ptr()), s):
+            raise RuntimeError("bench_stream_read failed")
+
+    for _ in range(3):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return n_wg * chunk * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def stream_ceiling(step_gbs, scan_gbs):
     """A streaming-read ceiling measured on the same GPU: a plain read of a
-    buffer the size of the 12-layer index (1.66 GB), 256 KB per workgroup with
-    eight 16-byte loads in flight per lane. The step's and the scan's
-    algorithmic GB/s are given as fractions of it."""
-    from qsa_synth import fill
-    gbs = fill.stream_read_gbs()
+    buffer the size of the 12-layer index (1.66 GB). The step's and the
+    scan's algorithmic GB/s are given as fractions of it."""
+    gbs = stream_read_gbs()
     return {"achieved": round(gbs, 1), "unit": "GB/s", "kind": "plain streaming read of 1.66 GB",
             "step_frac": round(step_gbs / gbs, 4), "scan_frac": round(scan_gbs / gbs, 4)}
+
+
+def ctx_label(n):
+    """262144 -> '256K', 1048576 -> '1M'."""
+    if n % (1 << 20) == 0:
+        return "%dM" % (n >> 20)
+    if n % 1024 == 0:
+        return "%dK" % (n >> 10)
+    return str(n)
+
+
+def metric_for(wl, kv_host):
+    """The metric string of a workload's decode step (the headline workload's
+    is the one the reference's benchmark is quoted with)."""
+    if wl.ctx is not None and len(set(wl.ctx)) == 1:
+        size = "%d\u00d7%s" % (wl.batch, ctx_label(int(wl.ctx[0])))
+    elif wl.ctx is not None:
+        size = "%d sequences of %s-%s" % (wl.batch, ctx_label(min(wl.ctx)), ctx_label(max(wl.ctx)))
+    else:
+        size = "%d\u00d7U[%d,%d]" % (wl.batch, wl.ragged[0], wl.ragged[1])
+    if kv_host:
+        return "QSA decode layer-steps/s at %s ctx, KV in pinned host memory; achieved PCIe GB/s as %% of peak" % size
+    return "QSA decode layer-steps/s at %s ctx; achieved HBM GB/s as %% of peak" % size
+
+
+def step_percentiles(ms):
+    """p10 / median / p90 (and the extremes) of per-step times in ms."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "median": round(float(np.median(a)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "min": round(float(a.min()), 4),
+            "max": round(float(a.max()), 4), "n": int(a.size)}
+
+
+def timed_steps(run, n, stream):
+    """Runs `run()` n times back to back with an event between consecutive
+    calls (no synchronisation inside the region): the mean and the per-call
+    times in ms."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n):
+        run()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    return evs[0].elapsed_time(evs[n]) / n, per
 
 
 def copy_calibration():
@@ -353,6 +472,66 @@ def cpu_baseline(wl, hi, seconds):
                       "layer-step is %d units; input generation excluded" % (n_thr, wl.name, n_done, wall,
                                                                             wl.batch),
             "single_core": single}
+
+
+def context_sweep(args, known):
+    """The headline schedule at a fixed budget over three contexts (8 x 16K,
+    64K and 256K tokens, 12 layers): the step time, the scan launch's time
+    (HIP events taken by the launch) and what is left, the selection chain
+    and attention, which do not grow with the context. `known` holds the
+    headline workload's (ms_per_step, scan_ms), measured already."""
+    import numpy as np
+    import torch
+    import kv_cache_selection_amd as qsa
+    import qsa_synth as S
+    from qsa_synth.device import DeviceInputs
+    g = S.GEOM
+    dev = torch.device("cuda:0")
+    hev = HipEvents()
+    points = []
+    for name in ("batch8-16k", "batch8-64k", "batch8-256k"):
+        wl = S.WORKLOADS[name]
+        if name in known:
+            ms, scan_ms = known[name]
+        else:
+            di = DeviceInputs(wl, dev)
+            NL, B = di.n_layers, di.batch
+            K = wl.budget // g.block_tokens
+            cfg = qsa.make_config(wl.budget, wl.sink_blocks, wl.tail_tokens, g.sm_scale)
+            bt = qsa.make_batch(B, di.max_ctx, di.ctx, di.row0, di.pt, di.pt_stride, di.n_slots, di.n_rows)
+            sel = torch.zeros((NL, B, K), dtype=torch.int32, device=dev)
+            ns = torch.zeros((NL, B), dtype=torch.int32, device=dev)
+            nws = qsa.qsa_workspace_size(cfg, B, di.max_ctx, NL, qsa.QSA_KV_DEVICE)
+            ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+            stream = torch.cuda.current_stream()
+            side = [torch.cuda.Stream()]
+            events = qsa.StepEvents(NL, 1)
+            ev = (hev.create(), hev.create())
+            lys = [qsa.make_layer(di.keys[l], di.scales[l], di.q_idx[l], di.w_idx[l], di.q[l], di.pool[l],
+                                  di.out[l], None, sel[l], ns[l], ev if l == 0 else None) for l in range(NL)]
+
+            def run():
+                qsa.qsa_decode_step(cfg, bt, lys, qsa.QSA_KV_DEVICE, ws, nws, stream, side, events)
+
+            for _ in range(args.warmup):
+                run()
+            ms, _ = timed_steps(run, args.steps, stream)
+            scans = []
+            for _ in range(args.steps):
+                run()
+                torch.cuda.synchronize()
+                scans.append(hev.elapsed_ms(*ev))
+            scan_ms = float(np.mean(scans))
+            del di, ws, lys
+            torch.cuda.empty_cache()
+        ctx = int(wl.ctx[0])
+        idx_bytes = wl.batch * ctx * g.index_row_bytes * wl.layers
+        points.append({"workload": name, "ctx": ctx, "ms_per_step": round(ms, 4),
+                       "scan_us": round(scan_ms * 1e3, 2), "non_scan_us": round((ms - scan_ms) * 1e3, 2),
+                       "scan_gbs": round(idx_bytes / (scan_ms * 1e-3) / 1e9, 1)})
+    return {"budget_tokens": 2048, "batch": 8, "layers": 12, "points": points,
+            "note": "non_scan_us = step - scan launch: selection chain, attention over the 2048 selected tokens "
+                    "per sequence and layer, merge, launch gaps"}
 
 
 def bench_append(args):
@@ -587,6 +766,8 @@ def main():
                     help="step: the decode step (default); append: the append step alone; lease: slot leases; "
                          "multi: multi-query scoring")
     ap.add_argument("--queries", type=int, default=64, help="queries per sequence for --op multi")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false",
+                    help="skip the fixed-budget context sweep (8 x {16K, 64K, 256K})")
     ap.add_argument("--copy-calibration", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--pmc-summary", nargs=4, metavar="CSV", help=argparse.SUPPRESS)
     ap.add_argument("--stats-summary", metavar="CSV", help=argparse.SUPPRESS)
@@ -681,15 +862,54 @@ def main():
         step(plain)
     torch.cuda.synchronize()
 
-    # Timed region 1: whole steps.
+    # Timed region 1: whole steps, an event between consecutive steps.
+    ms_step, per_step = timed_steps(lambda: step(plain), args.steps, stream)
+    ctx = di.hi.lay.ctx
+    ntok = tokens_selected(sel.cpu().numpy(), ns.cpu().numpy(), ctx)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step(plain)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # Timed region 1b (HBM workloads with one query set): the same steps with
+    # drifting indexer queries, cycling through DRIFT_VARIANTS query sets so
+    # that consecutive steps select different (overlapping) rows and no step
+    # re-reads exactly the rows the one before it read.
+    drifting = None
+    if NV == 1 and not di.kv_host and not hot:
+        import dataclasses
+        wl_d = dataclasses.replace(wl, drift=DRIFT, step_variants=DRIFT_VARIANTS)
+        qd = []
+        for v in range(DRIFT_VARIANTS):
+            qi, qq = S.step_queries(wl_d, di.hi, v)
+            qd.append((torch.from_numpy(qi.view(np.int16)).to(dev), torch.from_numpy(qq.view(np.int16)).to(dev)))
+        dl = [[qsa.make_layer(di.keys[l], di.scales[l], qd[v][0][l], di.w_idx[l], qd[v][1][l], di.pool[l],
+                              di.out[l], None, sel[l], ns[l]) for l in range(NL)] for v in range(DRIFT_VARIANTS)]
+        # the blocks that consecutive query sets share (untimed)
+        sels = []
+        for v in range(DRIFT_VARIANTS):
+            qsa.qsa_decode_step(cfg, bt, dl[v], loc, ws, nws, stream, side, events)
+            torch.cuda.synchronize()
+            sels.append((sel.cpu().numpy().copy(), ns.cpu().numpy().copy()))
+        shared = []
+        for v in range(DRIFT_VARIANTS):
+            (a, na), (b, nb) = sels[v], sels[(v + 1) % DRIFT_VARIANTS]
+            for l in range(NL):
+                for q in range(di.batch):
+                    sa, sb = set(a[l, q, :na[l, q]].tolist()), set(b[l, q, :nb[l, q]].tolist())
+                    shared.append(len(sa & sb) / max(len(sa), 1))
+        k_d = [0]
+
+        def step_drift():
+            qsa.qsa_decode_step(cfg, bt, dl[k_d[0] % DRIFT_VARIANTS], loc, ws, nws, stream, side, events)
+            k_d[0] += 1
+
+        for _ in range(args.warmup):
+            step_drift()
+        ms_drift, per_drift = timed_steps(step_drift, args.steps, stream)
+        drifting = {"ms_per_step": round(ms_drift, 4), "value": round(NL / (ms_drift * 1e-3), 2),
+                    "step_ms": step_percentiles(per_drift), "query_variants": DRIFT_VARIANTS, "drift": DRIFT,
+                    "shared_blocks_consecutive": round(float(np.mean(shared)), 4),
+                    "note": "indexer queries bf16(q_idx + drift N(0,1)), a new draw per variant, and fresh "
+                            "attention queries; the variants are cycled, so consecutive steps select overlapping "
+                            "but different blocks"}
 
     # Timed region 2: the same steps with every kernel in order on one stream (each layer's
     # score -> select -> attention -> merge before the next layer starts).
@@ -764,8 +984,6 @@ def main():
             tot += int(n_miss.sum())
         fetched = tot / NV
 
-    ctx = di.hi.lay.ctx
-    ntok = tokens_selected(sel.cpu().numpy(), ns.cpu().numpy(), ctx)
     idx_bytes_layer = int(ctx.sum()) * g.index_row_bytes
     idx_bytes_launch = idx_bytes_layer * layers_per_launch
     step_bytes = idx_bytes_layer * NL + int(ntok.sum()) * g.row_bytes
@@ -774,14 +992,17 @@ def main():
     step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     value = NL / (ms_step * 1e-3)
 
+    rows_bytes = int(ntok.sum()) * g.row_bytes
+    attn_traffic = read_attn_traffic(wl.name) if grouped else None
     result = {
-        "metric": "QSA decode layer-steps/s at 8x256K ctx; achieved HBM GB/s as % of peak",
+        "metric": metric_for(wl, di.kv_host),
         "value": round(value, 2),
         "unit": "layer-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": step_percentiles(per_step),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -808,7 +1029,16 @@ def main():
                        "value": round(NL / ((ms_serial if ms_serial is not None else ms_step) * 1e-3), 2)},
         "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes},
+        # the attention launch of the headline schedule (all layers in one
+        # launch): its algorithmic bytes (the selected rows) and the HBM
+        # bytes the counters measured for it (profiles/), when current
+        "attention": {"kernel": ATTN_KERNEL, "layers_per_launch": NL if grouped else 1,
+                      "bytes_per_launch": rows_bytes if grouped else rows_bytes // NL,
+                      "traffic": attn_traffic,
+                      "traffic_over_bytes": None if attn_traffic is None else round(attn_traffic / rows_bytes, 4)},
     }
+    if drifting is not None:
+        result["drifting"] = drifting
     if di.kv_host:
         # every gathered row crosses PCIe once per step (with a hot cache: the misses only)
         pcie_bytes = int(ntok.sum()) * g.row_bytes if fetched is None else int(round(fetched)) * g.row_bytes
@@ -824,6 +1054,8 @@ def main():
                                    "hit_rate": round(1.0 - fetched / max(int(ntok.sum()), 1), 4)}
     if not di.kv_host:
         result["stream_ceiling"] = stream_ceiling(step_gbs, achieved)
+    if wl.name == "batch8-256k" and args.sweep:
+        result["context_sweep"] = context_sweep(args, {wl.name: (ms_step, score_ms)})
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, di.hi, args.cpu_seconds)
     print(json.dumps(result), flush=True)

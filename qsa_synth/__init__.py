@@ -178,6 +178,9 @@ WORKLOADS = {
                              ragged=(3072, 4608), seed=2),
     "batch8-256k": Workload("batch8-256k", 8, (262144,) * 8, 12, 2048, sink_blocks=1,
                             planted=32, seed=3),
+    # the same batch at shorter contexts, for the fixed-budget context sweep
+    "batch8-64k": Workload("batch8-64k", 8, (65536,) * 8, 12, 2048, sink_blocks=1, planted=32, seed=3),
+    "batch8-16k": Workload("batch8-16k", 8, (16384,) * 8, 12, 2048, sink_blocks=1, planted=32, seed=3),
     "offload-1m": Workload("offload-1m", 1, (1048576,), 12, 2048, planted=8, kv_host=True, seed=4),
     "offload-1m-hot": Workload("offload-1m-hot", 1, (1048576,), 12, 2048, planted=8, kv_host=True, seed=4,
                                hot_slots=4096, drift=0.25, step_variants=8),

@@ -178,37 +178,4 @@ int synth_fill_kv(uint16_t *dst, int64_t slot0, int64_t n_slots, int64_t row_ele
     return (int)hipGetLastError();
 }
 
-// Not input generation: the bench's streaming-read reference. Workgroup w
-// (256 threads) reads bytes [w * chunk, (w + 1) * chunk) of buf, each lane
-// keeping eight 16-byte non-temporal loads in flight, and folds them into one
-// word per thread (so the loads are not removed). chunk must be a multiple of
-// 256 * 16 * 8 bytes; the grid covers n_wg chunks, all inside buf.
-typedef __attribute__((ext_vector_type(4))) uint32_t stream_u32x4;
-
-__global__ __launch_bounds__(256) void stream_read_kernel(const stream_u32x4 *__restrict__ buf, int64_t chunk_vec,
-                                                          uint32_t *__restrict__ out)
-{
-    const int64_t base = (int64_t)blockIdx.x * chunk_vec;
-    uint32_t acc = 0;
-    for (int64_t i = threadIdx.x; i < chunk_vec; i += 256 * 8) {
-        stream_u32x4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; u++)
-            v[u] = __builtin_nontemporal_load(buf + base + i + u * 256);
-#pragma unroll
-        for (int u = 0; u < 8; u++)
-            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
-}
-
-int synth_stream_read(const void *buf, int64_t n_wg, int64_t chunk_bytes, uint32_t *out, hipStream_t s)
-{
-    if (n_wg <= 0 || chunk_bytes <= 0 || chunk_bytes % (256 * 16 * 8) != 0)
-        return 1;
-    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)n_wg), dim3(256), 0, s, (const stream_u32x4 *)buf,
-                       chunk_bytes / 16, out);
-    return hipGetLastError() == hipSuccess ? 0 : 2;
-}
-
 } // extern "C"

@@ -1,5 +1,4 @@
-"""GPU fill of the large synthetic tensors (index keys, KV pools), and the
-bench's streaming-read reference (stream_read_gbs).
+"""GPU fill of the large synthetic tensors (index keys, KV pools).
 
 Builds ``csrc/synth_fill.hip`` into ``_build/libqsasynth.so`` and fills torch
 device tensors with exactly the bytes that ``qsa_synth`` generates on the
@@ -44,8 +43,6 @@ def _load():
         lib.synth_fill_index.restype = i32
         lib.synth_fill_kv.argtypes = [P, i64, i64, i64, i32, u64, P]
         lib.synth_fill_kv.restype = i32
-        lib.synth_stream_read.argtypes = [P, i64, i64, P, P]
-        lib.synth_stream_read.restype = i32
         _lib = lib
     return _lib
 
@@ -85,31 +82,3 @@ def fill_kv_rows(dst, slot0: int, n_slots: int, layer: int, seed: int, stream=No
                            _stream_ptr(stream))
     if rc != 0:
         raise RuntimeError("synth_fill_kv failed: %d" % rc)
-
-
-def stream_read_gbs(n_bytes: int = 1660944384 // (1 << 20) * (1 << 20), reps: int = 10) -> float:
-    """Not input generation: the bench's streaming-read reference, GB/s of a
-    plain read of an n_bytes device buffer (256 KB per workgroup, eight
-    16-byte loads in flight per lane), timed with events over `reps` reads."""
-    import torch
-    lib = _load()
-    chunk = 256 * 1024
-    n_wg = n_bytes // chunk
-    buf = torch.empty(n_wg * chunk, dtype=torch.uint8, device="cuda")
-    buf.fill_(1)
-    out = torch.empty(n_wg * 256, dtype=torch.int32, device="cuda")
-    s = _stream_ptr(None)
-
-    def run():
-        if lib.synth_stream_read(ctypes.c_void_p(buf.data_ptr()), n_wg, chunk, ctypes.c_void_p(out.data_ptr()), s):
-            raise RuntimeError("synth_stream_read failed")
-
-    for _ in range(3):
-        run()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    return n_wg * chunk * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
