@@ -219,9 +219,11 @@ def build_stream_probe():
     import subprocess
     os.makedirs(os.path.dirname(BENCH_STREAM_LIB), exist_ok=True)
     tmp = BENCH_STREAM_LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", BENCH_STREAM_SRC,
-                           "-o", tmp])
+    r = subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", BENCH_STREAM_SRC, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for bench_stream.hip:\n" + r.stdout + r.stderr)
     os.replace(tmp, BENCH_STREAM_LIB)
     return BENCH_STREAM_LIB
 

@@ -91,12 +91,19 @@ typedef enum {
     QSA_ERR_UNSUPPORTED = 2,        /* geometry other than the compiled one */
     QSA_ERR_WORKSPACE_TOO_SMALL = 3,
     QSA_ERR_HIP = 4,                /* a HIP launch or runtime call failed */
-    QSA_ERR_OUT_OF_SLOTS = 5        /* a slot pool has no free slot left */
+    QSA_ERR_OUT_OF_SLOTS = 5,       /* a slot pool has no free slot left */
+    /* not a status: keeps the type 32 bits wide with every int32 value in its
+     * range, so that a value from outside the list (a caller's bug, or another
+     * language's integer) is well defined and reported as unknown */
+    QSA_STATUS_RANGE_ = 0x7FFFFFFF
 } qsa_status_t;
 
 typedef enum {
     QSA_KV_DEVICE = 0,       /* KV pools in device memory (HBM) */
-    QSA_KV_HOST_PINNED = 1   /* KV pools in pinned host memory, read over PCIe */
+    QSA_KV_HOST_PINNED = 1,  /* KV pools in pinned host memory, read over PCIe */
+    /* not a location: every int32 value is in the type's range, so that an
+     * unknown value is rejected with QSA_ERR_INVALID_ARGUMENT, not undefined */
+    QSA_KV_LOCATION_RANGE_ = 0x7FFFFFFF
 } qsa_kv_location_t;
 
 typedef struct {

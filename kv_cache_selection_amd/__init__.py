@@ -17,7 +17,9 @@ except ImportError:  # pragma: no cover
     torch = None
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqsa.so")
+# QSA_LIBRARY names another build of the same library (the tests' sanitized
+# host build); by default the in-tree libqsa.so is loaded.
+LIB_PATH = os.environ.get("QSA_LIBRARY") or os.path.join(_HERE, "libqsa.so")
 
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE_TOO_SMALL, QSA_ERR_HIP, QSA_ERR_OUT_OF_SLOTS = range(6)
 QSA_KV_DEVICE, QSA_KV_HOST_PINNED = 0, 1

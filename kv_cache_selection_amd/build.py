@@ -1,4 +1,11 @@
-"""Build libqsa.so (the HIP library) in-tree with hipcc for gfx950."""
+"""Build libqsa.so (the HIP library) in-tree with hipcc for gfx950.
+
+``build(sanitize=True)`` builds a second copy, ``_build_san/libqsa.so``, whose
+host code (argument checks, workspace carving, the slot pool, the launch
+sequence) is instrumented with AddressSanitizer and UndefinedBehaviorSanitizer;
+the device code is the same. The CPU tests run against it with clang's ASan
+runtime preloaded (tests/test_sanitized.py); it is never shipped or timed.
+"""
 from __future__ import annotations
 
 import os
@@ -11,6 +18,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqsa.so")
 OBJ_DIR = os.path.join(HERE, "_build")
+SAN_DIR = os.path.join(HERE, "_build_san")
+SAN_OUT = os.path.join(SAN_DIR, "libqsa.so")
+# host-only instrumentation: each sanitizer flag applies to the host pass
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 SOURCES = ["api.hip", "index_score.hip", "select.hip", "gather.hip", "attention.hip", "append.hip", "hotcache.hip", "slots.hip", "multiscore.hip"]
 
 HIPCC = os.environ.get("HIPCC", "hipcc")
@@ -26,9 +38,10 @@ FLAGS = [
 FILE_FLAGS = {"multiscore.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_DIR if sanitize else OBJ_DIR, src.replace(".hip", ".o"))
+    extra = SAN_FLAGS if sanitize else []
+    cmd = [HIPCC, *FLAGS, *extra, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -39,17 +52,18 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(sanitize: bool = False) -> str:
+    out = SAN_OUT if sanitize else OUT
+    os.makedirs(SAN_DIR if sanitize else OBJ_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -338,8 +338,9 @@ const char *qsa_status_string(qsa_status_t s)
         return "HIP runtime error";
     case QSA_ERR_OUT_OF_SLOTS:
         return "slot pool exhausted";
+    default:
+        return "unknown status";
     }
-    return "unknown status";
 }
 
 qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, const uint8_t *idx_keys,

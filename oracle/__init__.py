@@ -22,29 +22,45 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qsa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "libqsa_oracle.so")
+# A copy instrumented with AddressSanitizer and UndefinedBehaviorSanitizer,
+# built with clang so that it shares the ASan runtime of the sanitized host
+# build of libqsa (the CPU tests run both under it, tests/test_sanitized.py).
+SAN_LIB_PATH = os.path.join(_HERE, "_build", "libqsa_oracle_san.so")
+SAN_CC = "/opt/rocm/llvm/bin/clang"
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile qsa_oracle.c with gcc (no fast-math, no FP contraction)."""
-    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call([
-            "gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
-            "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm",
-        ])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile qsa_oracle.c with gcc (no fast-math, no FP contraction); with
+    sanitize, the instrumented copy with clang."""
+    path = SAN_LIB_PATH if sanitize else _LIB_PATH
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp%d" % os.getpid()
+        if sanitize:
+            cmd = [SAN_CC, "-O1", "-g", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+                   "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+                   "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, path)
+    return path
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    if os.environ.get("QSA_ORACLE_SANITIZED") == "1":
+        if not os.path.exists(SAN_LIB_PATH):
+            raise RuntimeError("the sanitized oracle is not built (%s)" % SAN_LIB_PATH)
+        lib = ctypes.CDLL(SAN_LIB_PATH)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.qo_decode_e4m3.argtypes = [ctypes.c_uint8]
