@@ -350,6 +350,7 @@ class HipEvents:
         assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
 
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         assert self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
@@ -762,8 +763,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time spent on the CPU baseline (0: skip)")
     ap.add_argument("--side-streams", type=int, default=None,
-                    help="side streams of the overlapped schedule (default: 1 for pools in HBM, whose schedule uses "
-                         "one; 3 for pools in pinned host memory); 0: every kernel in order on one stream")
+                    help="side streams of the overlapped schedule (default: 1, or 3 with a hot cache); 0: every "
+                         "kernel in order on one stream")
     ap.add_argument("--op", choices=("step", "append", "lease", "multi"), default="step",
                     help="step: the decode step (default); append: the append step alone; lease: slot leases; "
                          "multi: multi-query scoring")
@@ -822,9 +823,10 @@ def main():
     nws = qsa.qsa_workspace_size(cfg, di.batch, di.max_ctx, NL, loc)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    # the second scan stream (HBM pools) or the PCIe gather and per-layer chains (host pools) run on side streams
+    # the second scan stream (HBM pools), the PCIe gather (host pools) or the
+    # per-layer chains (hot cache) run on side streams
     if args.side_streams is None:
-        args.side_streams = 3 if di.kv_host else 1
+        args.side_streams = 3 if wl.hot_slots else 1
     side = [torch.cuda.Stream() for _ in range(args.side_streams)]
     events = qsa.StepEvents(NL, len(side)) if side else None
 
@@ -1012,7 +1014,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 generator; planted relevant blocks)",
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(ctx.max()), "layers": NL,
                    "budget_tokens": wl.budget, "sink_blocks": wl.sink_blocks, "tail_tokens": wl.tail_tokens,
-                   "kv": "host-pinned" if di.kv_host else "hbm", "side_streams": args.side_streams,
+                   "kv": "host-pinned" if di.kv_host else "hbm", "side_streams": len(side),
                    "hot_cache_rows": wl.hot_slots},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -256,16 +256,22 @@ typedef struct {
  *     cache update, miss fetch, attend, merge) runs on stream
  *     l % (n_side + 1) of {compute, side[0], side[1], ...}, with at most two
  *     index scans at a time;
- *   - host pools without a hot cache: per group of up to 16 layers, one
- *     launch each scans, selects, gathers the selected rows over PCIe into
- *     the layers' staging buffers, and attends them, all on `compute` (side
- *     streams are not used).
+ *   - host pools without a hot cache: a pipeline over the layers (digest,
+ *     efficiency section: the copy of a layer's rows overlaps the next
+ *     layer's index scoring). `compute` scores and selects the layers;
+ *     side[0] gathers the selected rows over PCIe into their staging
+ *     buffers as soon as they are selected, back to back;
+ *     `compute` then attends each layer once its rows have arrived. The
+ *     layers go in groups of 1, 2, 4, ... layers (the last takes the rest),
+ *     one launch per group and step, and the gather runs on a few dozen
+ *     workgroups, enough for the PCIe reads, so that the scans beside it
+ *     keep the other CUs. Further side streams are not used.
  * The call leaves `compute` ordered after all of its work, so a sync on
  * `compute` covers the step. Results are bit-identical for every schedule
  * of a call (the attention's split size is chosen once per call, as for
  * qsa_sparse_decode with B x n_layers).
- * Events: the schedules that order several streams (side streams with a hot
- * cache, or with more than 16 layers on HBM pools) record and wait on the
+ * Events: the schedules that order several streams (side streams with host
+ * pools, or with more than 16 layers on HBM pools) record and wait on the
  * events of `events`, a set the caller created with qsa_step_events_create
  * on the current device for at least n_layers layers and n_side side
  * streams; the other schedules need none, and `events` may then be NULL.

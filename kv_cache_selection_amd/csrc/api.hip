@@ -199,9 +199,15 @@ const void *pool_device_ptr(const void *p, qsa_kv_location_t loc)
 }
 
 // The number of events a schedule of qsa_decode_step records: fork and join
-// events plus one per layer (the scans of the hot-cache schedule, the layer
-// groups of the HBM schedule).
+// events plus one or two per layer (the scans of the hot-cache schedule, the
+// layer groups of the HBM schedule, the selections and gathers of the
+// pinned-host pipeline).
 int events_needed(int n_layers, int n_side) { return 3 * n_layers + n_side + 1; }
+
+// Workgroups of the pinned-host pipeline's gathers: 64 x 32 KB of PCIe reads
+// in flight keep the link busy (32 did not; more took CUs from the scans
+// beside them and the step got slower).
+constexpr int kPipeGatherWgs = 64;
 
 } // namespace
 
@@ -570,12 +576,13 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                 return QSA_ERR_INVALID_ARGUMENT;
     }
     // The schedules that order several streams take their events from the
-    // caller's set: the hot-cache schedule, and HBM pools with more layers
-    // than one group. Side streams that a schedule does not use are ignored.
+    // caller's set: the hot-cache schedule, the pinned-host pipeline, and HBM
+    // pools with more layers than one group. Side streams that a schedule
+    // does not use are ignored.
     const bool offload = kv_location == QSA_KV_HOST_PINNED;
     const bool two_streams = n_side > 0;
-    const int NS = (offload && !hot) ? 0 : n_side;
-    const bool needs_events = two_streams && (hot || (!offload && n_layers > kMaxChainLayers));
+    const int NS = (offload && !hot) ? (n_side > 0 ? 1 : 0) : n_side;
+    const bool needs_events = two_streams && (hot || offload || n_layers > kMaxChainLayers);
     const hipEvent_t *ev = nullptr;
     if (needs_events) {
         if (!events || events->max_layers < n_layers || events->max_side < NS ||
@@ -814,19 +821,24 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return hip_status(e);
     }
 
-    // Pools in pinned host memory, side streams allowed: per group of up to
-    // kMaxChainLayers layers, one launch each scans, selects, gathers the
-    // selected rows over PCIe into the layers' own staging buffers, and
-    // attends them. Index scans running beside a gather slow its PCIe reads
-    // far more than they gain, so nothing overlaps the gather: the PCIe reads
-    // of all the group's layers stream in one launch. Everything runs on
-    // the compute stream.
-    for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
-        const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
-        ScoreLayers CL = {};
-        SelectLayers SL = {};
-        GatherLayers GL = {};
-        AttnLayers AL = {};
+    // Pools in pinned host memory, a side stream given: a pipeline over
+    // groups of layers of sizes 1, 2, 4, ... (the last takes the rest). The
+    // compute stream scores and selects group after group (one launch each
+    // per group); the side stream gathers each group's selected rows over
+    // PCIe as soon as that group is selected, one launch per group, back to
+    // back, so that the PCIe reads hardly stop; the compute stream then
+    // attends each group once its rows have arrived. Only the first group's
+    // scan and selection (one layer) and the last group's attention lie
+    // outside the gathers; each group's scan and selection take less time
+    // than the gather of the group before it. The gather runs on
+    // kPipeGatherWgs workgroups, enough for the PCIe reads, so that the scans
+    // beside it keep the other CUs. (Per-layer launches paid a cross-stream
+    // wait of 10-20 us per layer, more than they hid; the gather on a full
+    // grid starved the scans beside it of CUs.)
+    const hipEvent_t *ev_sel = ev + 1 + NS;              // group at l0 selected (compute stream)
+    const hipEvent_t *ev_gat = ev + 1 + NS + n_layers;   // group at l0 gathered (side stream)
+    const hipStream_t sg = (hipStream_t)side[0];
+    auto staged_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, GatherLayers &GL, AttnLayers &AL) {
         CL.flags = flags;
         GL.flags = flags;
         AL.flags = flags;
@@ -857,6 +869,25 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             AL.part_lse[i] = lw[l].aw.part_lse;
             AL.out[i] = Ly.out;
         }
+    };
+    int group_len[QSA_MAX_LAYERS];
+    int n_groups = 0;
+    for (int l0 = 0, want = 1; l0 < n_layers; want *= 2) {
+        const int rest = n_layers - l0;
+        int nl = want < kMaxChainLayers ? want : kMaxChainLayers;
+        nl = nl < rest ? nl : rest;
+        if (rest - nl > 0 && rest - nl < nl && rest <= kMaxChainLayers)
+            nl = rest;                      // a short remainder joins this group
+        group_len[n_groups++] = nl;
+        l0 += nl;
+    }
+    for (int g = 0, l0 = 0; g < n_groups && e == hipSuccess; l0 += group_len[g++]) {
+        const int nl = group_len[g];
+        ScoreLayers CL = {};
+        SelectLayers SL = {};
+        GatherLayers GL = {};
+        AttnLayers AL = {};
+        staged_tables(l0, nl, CL, SL, GL, AL);
         e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B, batch->max_ctx,
                                       bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
                                       (hipEvent_t)layers[l0].score_events[0], (hipEvent_t)layers[l0].score_events[1]);
@@ -864,8 +895,25 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
                                      cfg->tail_tokens, sc);
         if (e == hipSuccess)
+            e = hipEventRecord(ev_sel[l0], sc);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(sg, ev_sel[l0], 0);
+        if (e == hipSuccess)
             e = launch_gather_layers(GL, nl, batch->ctx_len, B, batch->max_ctx, batch->pt_stride, batch->n_slots, K,
-                                     cfg->budget_tokens, sc);
+                                     cfg->budget_tokens, sg, kPipeGatherWgs);
+        if (e == hipSuccess)
+            e = hipEventRecord(ev_gat[l0], sg);
+    }
+    // The compute stream waits for every gather before the call returns, so
+    // the side stream holds no work of this call afterwards.
+    for (int g = 0, l0 = 0; g < n_groups && e == hipSuccess; l0 += group_len[g++]) {
+        const int nl = group_len[g];
+        ScoreLayers CL = {};
+        SelectLayers SL = {};
+        GatherLayers GL = {};
+        AttnLayers AL = {};
+        staged_tables(l0, nl, CL, SL, GL, AL);
+        e = hipStreamWaitEvent(sc, ev_gat[l0], 0);
         if (e == hipSuccess)
             e = launch_attention_layers(false, AL, nl, 0, 0, B, 0, cfg->budget_tokens, cfg->sm_scale,
                                         lw[l0].aw.tps, sc);

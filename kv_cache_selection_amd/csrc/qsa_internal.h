@@ -257,7 +257,7 @@ hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t
 // Row gathers of layers 0 .. n_layers - 1 of L in one launch (grid z = layer).
 hipError_t launch_gather_layers(const GatherLayers &L, int n_layers, const int32_t *ctx_len, int batch, int max_ctx,
                                 int64_t pt_stride, int64_t n_slots, int budget_blocks, int budget_tokens,
-                                hipStream_t s);
+                                hipStream_t s, int max_wgs = 0);
 
 // Attention over staged rows (kv != nullptr) or through the page table.
 hipError_t launch_attention_staged(const uint16_t *q, const void *kv, const int32_t *n_tok, int batch,

@@ -137,14 +137,16 @@ def test_bad_arguments_rejected_before_launch():
 
 
 def test_step_events_required_and_validated():
-    """The schedules that order several streams (a hot cache with side
-    streams, or more than 16 layers on HBM pools with side streams) need a
-    caller-made event set; the library creates no HIP object inside a call."""
+    """The schedules that order several streams (side streams with pools in
+    pinned host memory, with or without a hot cache, or more than 16 layers
+    on HBM pools with side streams) need a caller-made event set; the library
+    creates no HIP object inside a call."""
     cfg = qsa.make_config(256)
     hc = qsa.make_hot_cache(FAKE, FAKE, FAKE, 256)
     lay_hot = qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, hot=hc)
     lay = qsa.make_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
-    for layers, loc in [([lay_hot] * 2, qsa.QSA_KV_HOST_PINNED), ([lay] * 17, qsa.QSA_KV_DEVICE)]:
+    for layers, loc in [([lay_hot] * 2, qsa.QSA_KV_HOST_PINNED), ([lay] * 2, qsa.QSA_KV_HOST_PINNED),
+                        ([lay] * 17, qsa.QSA_KV_DEVICE)]:
         with pytest.raises(qsa.QsaError) as ei:
             qsa.qsa_decode_step(cfg, _batch(), layers, loc, FAKE, 1 << 34, 4096, [8192])
         assert ei.value.status == qsa.QSA_ERR_INVALID_ARGUMENT

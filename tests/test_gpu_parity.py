@@ -536,7 +536,8 @@ def test_decode_step_reports_bad_entries(gpu):
         ws, nws = _ws(cfg, d.batch, d.max_ctx, 2, loc)
         ws.fill_(0x77)
         side = [torch.cuda.Stream() for _ in range(n_side)]
-        qsa.qsa_decode_step(cfg, bt, layers, loc, ws, nws, torch.cuda.current_stream(), side)
+        ev = qsa.StepEvents(2, n_side) if n_side else None
+        qsa.qsa_decode_step(cfg, bt, layers, loc, ws, nws, torch.cuda.current_stream(), side, events=ev)
         qsa.qsa_read_flags(ws, flags)
         torch.cuda.synchronize()
         return int(flags[0]), ns.cpu().numpy()
