@@ -98,7 +98,7 @@ def pmc_summary(paths, workload):
     lines = ["# HBM traffic per dispatch from rocprofv3 counters, workload %s" % workload,
              "# four passes, each its own run (cd /tmp && export TMPDIR=/tmp first), C in FETCH_SIZE WRITE_SIZE:",
              "#   rocprofv3 --pmc C --kernel-trace -f csv -d OUT_C -o run -- python3 bench.py --steps 2 --warmup 1 "
-             "--cpu-seconds 0",
+             "--cpu-seconds 0 --no-sweep",
              "#   rocprofv3 --pmc C --kernel-trace -f csv -d COPY_C -o run -- python3 bench.py --copy-calibration",
              "# summary: python3 bench.py --pmc-summary OUT_FETCH_SIZE/run_counter_collection.csv "
              "OUT_WRITE_SIZE/run_counter_collection.csv COPY_FETCH_SIZE/run_counter_collection.csv "
