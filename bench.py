@@ -357,6 +357,15 @@ class HipEvents:
         assert self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
         return ms.value
 
+    def recorded(self, a, b):
+        """Whether the pair (a, b) has been recorded: the elapsed time of a
+        pair that never was is an error."""
+        ms = ctypes.c_float()
+        ok = self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        if not ok:
+            self.rt.hipGetLastError()            # clear it, so that no later check reports it
+        return ok
+
 
 def tokens_selected(sel, ns, ctx):
     """Tokens covered by each (layer, sequence) selection (host arithmetic)."""
@@ -952,21 +961,26 @@ def main():
         del ws1
 
     # Timed region 3: the headline schedule again, with HIP events around
-    # the scoring launches. With side streams and no hot cache one launch
-    # scans all the layers (up to 16), and the first layer's events time it;
-    # otherwise every layer's scan is a launch of its own.
+    # the scoring launches. A launch that scans a group of layers takes the
+    # events of the group's first layer, so only those are recorded: with
+    # HBM pools one launch scans all the layers (up to 16), the pinned-host
+    # pipeline scans groups of 1, 2, 4, ... layers, and the one-stream
+    # schedule scans layer by layer. The roofline is the scanned bytes over
+    # the scan launches' summed durations.
     hev = HipEvents()
-    grouped = bool(side) and not hot and NL <= 16
     evs = [(hev.create(), hev.create()) for _ in range(NL)]
-    ev_used = evs[:1] if grouped else evs
-    timed = [layers(v, ev_used + [None] * (NL - len(ev_used))) for v in range(NV)]
+    timed = [layers(v, evs) for v in range(NV)]
+    step(timed)                          # which layers lead a scan launch
+    torch.cuda.synchronize()
+    ev_used = [p for p in evs if hev.recorded(*p)]
     durs = []
     for _ in range(args.steps):
         step(timed)
         torch.cuda.synchronize()
-        durs.extend(hev.elapsed_ms(a, b) for (a, b) in ev_used)
-    score_ms = float(np.mean(durs))
-    layers_per_launch = NL if grouped else 1
+        durs.append(sum(hev.elapsed_ms(a, b) for (a, b) in ev_used))
+    n_launch = len(ev_used)
+    score_ms = float(np.mean(durs)) / n_launch             # per launch
+    layers_per_launch = NL / n_launch
 
     # Timed region 4: one-stream steps with events around every per-layer
     # scoring launch (each scan alone, as a kernel-trace profile sees it).
@@ -990,7 +1004,7 @@ def main():
         fetched = tot / NV
 
     idx_bytes_layer = int(ctx.sum()) * g.index_row_bytes
-    idx_bytes_launch = idx_bytes_layer * layers_per_launch
+    idx_bytes_launch = int(round(idx_bytes_layer * layers_per_launch))
     step_bytes = idx_bytes_layer * NL + int(ntok.sum()) * g.row_bytes
     achieved = idx_bytes_launch / (score_ms * 1e-3) / 1e9
     achieved1 = idx_bytes_layer / (score1_ms * 1e-3) / 1e9
@@ -998,7 +1012,7 @@ def main():
     value = NL / (ms_step * 1e-3)
 
     rows_bytes = int(ntok.sum()) * g.row_bytes
-    attn_traffic = read_attn_traffic(wl.name) if grouped else None
+    attn_traffic = read_attn_traffic(wl.name) if n_launch == 1 else None
     result = {
         "metric": metric_for(wl, di.kv_host),
         "value": round(value, 2),
@@ -1019,8 +1033,10 @@ def main():
                    "hot_cache_rows": wl.hot_slots},
         "roofline": {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(wl.name, grouped), "bytes_per_launch": idx_bytes_launch,
-                     "layers_per_launch": layers_per_launch,
+                     "traffic": (read_traffic(wl.name, True) if n_launch == 1 else
+                                 read_traffic(wl.name, False) if n_launch == NL else None),
+                     "bytes_per_launch": idx_bytes_launch,
+                     "layers_per_launch": round(layers_per_launch, 3), "launches_per_step": n_launch,
                      "avg_launch_us": round(score_ms * 1e3, 2)},
         # the per-layer scoring launch of the one-stream step, each launch alone
         "one_stream_score": {"achieved": round(achieved1, 1), "unit": "GB/s",
@@ -1043,8 +1059,8 @@ def main():
         # the attention launch of the headline schedule (all layers in one
         # launch): its algorithmic bytes (the selected rows) and the HBM
         # bytes the counters measured for it (profiles/), when current
-        "attention": {"kernel": ATTN_KERNEL, "layers_per_launch": NL if grouped else 1,
-                      "bytes_per_launch": rows_bytes if grouped else rows_bytes // NL,
+        "attention": {"kernel": ATTN_KERNEL, "layers_per_launch": NL if n_launch == 1 else None,
+                      "bytes_per_launch": rows_bytes if n_launch == 1 else None,
                       "traffic": attn_traffic,
                       "traffic_over_bytes": None if attn_traffic is None else round(attn_traffic / rows_bytes, 4)},
     }
