@@ -19,15 +19,17 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int n_split_of(int budget_tokens) { return (budget_tokens + kTPSMin - 1) / kTPSMin; }
 
-// Byte offsets of the workspace pieces. The flags word and the histograms of
-// every layer come first, contiguous, so one fill kernel clears them all.
+// Byte offsets of the workspace pieces. Nothing in it needs clearing but the
+// flags word, which the first kernel of each call zeroes.
 struct WsLayout {
-    int B = 0, K = 0, n_blk_max = 0, n_slices = 0, n_layers = 0, n_split = 0, budget = 0;
-    size_t flags = 0, hist = 0, zero_bytes = 0;
-    size_t cnt = 0, sdef = 0, scand = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0,
+    int B = 0, K = 0, n_blk_max = 0, n_layers = 0, n_split = 0, budget = 0;
+    ListGeom g = {};
+    bool lists = false;                             // the selection goes through chunk lists
+    size_t flags = 0;
+    size_t heads = 0, lists_off = 0, cand = 0, bs = 0, sel = 0, nsel = 0, ntok = 0, po = 0, plse = 0, stage = 0,
            fetch = 0, nfetch = 0;
-    size_t per_hist = 0, per_cnt = 0, per_sdef = 0, per_scand = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0,
-           per_ntok = 0, per_po = 0, per_plse = 0, per_stage = 0, per_fetch = 0, per_nfetch = 0;
+    size_t per_heads = 0, per_lists = 0, per_cand = 0, per_bs = 0, per_sel = 0, per_nsel = 0, per_ntok = 0,
+           per_po = 0, per_plse = 0, per_stage = 0, per_fetch = 0, per_nfetch = 0;
     size_t total = 0;
 };
 
@@ -38,15 +40,14 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     w.K = cfg->budget_tokens / kBT;
     w.budget = cfg->budget_tokens;
     w.n_blk_max = (max_ctx + kBT - 1) / kBT;
-    w.n_slices = w.n_blk_max > 0 ? (w.n_blk_max + kSliceBlocks - 1) / kSliceBlocks : 1;
     w.n_layers = n_layers;
     w.n_split = n_split_of(cfg->budget_tokens);
+    w.g = list_geom(batch, max_ctx, w.K);
+    w.lists = uses_lists(max_ctx, w.K);
     const size_t nb = (size_t)(w.n_blk_max > 0 ? w.n_blk_max : 1);
-    w.per_hist = align_up((size_t)batch * kHistReps * kHistBins * 4);
-    w.per_cnt = align_up((size_t)batch * w.n_slices * 2 * 4);
-    w.per_sdef = align_up((size_t)batch * w.n_slices * kSliceBlocks * 4);
-    w.per_scand = align_up((size_t)batch * w.n_slices * kSliceBlocks * 8);
-    w.per_cand = align_up((size_t)batch * nb * 8);
+    w.per_heads = w.lists ? align_up((size_t)batch * w.g.n_chunks * 4) : 0;
+    w.per_lists = w.lists ? align_up((size_t)batch * w.g.n_chunks * w.g.cap * 8) : 0;
+    w.per_cand = w.lists ? align_up((size_t)batch * (nb + (size_t)w.g.n_chunks * w.g.cap) * 8) : 0;
     w.per_bs = align_up((size_t)batch * nb * 4);
     w.per_sel = align_up((size_t)batch * w.K * 4);
     w.per_nsel = align_up((size_t)batch * 4);
@@ -60,15 +61,10 @@ WsLayout make_layout(const qsa_config_t *cfg, int batch, int max_ctx, int n_laye
     size_t off = 0;
     w.flags = off;            // one uint32 (QSA_FLAG_*), in its own 256-byte piece
     off += kAlign;
-    w.hist = off;
-    off += w.per_hist * n_layers;
-    w.zero_bytes = off;
-    w.cnt = off;
-    off += w.per_cnt * n_layers;
-    w.sdef = off;
-    off += w.per_sdef * n_layers;
-    w.scand = off;
-    off += w.per_scand * n_layers;
+    w.heads = off;
+    off += w.per_heads * n_layers;
+    w.lists_off = off;
+    off += w.per_lists * n_layers;
     w.cand = off;
     off += w.per_cand * n_layers;
     w.bs = off;
@@ -98,12 +94,10 @@ template <typename T> T *at(void *ws, size_t off) { return reinterpret_cast<T *>
 SelectWs select_ws(void *ws, const WsLayout &w, int l)
 {
     SelectWs s;
-    s.hist = at<uint32_t>(ws, w.hist + w.per_hist * l);
-    s.slot_count = at<uint32_t>(ws, w.cnt + w.per_cnt * l);
-    s.slot_def = at<int32_t>(ws, w.sdef + w.per_sdef * l);
-    s.slot_cand = at<uint64_t>(ws, w.scand + w.per_scand * l);
-    s.spill = at<uint64_t>(ws, w.cand + w.per_cand * l);
-    s.spill_stride = w.n_blk_max > 0 ? w.n_blk_max : 1;
+    s.heads = w.lists ? at<uint32_t>(ws, w.heads + w.per_heads * l) : nullptr;
+    s.lists = w.lists ? at<uint64_t>(ws, w.lists_off + w.per_lists * l) : nullptr;
+    s.spill = w.lists ? at<uint64_t>(ws, w.cand + w.per_cand * l) : nullptr;
+    s.spill_stride = (w.n_blk_max > 0 ? w.n_blk_max : 1) + (int64_t)w.g.n_chunks * w.g.cap;
     s.flags = at<uint32_t>(ws, w.flags);
     s.row0 = nullptr;
     s.n_rows = 0;
@@ -362,9 +356,10 @@ qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         !aligned(idx_scales, 2) || !aligned(q_idx, 16) || !aligned(w_idx, 4) ||
         bs_stride < (batch->max_ctx + kBT - 1) / kBT)
         return QSA_ERR_INVALID_ARGUMENT;
+    const ListGeom g = {};
     return hip_status(launch_index_score(idx_keys, idx_scales, q_idx, w_idx, batch->ctx_len, batch->idx_row0,
-                                         batch->n_idx_rows, batch->batch, batch->max_ctx, token_scores, block_scores, bs_stride,
-                                         nullptr, 0, 0, 0, nullptr, (hipStream_t)stream));
+                                         batch->n_idx_rows, batch->batch, batch->max_ctx, token_scores, block_scores,
+                                         bs_stride, nullptr, nullptr, g, 0, 0, 0, nullptr, (hipStream_t)stream));
 }
 
 qsa_status_t qsa_index_score_multi(const qsa_config_t *cfg, const qsa_batch_t *batch, int32_t n_queries,
@@ -405,12 +400,12 @@ qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return QSA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = (hipStream_t)stream;
     const SelectWs sw = select_ws(workspace, w, 0);
-    hipError_t e = launch_zero_u32(at<uint32_t>(workspace, 0), (int64_t)(w.zero_bytes / 4), s);
+    hipError_t e = launch_zero_u32(at<uint32_t>(workspace, w.flags), 1, s);
+    if (e == hipSuccess && w.lists)
+        e = launch_list_build(block_scores, bs_stride, batch->ctx_len, batch->batch, batch->max_ctx, sw.heads,
+                              sw.lists, w.g, w.K, cfg->sink_blocks, cfg->tail_tokens, s);
     if (e == hipSuccess)
-        e = launch_block_hist(block_scores, bs_stride, batch->ctx_len, batch->batch, batch->max_ctx, sw.hist, w.K,
-                              cfg->sink_blocks, cfg->tail_tokens, s);
-    if (e == hipSuccess)
-        e = launch_select(block_scores, bs_stride, batch->ctx_len, batch->batch, batch->max_ctx, sw, w.K,
+        e = launch_select(block_scores, bs_stride, batch->ctx_len, batch->batch, batch->max_ctx, sw, w.g, w.K,
                           cfg->sink_blocks, cfg->tail_tokens, sel_blocks, n_sel, n_tok, s);
     return hip_status(e);
 }
@@ -639,16 +634,22 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         x.nfetch = offload ? at<int32_t>(workspace, w.nfetch + w.per_nfetch * l) : nullptr;
     }
     uint32_t *const flags = at<uint32_t>(workspace, w.flags);
+    // The first scan of the call clears the flags word (and raises none
+    // itself), unless a fill kernel has done so before it.
+    bool flags_cleared = false;
     auto score = [&](int l, hipStream_t s) {
         const qsa_layer_t &Ly = layers[l];
+        uint32_t *clear = flags_cleared ? nullptr : flags;
+        flags_cleared = true;
         return launch_index_score(Ly.idx_keys, Ly.idx_scales, Ly.q_idx, Ly.w_idx, batch->ctx_len, batch->idx_row0,
-                                  batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.hist, K,
-                                  cfg->sink_blocks, cfg->tail_tokens, flags, s, (hipEvent_t)Ly.score_events[0],
-                                  (hipEvent_t)Ly.score_events[1]);
+                                  batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.heads,
+                                  lw[l].sw.lists, w.g, K, cfg->sink_blocks, cfg->tail_tokens,
+                                  clear ? nullptr : flags, s, (hipEvent_t)Ly.score_events[0],
+                                  (hipEvent_t)Ly.score_events[1], clear);
     };
     auto select = [&](int l, hipStream_t s) {
-        return launch_select(lw[l].bs, bs_stride, batch->ctx_len, B, batch->max_ctx, lw[l].sw, K, cfg->sink_blocks,
-                             cfg->tail_tokens, lw[l].sel, lw[l].nsel, lw[l].ntok, s);
+        return launch_select(lw[l].bs, bs_stride, batch->ctx_len, B, batch->max_ctx, lw[l].sw, w.g, K,
+                             cfg->sink_blocks, cfg->tail_tokens, lw[l].sel, lw[l].nsel, lw[l].ntok, s);
     };
     // Hot cache: update the mapping, fetch the misses over PCIe, then attend
     // the cached rows with the mapping as the page table.
@@ -682,7 +683,13 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                        lw[l].aw, layers[l].out, s);
     };
 
-    hipError_t e = launch_zero_u32(at<uint32_t>(workspace, 0), (int64_t)(w.zero_bytes / 4), sc);
+    hipError_t e = hipSuccess;
+    if (two_streams && (hot || offload)) {
+        // These schedules start work on several streams from an event after
+        // the clear, so the clear is a kernel of its own.
+        e = launch_zero_u32(flags, 1, sc);
+        flags_cleared = true;
+    }
 
     if (!two_streams) {
         // One stream: every layer's kernels in order.
@@ -702,7 +709,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
 
     // The per-layer pointer tables of layers l0 .. l0 + nl - 1 (HBM pools).
     auto hbm_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, AttnLayers &AL) {
-        CL.flags = flags;
+        CL.flags = l0 == 0 ? nullptr : flags;      // the first scan clears the word instead
         AL.flags = flags;
         for (int i = 0; i < nl; i++) {
             const int l = l0 + i;
@@ -712,7 +719,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             CL.q_idx[i] = Ly.q_idx;
             CL.w_idx[i] = Ly.w_idx;
             CL.block_scores[i] = lw[l].bs;
-            CL.hist[i] = lw[l].sw.hist;
+            CL.heads[i] = lw[l].sw.heads;
+            CL.lists[i] = lw[l].sw.lists;
             SL.bs[i] = lw[l].bs;
             SL.ws[i] = lw[l].sw;
             SL.sel[i] = lw[l].sel;
@@ -757,17 +765,17 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             AttnLayers AL = {};
             hbm_tables(l0, nl, CL, SL, AL);
             e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B,
-                                          batch->max_ctx, bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
+                                          batch->max_ctx, bs_stride, w.g, K, cfg->sink_blocks, cfg->tail_tokens, sc,
                                           (hipEvent_t)layers[l0].score_events[0],
-                                          (hipEvent_t)layers[l0].score_events[1]);
+                                          (hipEvent_t)layers[l0].score_events[1], l0 == 0 ? flags : nullptr);
             if (e == hipSuccess && cs != sc) {
                 e = hipEventRecord(ev[1 + NS + l0], sc);
                 if (e == hipSuccess)
                     e = hipStreamWaitEvent(cs, ev[1 + NS + l0], 0);
             }
             if (e == hipSuccess)
-                e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
-                                         cfg->tail_tokens, cs);
+                e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
+                                         cfg->sink_blocks, cfg->tail_tokens, cs);
             if (e == hipSuccess)
                 e = launch_attention_layers(true, AL, nl, batch->pt_stride, batch->max_ctx, B, K,
                                             cfg->budget_tokens, cfg->sm_scale, lw[l0].aw.tps, cs);
@@ -785,8 +793,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         // Hot-cached pinned-host pools: layer l's whole chain (score, select,
         // hot-cache update and fetch, attend, merge) runs on stream
         // l % (NS + 1) of {compute, side...}, after the compute stream has
-        // cleared the histograms. Several chains are in
-        // flight at once, so the latency-bound selection and attention of one
+        // cleared the flags word. Several chains are in flight at once, so the latency-bound selection and attention of one
         // layer, and the ramp and tail of each scan, hide under the index
         // scans of the others. No more than kScansInFlight scans run at once
         // (the scan of layer l waits for that of layer l - kScansInFlight):
@@ -850,7 +857,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             CL.q_idx[i] = Ly.q_idx;
             CL.w_idx[i] = Ly.w_idx;
             CL.block_scores[i] = lw[l].bs;
-            CL.hist[i] = lw[l].sw.hist;
+            CL.heads[i] = lw[l].sw.heads;
+            CL.lists[i] = lw[l].sw.lists;
             SL.bs[i] = lw[l].bs;
             SL.ws[i] = lw[l].sw;
             SL.sel[i] = lw[l].sel;
@@ -889,11 +897,11 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         AttnLayers AL = {};
         staged_tables(l0, nl, CL, SL, GL, AL);
         e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B, batch->max_ctx,
-                                      bs_stride, K, cfg->sink_blocks, cfg->tail_tokens, sc,
+                                      bs_stride, w.g, K, cfg->sink_blocks, cfg->tail_tokens, sc,
                                       (hipEvent_t)layers[l0].score_events[0], (hipEvent_t)layers[l0].score_events[1]);
         if (e == hipSuccess)
-            e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, K, cfg->sink_blocks,
-                                     cfg->tail_tokens, sc);
+            e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
+                                     cfg->sink_blocks, cfg->tail_tokens, sc);
         if (e == hipSuccess)
             e = hipEventRecord(ev_sel[l0], sc);
         if (e == hipSuccess)

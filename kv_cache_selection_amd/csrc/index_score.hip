@@ -25,11 +25,13 @@
 // One launch may scan several layers (grid z), their pointers in the kernel
 // arguments, so that the scan streams from one layer into the next.
 //
-// When the sequence has more blocks than the budget, each workgroup also
-// builds an LDS histogram of the top 12 bits of its blocks' order keys
-// (forced blocks excluded) and adds it to the sequence's global histogram:
-// the first pass of the radix selection, fused here so that the selection
-// never re-reads the scores just to count them.
+// For the long-context selection (sequences with more blocks than the budget
+// and than the one-workgroup selection holds), each workgroup also builds an
+// LDS histogram of the top 12 bits of its blocks' order keys (forced blocks
+// excluded) and from it the chunk's candidate list: its best blocks, cut at a
+// bin boundary (build_chunk_list). The selection then starts from these
+// lists, so nothing needs to be counted across workgroups, and no global
+// histogram has to be cleared before the scan.
 #include "qsa_internal.h"
 
 #include <hip/hip_ext.h>
@@ -42,20 +44,23 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kThreads = 512;                      // 8 waves: half as many histogram clears and flushes
+constexpr int kThreads = 512;                      // 8 waves: half as many histogram clears
 constexpr int kWaveTok = 64;                       // tokens per wave iteration
 constexpr int kWgTok = kThreads / 64 * kWaveTok;   // 512 tokens per workgroup iteration
-constexpr int kMaxChunkTokens = 8192;              // tokens per workgroup, at most
+constexpr int kMaxChunkTokens = kMaxScoreChunkTokens;
+static_assert(kWgTok == kScoreWgTokens, "chunks are whole workgroup iterations");
 
 // Grid (chunks of chunk_tokens, B, layers).
-template <bool kTokens, bool kHist, int N>
+template <bool kTokens, bool kLists, int N>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayersT<N> Ls,
                                                                const int32_t *__restrict__ ctx_len,
                                                                const int64_t *__restrict__ row0, int64_t n_rows,
                                                                int max_ctx, int chunk_tokens, int64_t bs_stride,
-                                                               int budget_blocks, int sink_blocks, int tail_tokens)
+                                                               ListGeom g, int budget_blocks, int sink_blocks,
+                                                               int tail_tokens, uint32_t *clear_flags)
 {
-    __shared__ uint32_t lhist[kHist ? kHistBins : 1];
+    __shared__ uint32_t lhist[kLists ? kHistBins : 1];
+    __shared__ uint32_t lsh[3];                    // highest key bin; list threshold and fill
     // The chunk's block scores, written out at the end as contiguous rows
     // with non-temporal stores. Their 2 MB per layer are 1.5 % of the bytes,
     // but stored from the loop with ordinary stores they slowed the 12-layer
@@ -67,7 +72,12 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     const float *__restrict__ w_idx = Ls.w_idx[blockIdx.z];
     float *__restrict__ token_scores = Ls.token_scores[blockIdx.z];
     float *__restrict__ block_scores = Ls.block_scores[blockIdx.z];
-    uint32_t *__restrict__ hist = Ls.hist[blockIdx.z];
+
+    // The call's flags word is cleared here, before anything of the call can
+    // raise a flag: this launch raises none (the selection reports what it
+    // would), and every later kernel of the call follows it on its stream.
+    if (clear_flags && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+        *clear_flags = 0u;
 
     const int b = blockIdx.y;
     const int64_t r0 = row0[b];
@@ -86,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     if (t_begin >= L)
         return;
     const int n_blk = (L + kBT - 1) / kBT;
-    const bool do_hist = kHist && n_blk > budget_blocks;
+    const bool do_hist = kLists && n_blk > budget_blocks;
     const int tail_first = tail_first_block(L, tail_tokens, n_blk);
 
     const int tid = threadIdx.x;
@@ -122,7 +132,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     if (do_hist) {
         for (int i = tid; i < kHistBins; i += kThreads)
             lhist[i] = 0;
+        if (tid == 0)
+            lsh[0] = 0;
     }
+    uint32_t top = 0;                       // highest key bin of this lane's eligible blocks
 
     // A operands: for group g, lane l (row l&15 of A) holds head (l&3) of the
     // query when (l&15)>>2 == g, else zeros; dims follow the lane's bytes:
@@ -181,8 +194,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
         const int blk = t >> 2;
         if ((lane & 3) == 0 && blk < n_blk) {
             lbs[blk - blk_begin] = s;
-            if (do_hist && blk >= sink_blocks && blk < tail_first)
-                atomicAdd(&lhist[order_key(s) >> kHistShift], 1u);
+            if (do_hist && blk >= sink_blocks && blk < tail_first) {
+                const uint32_t bin = order_key(s) >> kHistShift;
+                atomicAdd(&lhist[bin], 1u);
+                top = bin > top ? bin : top;
+            }
         }
 #pragma unroll
         for (int g = 0; g < 4; g++)
@@ -190,50 +206,65 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
         sc_bits = sc_next;
     }
 
+    if (do_hist) {
+        top = wave_max(top);
+        if (lane == 0)
+            atomicMax(&lsh[0], top);
+    }
     __syncthreads();
     const int blk_end = min(blk_begin + chunk_tokens / kBT, n_blk);
     for (int j = blk_begin + tid; j < blk_end; j += kThreads)
         __builtin_nontemporal_store(lbs[j - blk_begin], bs_row + j);
     if (do_hist) {
-        uint32_t *gh = hist + ((int64_t)b * kHistReps + blockIdx.x % kHistReps) * kHistBins;
-        for (int i = tid; i < kHistBins; i += kThreads) {
-            uint32_t c = lhist[i];
-            if (c)
-                atomicAdd(gh + i, c);
-        }
+        const int64_t c = (int64_t)b * g.n_chunks + blockIdx.x;
+        build_chunk_list<kThreads>(lhist, lbs, blk_begin, blk_end, sink_blocks, tail_first, g.m, g.cap,
+                                   (int)lsh[0], lsh + 1, Ls.heads[blockIdx.z] + c, Ls.lists[blockIdx.z] + c * g.cap);
     }
 }
 
-// Histogram of existing block scores (standalone selection call).
-__global__ __launch_bounds__(kThreads) void block_hist_kernel(const float *__restrict__ block_scores,
+// Chunk lists of existing block scores (standalone selection call): the
+// same lists the scan builds, one workgroup per chunk. Grid (n_chunks, B).
+__global__ __launch_bounds__(kThreads) void list_build_kernel(const float *__restrict__ block_scores,
                                                               int64_t bs_stride, const int32_t *__restrict__ ctx_len,
-                                                              int max_ctx, int chunk_blocks, uint32_t *__restrict__ hist,
-                                                              int budget_blocks, int sink_blocks, int tail_tokens)
+                                                              int max_ctx, ListGeom g, uint32_t *__restrict__ heads,
+                                                              uint64_t *__restrict__ lists, int budget_blocks,
+                                                              int sink_blocks, int tail_tokens)
 {
     __shared__ uint32_t lhist[kHistBins];
+    __shared__ float lbs[kMaxChunkTokens / kBT];
+    __shared__ uint32_t lsh[3];
     const int b = blockIdx.y;
+    const int tid = threadIdx.x;
     const int L = clamp_ctx(ctx_len[b], max_ctx);
     const int n_blk = (L + kBT - 1) / kBT;
-    const int j0 = blockIdx.x * chunk_blocks;
+    const int j0 = blockIdx.x * g.chunk_blocks;
     if (n_blk <= budget_blocks || j0 >= n_blk)
         return;
     const int tail_first = tail_first_block(L, tail_tokens, n_blk);
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
+    const int j1 = min(j0 + g.chunk_blocks, n_blk);
+    for (int i = tid; i < kHistBins; i += kThreads)
         lhist[i] = 0;
+    if (tid == 0)
+        lsh[0] = 0;
     __syncthreads();
     const float *row = block_scores + (int64_t)b * bs_stride;
-    const int j1 = min(j0 + chunk_blocks, n_blk);
-    for (int j = j0 + threadIdx.x; j < j1; j += kThreads) {
-        if (j >= sink_blocks && j < tail_first)
-            atomicAdd(&lhist[order_key(row[j]) >> kHistShift], 1u);
+    uint32_t top = 0;
+    for (int j = j0 + tid; j < j1; j += kThreads) {
+        const float v = row[j];
+        lbs[j - j0] = v;
+        if (j >= sink_blocks && j < tail_first) {
+            const uint32_t bin = order_key(v) >> kHistShift;
+            atomicAdd(&lhist[bin], 1u);
+            top = bin > top ? bin : top;
+        }
     }
+    top = wave_max(top);
+    if ((tid & 63) == 0)
+        atomicMax(&lsh[0], top);
     __syncthreads();
-    uint32_t *gh = hist + ((int64_t)b * kHistReps + blockIdx.x % kHistReps) * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
-        uint32_t c = lhist[i];
-        if (c)
-            atomicAdd(gh + i, c);
-    }
+    const int64_t c = (int64_t)b * g.n_chunks + blockIdx.x;
+    build_chunk_list<kThreads>(lhist, lbs, j0, j1, sink_blocks, tail_first, g.m, g.cap, (int)lsh[0], lsh + 1,
+                               heads + c, lists + c * g.cap);
 }
 
 __global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n)
@@ -288,23 +319,24 @@ void launch_timed(Kernel k, dim3 grid, hipStream_t s, hipEvent_t ev0, hipEvent_t
 template <int N>
 static hipError_t launch_score_n(const ScoreLayersT<N> &L, int n_layers, const int32_t *ctx_len,
                                  const int64_t *row0, int64_t n_rows, int batch, int max_ctx, int64_t bs_stride,
-                                 int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s, hipEvent_t ev0,
-                                 hipEvent_t ev1)
+                                 const ListGeom &g, int budget_blocks, int sink_blocks, int tail_tokens,
+                                 hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, uint32_t *clear_flags)
 {
-    // Tokens per workgroup: a multiple of 512, grown while the grid keeps
-    // at least 512 workgroups (2 per CU, 16 waves) per layer so every CU streams.
-    int chunk = kWgTok;
-    while (chunk < kMaxChunkTokens && (int64_t)batch * ((max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 512)
-        chunk *= 2;
-    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)batch, (unsigned)n_layers);
-#define QSA_SCORE_ARGS L, ctx_len, row0, n_rows, max_ctx, chunk, bs_stride, budget_blocks, sink_blocks, tail_tokens
+    const int chunk = score_chunk_tokens(batch, max_ctx);
+    const int n_chunks = (max_ctx + chunk - 1) / chunk;
+    if (L.heads[0] && (g.chunk_blocks * kBT != chunk || g.n_chunks != n_chunks || n_chunks > kMaxListChunks ||
+                       g.m < 1 || g.m > g.cap || g.cap > kListCap))
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)n_chunks, (unsigned)batch, (unsigned)n_layers);
+#define QSA_SCORE_ARGS \
+    L, ctx_len, row0, n_rows, max_ctx, chunk, bs_stride, g, budget_blocks, sink_blocks, tail_tokens, clear_flags
     if (L.token_scores[0]) {
-        if (L.hist[0])
+        if (L.heads[0])
             launch_timed(index_score_kernel<true, true, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
         else
             launch_timed(index_score_kernel<true, false, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
     } else {
-        if (L.hist[0])
+        if (L.heads[0])
             launch_timed(index_score_kernel<false, true, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
         else
             launch_timed(index_score_kernel<false, false, N>, grid, s, ev0, ev1, QSA_SCORE_ARGS);
@@ -314,30 +346,40 @@ static hipError_t launch_score_n(const ScoreLayersT<N> &L, int n_layers, const i
 }
 
 hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const int32_t *ctx_len, const int64_t *row0,
-                                     int64_t n_rows, int batch, int max_ctx, int64_t bs_stride, int budget_blocks,
-                                     int sink_blocks, int tail_tokens, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
+                                     int64_t n_rows, int batch, int max_ctx, int64_t bs_stride, const ListGeom &g,
+                                     int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s,
+                                     hipEvent_t ev0, hipEvent_t ev1, uint32_t *clear_flags)
 {
-    if (n_layers < 1 || n_layers > kMaxChainLayers)
+    if (n_layers < 1 || n_layers > kMaxChainLayers || (clear_flags && L.flags))
         return hipErrorInvalidValue;
-    if (max_ctx <= 0)
+    if (max_ctx <= 0) {
+        // nothing to scan: the flags word is still cleared for the call
+        if (clear_flags)
+            return launch_zero_u32(clear_flags, 1, s);
         return hipSuccess;
+    }
     for (int l = 1; l < n_layers; l++)
-        if (!L.token_scores[l] != !L.token_scores[0] || !L.hist[l] != !L.hist[0])
+        if (!L.token_scores[l] != !L.token_scores[0] || !L.heads[l] != !L.heads[0] ||
+            (L.heads[l] && !L.lists[l]))
             return hipErrorInvalidValue;
+    if (L.heads[0] && !L.lists[0])
+        return hipErrorInvalidValue;
     if (n_layers > 1)
-        return launch_score_n(L, n_layers, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks,
-                              sink_blocks, tail_tokens, s, ev0, ev1);
+        return launch_score_n(L, n_layers, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, g, budget_blocks,
+                              sink_blocks, tail_tokens, s, ev0, ev1, clear_flags);
     const ScoreLayersT<1> L1 = {{L.keys[0]},         {L.scales[0]},       {L.q_idx[0]}, {L.w_idx[0]},
-                                {L.token_scores[0]}, {L.block_scores[0]}, {L.hist[0]},  L.flags};
-    return launch_score_n(L1, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks, sink_blocks,
-                          tail_tokens, s, ev0, ev1);
+                                {L.token_scores[0]}, {L.block_scores[0]}, {L.heads[0]}, {L.lists[0]},
+                                L.flags};
+    return launch_score_n(L1, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, g, budget_blocks, sink_blocks,
+                          tail_tokens, s, ev0, ev1, clear_flags);
 }
 
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
-                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, uint32_t *flags,
-                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1)
+                              uint32_t *heads, uint64_t *lists, const ListGeom &g, int budget_blocks,
+                              int sink_blocks, int tail_tokens, uint32_t *flags, hipStream_t s, hipEvent_t ev0,
+                              hipEvent_t ev1, uint32_t *clear_flags)
 {
     ScoreLayers L = {};
     L.flags = flags;
@@ -347,22 +389,25 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
     L.w_idx[0] = w_idx;
     L.token_scores[0] = token_scores;
     L.block_scores[0] = block_scores;
-    L.hist[0] = hist;
-    return launch_index_score_layers(L, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, budget_blocks,
-                                     sink_blocks, tail_tokens, s, ev0, ev1);
+    L.heads[0] = heads;
+    L.lists[0] = lists;
+    return launch_index_score_layers(L, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, g, budget_blocks,
+                                     sink_blocks, tail_tokens, s, ev0, ev1, clear_flags);
 }
 
-hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
-                             int max_ctx, uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
-                             hipStream_t s)
+hipError_t launch_list_build(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
+                             int max_ctx, uint32_t *heads, uint64_t *lists, const ListGeom &g, int budget_blocks,
+                             int sink_blocks, int tail_tokens, hipStream_t s)
 {
     const int n_blk_max = (max_ctx + kBT - 1) / kBT;
     if (n_blk_max <= 0)
         return hipSuccess;
-    const int chunk = 4096;
-    dim3 grid((unsigned)((n_blk_max + chunk - 1) / chunk), (unsigned)batch);
-    hipLaunchKernelGGL(block_hist_kernel, grid, dim3(kThreads), 0, s, block_scores, bs_stride, ctx_len, max_ctx,
-                       chunk, hist, budget_blocks, sink_blocks, tail_tokens);
+    if (g.chunk_blocks < 1 || g.chunk_blocks > kMaxChunkTokens / kBT || g.n_chunks > kMaxListChunks ||
+        (int64_t)g.n_chunks * g.chunk_blocks < n_blk_max || g.m < 1 || g.m > g.cap || g.cap > kListCap)
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)g.n_chunks, (unsigned)batch);
+    hipLaunchKernelGGL(list_build_kernel, grid, dim3(kThreads), 0, s, block_scores, bs_stride, ctx_len, max_ctx, g,
+                       heads, lists, budget_blocks, sink_blocks, tail_tokens);
     return hipGetLastError();
 }
 

@@ -27,10 +27,6 @@ constexpr int kMaxCtx = 1 << 21;               // tokens per sequence
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
-// Each sequence's histogram is kept in kHistReps copies; scoring workgroup x
-// adds into copy x % kHistReps, so that no more than 1/kHistReps of a
-// sequence's workgroups queue up on the same counter. Readers sum the copies.
-constexpr int kHistReps = 2;
 
 // Attention: tokens per split. A call whose kTPS-token splits number at
 // least three quarters of the device's CUs uses splits of kTPS tokens;
@@ -79,16 +75,75 @@ __device__ __forceinline__ int forced_count(int n_blk, int sink, int tail_first)
     return s + (n_blk > t0 ? n_blk - t0 : 0);
 }
 
-// Per-layer pieces of the caller's workspace, carved on the host.
-constexpr int kSliceBlocks = 2048;             // blocks per selection slice (one collect workgroup)
+// Scoring chunks: tokens per scoring workgroup, a multiple of 512 grown
+// while the grid keeps at least 512 workgroups (2 per CU, 16 waves) per
+// layer, so every CU streams. At most kMaxScoreChunkTokens; the result gives
+// fewer than 1024 chunks per sequence for any batch and max_ctx <= kMaxCtx.
+constexpr int kScoreWgTokens = 512;
+constexpr int kMaxScoreChunkTokens = 8192;
+inline int score_chunk_tokens(int batch, int max_ctx)
+{
+    int chunk = kScoreWgTokens;
+    while (chunk < kMaxScoreChunkTokens &&
+           (int64_t)batch * (((int64_t)max_ctx + 2 * chunk - 1) / (2 * chunk)) >= 512)
+        chunk *= 2;
+    return chunk;
+}
+
+// Candidate lists of the long-context selection. Each scoring chunk of a
+// sequence keeps, from its own block scores, the eligible blocks whose key
+// lies in the top histogram bins: the smallest such set of at least m
+// blocks, or, when the bin that reaches m would take the list past cap
+// entries, the blocks above that bin only. The selection kernel then works on
+// the union of the lists, and re-reads only chunks whose whole list it took
+// (their next blocks could still belong to the answer).
+constexpr int kListCap = 128;                  // entries per chunk list, at most
+constexpr int kMaxListChunks = 1024;           // chunks per sequence (one selection thread each)
+struct ListGeom {
+    int chunk_blocks;    // blocks per chunk
+    int n_chunks;        // chunks per sequence (row stride of the headers)
+    int m;               // entries a list aims at
+    int cap;             // entries a list may hold (row stride of the lists)
+};
+// m is about three times a chunk's share of the budget, at least 4: a chunk
+// whose share of the answer reaches m is rare unless the scores cluster.
+// cap = 2 m leaves room for the blocks that share the m-th block's bin.
+inline ListGeom list_geom(int batch, int max_ctx, int budget_blocks)
+{
+    ListGeom g;
+    g.chunk_blocks = score_chunk_tokens(batch, max_ctx) / kBT;
+    const int n_blk = (max_ctx + kBT - 1) / kBT;
+    g.n_chunks = n_blk > 0 ? (n_blk + g.chunk_blocks - 1) / g.chunk_blocks : 1;
+    int m = (int)((3 * (int64_t)budget_blocks + g.n_chunks - 1) / g.n_chunks);
+    m = m < 4 ? 4 : (m > kListCap / 2 ? kListCap / 2 : m);
+    g.m = m;
+    g.cap = 2 * m;
+    return g;
+}
+// Sequences of at most this many blocks are selected by one workgroup
+// holding every score (select_one_kernel); longer ones go through the lists.
+constexpr int kOneMaxBlocks = 16384;
+
+// Header of a chunk list: entry count (bits 0-15); threshold bin (bits
+// 16-28): the list holds exactly the chunk's eligible blocks whose key bin is
+// at least this; bit 31: the list holds every eligible block of the chunk.
+constexpr uint32_t kListComplete = 1u << 31;
+__device__ __forceinline__ uint32_t list_count(uint32_t h) { return h & 0xFFFFu; }
+__device__ __forceinline__ uint32_t list_bin(uint32_t h) { return (h >> 16) & 0x1FFFu; }
+
+// Block j with order key k as a 64-bit composite: unique per block, and
+// ordered like (score descending, block index ascending).
+__device__ __forceinline__ uint64_t composite(uint32_t key, int j)
+{
+    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+__device__ __forceinline__ int composite_block(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
 
 struct SelectWs {
-    uint32_t *hist;        // [B][kHistReps][kHistBins], zeroed before scoring
-    uint32_t *slot_count;  // [B][n_slices][2] per-slice list lengths (definite, candidates)
-    int32_t *slot_def;     // [B][n_slices][kSliceBlocks] blocks above the threshold bin
-    uint64_t *slot_cand;   // [B][n_slices][kSliceBlocks] blocks inside the threshold bin
-    uint64_t *spill;       // [B][spill_stride] candidates past the finish kernel's LDS
-    int64_t spill_stride;
+    uint32_t *heads;       // [B][n_chunks] chunk list headers (long-context route)
+    uint64_t *lists;       // [B][n_chunks][cap] chunk lists: composites
+    uint64_t *spill;       // [B][spill_stride] pool entries past the selection kernel's LDS
+    int64_t spill_stride;  // n_chunks * cap + blocks of the longest sequence
     uint32_t *flags;       // the call's flags word (QSA_FLAG_*), or null
     // The index rows of the batch (qsa_decode_step): a sequence whose rows
     // [row0[b], row0[b] + L) fall outside [0, n_rows) was scored as empty, and
@@ -129,7 +184,8 @@ struct ScoreLayersT {
     const float *w_idx[N];                // [B][kIdxH]
     float *token_scores[N];               // [rows] or null
     float *block_scores[N];               // [B][bs_stride]
-    uint32_t *hist[N];                    // [B][kHistReps][kHistBins] or null
+    uint32_t *heads[N];                   // chunk list headers, or null (no lists)
+    uint64_t *lists[N];                   // chunk lists
     uint32_t *flags;                      // the call's flags word, or null
 };
 using ScoreLayers = ScoreLayersT<kMaxChainLayers>;
@@ -205,6 +261,147 @@ __device__ inline uint32_t block_inclusive_scan(uint32_t v, uint32_t *sh /* [NT 
     return v + off;
 }
 
+// Walk a histogram of NT * W bins from the top: the bin where the running
+// count first reaches `want`, the count strictly above it and the count in
+// it (outputs untouched when the whole histogram holds fewer than `want`).
+// Thread i holds bins W (NT - 1 - i) .. + W - 1 in hv, so thread 0 holds the
+// top ones. Returns the histogram's total.
+template <int W, int NT>
+__device__ uint32_t crossing_of(const uint32_t (&hv)[W], uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
+                                uint32_t *above_out, uint32_t *in_bin_out = nullptr)
+{
+    const int tr = NT - 1 - threadIdx.x;
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < W; i++)
+        local += hv[i];
+    uint32_t total;
+    uint32_t above = block_inclusive_scan<NT>(local, sh_scan, &total) - local;
+#pragma unroll
+    for (int i = W - 1; i >= 0; i--) {
+        if (above < want && above + hv[i] >= want) {
+            *bin_out = W * tr + i;
+            *above_out = above;
+            if (in_bin_out)
+                *in_bin_out = hv[i];
+        }
+        above += hv[i];
+    }
+    __syncthreads();
+    return total;
+}
+
+// The same over a histogram in memory.
+template <int W, int NT>
+__device__ void find_crossing(const uint32_t *h, uint32_t want, uint32_t *sh_scan, uint32_t *bin_out,
+                              uint32_t *above_out, uint32_t *in_bin_out = nullptr)
+{
+    const int tr = NT - 1 - threadIdx.x;
+    uint32_t hv[W];
+#pragma unroll
+    for (int i = 0; i < W; i++)
+        hv[i] = h[W * tr + i];
+    crossing_of<W, NT>(hv, want, sh_scan, bin_out, above_out, in_bin_out);
+}
+
+// Largest value of v over the wave.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t o = __shfl_xor(v, d);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// One chunk's candidate list (see ListGeom), built by the NT threads of a
+// workgroup from its LDS histogram `lhist` of the eligible blocks' key bins
+// (top_bin: the highest bin that holds one) and its LDS copy `lbs` of the
+// chunk's block scores (blocks blk_begin .. blk_end - 1; eligible: el_begin
+// <= j < el_end). Call after a barrier that completes lhist and lbs; the
+// other waves' stores do not wait for the search. Wave 0 finds the bin where
+// the count from the top reaches m, 64 bins at a time from top_bin (one
+// step, unless the chunk's scores spread over more than 64 bins); then every
+// thread places its eligible blocks at or above the list's threshold bin.
+// Writes the header and the entries (in no particular order). `sh` is two
+// words of LDS.
+template <int NT>
+__device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int blk_begin, int blk_end, int el_begin,
+                                 int el_end, int m, int cap, int top_bin, uint32_t *sh, uint32_t *head_out,
+                                 uint64_t *list_out)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int lo = blk_begin > el_begin ? blk_begin : el_begin;
+    const int hi = blk_end < el_end ? blk_end : el_end;
+    const uint32_t n_el = hi > lo ? (uint32_t)(hi - lo) : 0u;
+    if (tid < 64) {
+        uint32_t theta = 0, size = n_el;
+        bool complete = true;
+        if (n_el >= (uint32_t)m) {
+            uint32_t carry = 0;
+            for (int hb = top_bin; hb >= 0; hb -= 64) {        // uniform in the wave
+                const int bin = hb - lane;                      // lane 0: the highest bin of the window
+                const uint32_t h = bin >= 0 ? lhist[bin] : 0u;
+                uint32_t incl = h;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t o = __shfl_up(incl, d);
+                    if (lane >= d)
+                        incl += o;
+                }
+                incl += carry;
+                const uint64_t hit = __ballot(incl >= (uint32_t)m);
+                if (hit) {
+                    const int f = __ffsll((unsigned long long)hit) - 1;
+                    const uint32_t cum = __shfl(incl, f);
+                    const uint32_t in_bin = __shfl(h, f);
+                    if (cum <= (uint32_t)cap) {
+                        theta = (uint32_t)(hb - f);
+                        size = cum;
+                        complete = cum == n_el;
+                    } else {                                    // the crossing bin would overflow
+                        theta = (uint32_t)(hb - f + 1);
+                        size = cum - in_bin;
+                        complete = false;
+                    }
+                    break;
+                }
+                carry = __shfl(incl, 63);
+            }
+        }
+        if (size > (uint32_t)cap) {                             // never, with lhist consistent
+            size = (uint32_t)cap;
+            complete = false;
+        }
+        if (tid == 0) {
+            sh[0] = theta;
+            sh[1] = 0;
+            *head_out = size | (theta << 16) | (complete ? kListComplete : 0u);
+        }
+    }
+    __syncthreads();
+    const uint32_t theta = sh[0];
+    for (int j0 = blk_begin; j0 < blk_end; j0 += NT) {
+        const int j = j0 + tid;
+        uint32_t key = 0;
+        bool in = false;
+        if (j < blk_end && j >= el_begin && j < el_end) {
+            key = order_key(lbs[j - blk_begin]);
+            in = (key >> kHistShift) >= theta;
+        }
+        const uint64_t bal = __ballot(in);
+        uint32_t base = 0;
+        if (lane == 0 && bal)
+            base = atomicAdd(&sh[1], (uint32_t)__popcll(bal));
+        base = __shfl(base, 0);
+        const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (in && pos < (uint32_t)cap)
+            list_out[pos] = composite(key, j);
+    }
+}
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
 // Eight e4m3 codes (two dwords, lowest byte first) -> eight bf16 (exact). The
@@ -224,31 +421,46 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1)
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 hipError_t launch_copy_u32(const uint32_t *src, uint32_t *dst, int64_t n, hipStream_t s);
 
+// True when a call's selection goes through the chunk lists (sequences
+// longer than the one-workgroup route, and longer than the budget).
+inline bool uses_lists(int max_ctx, int budget_blocks)
+{
+    const int n_blk = (max_ctx + kBT - 1) / kBT;
+    return n_blk > budget_blocks && n_blk > kOneMaxBlocks;
+}
+
+// Index scoring of one layer. heads/lists null: no chunk lists.
 hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const uint16_t *q_idx,
                               const float *w_idx, const int32_t *ctx_len, const int64_t *row0, int64_t n_rows,
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
-                              uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens, uint32_t *flags,
-                              hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                              uint32_t *heads, uint64_t *lists, const ListGeom &g, int budget_blocks,
+                              int sink_blocks, int tail_tokens, uint32_t *flags, hipStream_t s,
+                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, uint32_t *clear_flags = nullptr);
 
 // Index scoring of layers 0 .. n_layers - 1 of L in one launch (grid z =
-// layer); token_scores and hist must be null for all layers or for none.
+// layer); token_scores and heads must be null for all layers or for none.
+// clear_flags non-null: the launch first zeroes that flags word, and raises
+// no flag itself (L.flags must then be null; the selection raises what the
+// scan would have).
 hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const int32_t *ctx_len, const int64_t *row0,
-                                     int64_t n_rows, int batch, int max_ctx, int64_t bs_stride, int budget_blocks,
-                                     int sink_blocks, int tail_tokens, hipStream_t s, hipEvent_t ev0 = nullptr,
-                                     hipEvent_t ev1 = nullptr);
+                                     int64_t n_rows, int batch, int max_ctx, int64_t bs_stride, const ListGeom &g,
+                                     int budget_blocks, int sink_blocks, int tail_tokens, hipStream_t s,
+                                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr,
+                                     uint32_t *clear_flags = nullptr);
 
-hipError_t launch_block_hist(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
-                             int max_ctx, uint32_t *hist, int budget_blocks, int sink_blocks, int tail_tokens,
-                             hipStream_t s);
+// Chunk lists built from existing block scores (standalone selection call).
+hipError_t launch_list_build(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
+                             int max_ctx, uint32_t *heads, uint64_t *lists, const ListGeom &g, int budget_blocks,
+                             int sink_blocks, int tail_tokens, hipStream_t s);
 
 hipError_t launch_select(const float *block_scores, int64_t bs_stride, const int32_t *ctx_len, int batch,
-                         int max_ctx, const SelectWs &ws, int budget_blocks, int sink_blocks, int tail_tokens,
-                         int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s);
+                         int max_ctx, const SelectWs &ws, const ListGeom &g, int budget_blocks, int sink_blocks,
+                         int tail_tokens, int32_t *sel, int32_t *n_sel, int32_t *n_tok, hipStream_t s);
 
 // Selection of layers 0 .. n_layers - 1 of L (n_layers <= kMaxChainLayers).
 hipError_t launch_select_layers(const SelectLayers &L, int n_layers, int64_t bs_stride, const int32_t *ctx_len,
-                                int batch, int max_ctx, int budget_blocks, int sink_blocks, int tail_tokens,
-                                hipStream_t s);
+                                int batch, int max_ctx, const ListGeom &g, int budget_blocks, int sink_blocks,
+                                int tail_tokens, hipStream_t s);
 
 hipError_t launch_gather(const int32_t *sel, const int32_t *n_sel, const int32_t *ctx_len, int batch, int max_ctx,
                          const int32_t *pt, int64_t pt_stride, int64_t n_slots, const void *pool, void *out, int budget_blocks,

@@ -128,15 +128,15 @@ def _topk(budget, sink, tail, bs_rows, lens):
         assert nt[b] == len(oracle.tokens_of_blocks(L, ref)), (b, L)
 
 
-# 1,048,576 tokens fill exactly one 262,144-block segment of the finish
+# 1,048,576 tokens fill exactly one 262,144-block segment of the selection
 # kernel's output bitmap; one token more starts a second segment; 2,097,152
 # tokens is the longest context the library accepts (two full segments).
 LONG = [1048576, 1048577, 2097152]
 
 
-@pytest.mark.parametrize("kind", ["random", "ties", "constant", "two-values"])
+@pytest.mark.parametrize("kind", ["random", "ties", "constant", "two-values", "clustered"])
 def test_topk_exact_at_1m_and_2m_tokens(gpu, kind):
-    rng = np.random.default_rng({"random": 31, "ties": 32, "constant": 33, "two-values": 34}[kind])
+    rng = np.random.default_rng({"random": 31, "ties": 32, "constant": 33, "two-values": 34, "clustered": 35}[kind])
     lens = LONG + [4 * 512 + 3, 300001]
     n_max = (max(lens) + 3) // 4
     if kind == "random":
@@ -146,6 +146,10 @@ def test_topk_exact_at_1m_and_2m_tokens(gpu, kind):
         bs = rng.integers(0, 50, size=(len(lens), n_max)).astype(np.float32)
     elif kind == "constant":
         bs = np.full((len(lens), n_max), 3.5, np.float32)
+    elif kind == "clustered":                  # the answer crowded into a few chunks
+        bs = rng.standard_normal((len(lens), n_max)).astype(np.float32)
+        bs[:, 40000:41500] += 30.0
+        bs[:, 270000:270400] += 25.0
     else:
         bs = np.full((len(lens), n_max), 3.5, np.float32)
         bs[:, 1::2] = np.nextafter(np.float32(3.5), np.float32(10))

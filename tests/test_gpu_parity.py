@@ -216,7 +216,7 @@ def _check_topk_exact(bs_rows, lens, budget, sink=0, tail=0):
 
 # Longest context of the case picks the route: the one-kernel selection with 2
 # or 16 scores per thread (up to 8,192 and 65,536 tokens, both ends of the
-# second), and the collect + finish kernels past that.
+# second), and the chunk lists with the pool selection past that.
 @pytest.mark.parametrize("max_len", [8000, 40000, 65536, 65536 + 1, 262144, 262144 + 4 * 2048 + 1])
 def test_topk_exact_random_and_ties(gpu, max_len):
     rng = np.random.default_rng(5 + max_len)
@@ -236,8 +236,9 @@ def test_topk_exact_random_and_ties(gpu, max_len):
 
 @pytest.mark.parametrize("max_len", [6000, 60000, 262144, 280000])
 def test_topk_exact_degenerate_constant_scores(gpu, max_len):
-    """All scores equal: every block lands in one histogram bin, the candidate
-    list is the whole sequence (radix path), and ties break by index."""
+    """All scores equal: every block lands in one histogram bin, so on the
+    list route every chunk list is cut short and every chunk is re-read; ties
+    break by index."""
     lens = [max_len, 9000, 4 * 512 + 1]
     n_max = (max(lens) + 3) // 4
     bs = np.full((3, n_max), 3.5, np.float32)
@@ -245,6 +246,30 @@ def test_topk_exact_degenerate_constant_scores(gpu, max_len):
     bs2 = np.full((3, n_max), 3.5, np.float32)
     bs2[:, 1::2] = np.nextafter(np.float32(3.5), np.float32(10))     # two adjacent values
     _check_topk_exact(bs2, lens, 2048, tail=64)
+
+
+@pytest.mark.parametrize("max_len", [70001, 262144 + 4 * 2048 + 1])
+def test_topk_exact_clustered_scores(gpu, max_len):
+    """The answer crowded into a few chunks: their lists (m entries each) are
+    wholly chosen, so the pool selection must re-read those chunks; also a
+    boost that leaves lists short of the crossing bin, and sequences where
+    most of the answer sits in one chunk."""
+    rng = np.random.default_rng(7 + max_len)
+    lens = [max_len, max_len - 12345, 4 * 512 + 3, 100003]
+    n_max = (max(lens) + 3) // 4
+    for trial in range(4):
+        bs = rng.standard_normal((len(lens), n_max)).astype(np.float32)
+        if trial == 0:                          # one dense run of high scores
+            bs[:, 5000:7000] += 20.0
+        elif trial == 1:                        # several runs in different chunks
+            for a in (1000, 9000, 17000):
+                bs[:, a:a + 300] += 8.0 + rng.standard_normal((len(lens), 300)).astype(np.float32)
+        elif trial == 2:                        # a run of equal top scores inside one chunk
+            bs[:, 3000:3900] = 50.0
+        else:                                   # rising scores: the last chunks hold the answer
+            bs += np.linspace(0.0, 40.0, n_max, dtype=np.float32)[None, :]
+        for budget, sink, tail in ((2048, 1, 0), (8192, 0, 64), (64, 0, 0)):
+            _check_topk_exact(bs, lens, budget, sink=sink, tail=tail)
 
 
 def test_topk_exact_small_budget_many_candidates(gpu):
@@ -368,7 +393,7 @@ def _check_step_units(di, sel, ns, out, units):
 
 
 # The longest context picks the selection route: the one-kernel selection
-# (65,536 tokens) or collect + finish (70,001).
+# (65,536 tokens) or the chunk lists (70,001).
 @pytest.mark.parametrize("longest", [65536, 70001])
 def test_decode_step_edge_lengths(gpu, longest):
     """A batch of edge lengths through the whole step: an empty sequence, one
