@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
                                                                int tail_tokens, uint32_t *clear_flags)
 {
     __shared__ uint32_t lhist[kLists ? kHistBins : 1];
-    __shared__ uint32_t lsh[3];                    // highest key bin; list threshold and fill
+    __shared__ uint32_t lsh[4];                    // highest key bin; list threshold, fill and size
     // The chunk's block scores, written out at the end as contiguous rows
     // with non-temporal stores. Their 2 MB per layer are 1.5 % of the bytes,
     // but stored from the loop with ordinary stores they slowed the 12-layer
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void list_build_kernel(const float *__res
 {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ float lbs[kMaxChunkTokens / kBT];
-    __shared__ uint32_t lsh[3];
+    __shared__ uint32_t lsh[4];
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int L = clamp_ctx(ctx_len[b], max_ctx);
@@ -325,7 +325,7 @@ static hipError_t launch_score_n(const ScoreLayersT<N> &L, int n_layers, const i
     const int chunk = score_chunk_tokens(batch, max_ctx);
     const int n_chunks = (max_ctx + chunk - 1) / chunk;
     if (L.heads[0] && (g.chunk_blocks * kBT != chunk || g.n_chunks != n_chunks || n_chunks > kMaxListChunks ||
-                       g.m < 1 || g.m > g.cap || g.cap > kListCap))
+                       g.m < 1 || g.m > g.cap || g.cap > kListCap || g.cap > kThreads))
         return hipErrorInvalidValue;
     dim3 grid((unsigned)n_chunks, (unsigned)batch, (unsigned)n_layers);
 #define QSA_SCORE_ARGS \
@@ -403,7 +403,8 @@ hipError_t launch_list_build(const float *block_scores, int64_t bs_stride, const
     if (n_blk_max <= 0)
         return hipSuccess;
     if (g.chunk_blocks < 1 || g.chunk_blocks > kMaxChunkTokens / kBT || g.n_chunks > kMaxListChunks ||
-        (int64_t)g.n_chunks * g.chunk_blocks < n_blk_max || g.m < 1 || g.m > g.cap || g.cap > kListCap)
+        (int64_t)g.n_chunks * g.chunk_blocks < n_blk_max || g.m < 1 || g.m > g.cap || g.cap > kListCap ||
+        g.cap > kThreads)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)g.n_chunks, (unsigned)batch);
     hipLaunchKernelGGL(list_build_kernel, grid, dim3(kThreads), 0, s, block_scores, bs_stride, ctx_len, max_ctx, g,

@@ -107,7 +107,8 @@ struct ListGeom {
 };
 // m is about three times a chunk's share of the budget, at least 4: a chunk
 // whose share of the answer reaches m is rare unless the scores cluster.
-// cap = 2 m leaves room for the blocks that share the m-th block's bin.
+// cap = 2 m leaves room for the blocks that share the m-th block's bin; a
+// crowded bin cuts the list short instead.
 inline ListGeom list_geom(int batch, int max_ctx, int budget_blocks)
 {
     ListGeom g;
@@ -324,8 +325,10 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v)
 // the count from the top reaches m, 64 bins at a time from top_bin (one
 // step, unless the chunk's scores spread over more than 64 bins); then every
 // thread places its eligible blocks at or above the list's threshold bin.
-// Writes the header and the entries (in no particular order). `sh` is two
-// words of LDS.
+// Writes the header and the entries (in no particular order), and 0 in the
+// list's unused slots, so that a reader can tell entries from empty slots by
+// their value (no block's composite is 0). `sh` is three words of LDS. NT >=
+// cap.
 template <int NT>
 __device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int blk_begin, int blk_end, int el_begin,
                                  int el_end, int m, int cap, int top_bin, uint32_t *sh, uint32_t *head_out,
@@ -378,11 +381,14 @@ __device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int bl
         if (tid == 0) {
             sh[0] = theta;
             sh[1] = 0;
+            sh[2] = size;
             *head_out = size | (theta << 16) | (complete ? kListComplete : 0u);
         }
     }
     __syncthreads();
     const uint32_t theta = sh[0];
+    if (tid >= (int)sh[2] && tid < cap)
+        list_out[tid] = 0ull;
     for (int j0 = blk_begin; j0 < blk_end; j0 += NT) {
         const int j = j0 + tid;
         uint32_t key = 0;

@@ -213,11 +213,12 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 // Grid (B, layers). The pool holds every list slot of the sequence, chunk c's
 // at positions c * cap .. c * cap + cap - 1, so that the headers and all slots
 // come in one round of loads issued before the length is known; empty slots
-// hold 0, which is below every block's composite (a composite is 0 only for
-// key 0 and index 2^32 - 1). Blocks added by the re-read follow at n_chunks *
-// cap. In the common case (no chunk to re-read) the output bitmap is marked
-// from the registers that brought the lists, in the pass that checks the
-// chunks.
+// hold 0 (the scan writes 0 past each list; slots of chunks past the
+// sequence are ignored), which is below every block's composite (a composite
+// is 0 only for key 0 and index 2^32 - 1), so a slot's value tells whether
+// it holds an entry. Blocks added by the re-read follow at n_chunks * cap. In
+// the common case (no chunk to re-read) the output bitmap is marked from the
+// registers that brought the lists, in the pass that checks the chunks.
 template <int N>
 __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayersT<N> Ls, int64_t bs_stride,
                                                                const int32_t *__restrict__ ctx_len, int max_ctx,
@@ -321,21 +322,19 @@ __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayer
     uint32_t C = E;                                 // pool positions in use
     bool seg0_marked = false;                       // bitmap segment 0 holds the answer
     if (r > 0) {
-        // ---- the pool: valid slots of the sequence's chunks, 0 elsewhere ----
+        // ---- the pool: entries of the sequence's chunks, 0 elsewhere; its
+        //      size and extremes, all from the slots' values ----------------
         if (tid < NCH)
             head[tid] = tid < nc ? hd : 0u;
-        const uint32_t cw = wave_sum(tid < nc ? min(list_count(hd), (uint32_t)cap) : 0u);
-        if (lane == 0 && cw)
-            atomicAdd(&sh_p, cw);
-        __syncthreads();
-        const uint32_t P = sh_p;
-        uint64_t lmax = 0ull, lmin = ~0ull;         // this thread's valid entries
+        const uint32_t E_seq = (uint32_t)(nc * cap);   // slots of this sequence's chunks
+        uint64_t lmax = 0ull, lmin = ~0ull;         // this thread's entries
+        uint32_t cnt = 0;
         auto place = [&](uint32_t p, uint64_t x) -> bool {
-            const uint32_t c = p / (uint32_t)cap;
-            const bool valid = p - c * (uint32_t)cap < min(list_count(head[c]), (uint32_t)cap);
+            const bool valid = p < E_seq && x != 0ull;
             if (valid) {
                 lmax = x > lmax ? x : lmax;
                 lmin = x < lmin ? x : lmin;
+                cnt++;
             }
             put(p, valid ? x : 0ull);
             return valid;
@@ -349,6 +348,7 @@ __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayer
         }
         for (uint32_t p = kCandCap + tid; p < E; p += kThreads)   // more slots than the LDS pool holds
             place(p, lists_b[p]);
+        const uint32_t cw = wave_sum(cnt);
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) {
             const uint64_t omax = __shfl_xor(lmax, d), omin = __shfl_xor(lmin, d);
@@ -356,10 +356,13 @@ __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayer
             lmin = omin < lmin ? omin : lmin;
         }
         if (lane == 0) {
+            if (cw)
+                atomicAdd(&sh_p, cw);
             atomicMax(reinterpret_cast<unsigned long long *>(&vext[0]), (unsigned long long)lmax);
             atomicMin(reinterpret_cast<unsigned long long *>(&vext[1]), (unsigned long long)lmin);
         }
         __syncthreads();
+        const uint32_t P = sh_p;
 
         // ---- T_U = the pool's r-th largest (every list entry if the pool has
         //      fewer than r). Then, in one pass over the entries: a list with

@@ -113,7 +113,7 @@ def cases():
             s = rng.standard_normal(n) * 1e-3 + 1.0
         n_chunks = (n + cb - 1) // cb
         m = max(4, min(64, (3 * K + n_chunks - 1) // n_chunks))
-        cap = 2 * m if trial % 3 else int(rng.choice([m, 128]))
+        cap = 2 * m if trial % 3 else int(rng.choice([m, m + 2, 128]))
         yield np.asarray(s, np.float32), L, K, sink, tail, tail_first, cb, m, cap
 
 
