@@ -262,7 +262,7 @@ typedef struct {
  *     side[0] gathers the selected rows over PCIe into their staging
  *     buffers as soon as they are selected, back to back;
  *     `compute` then attends each layer once its rows have arrived. The
- *     layers go in groups of 1, 2, 4, ... layers (the last takes the rest),
+ *     layers go in groups of 1, 3, 9, ... layers (the last takes the rest),
  *     one launch per group and step, and the gather runs on a few dozen
  *     workgroups, enough for the PCIe reads, so that the scans beside it
  *     keep the other CUs. Further side streams are not used.

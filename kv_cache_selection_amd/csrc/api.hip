@@ -684,9 +684,11 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     };
 
     hipError_t e = hipSuccess;
-    if (two_streams && (hot || offload)) {
-        // These schedules start work on several streams from an event after
-        // the clear, so the clear is a kernel of its own.
+    if (two_streams && hot) {
+        // This schedule starts scans on several streams from an event after
+        // the clear, so the clear is a kernel of its own. (The pinned-host
+        // pipeline starts its side stream after the first group's selection,
+        // so its first scan clears the word.)
         e = launch_zero_u32(flags, 1, sc);
         flags_cleared = true;
     }
@@ -829,7 +831,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     }
 
     // Pools in pinned host memory, a side stream given: a pipeline over
-    // groups of layers of sizes 1, 2, 4, ... (the last takes the rest). The
+    // groups of layers of sizes 1, 3, 9, ... (the last takes the rest). The
     // compute stream scores and selects group after group (one launch each
     // per group); the side stream gathers each group's selected rows over
     // PCIe as soon as that group is selected, one launch per group, back to
@@ -837,7 +839,10 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     // attends each group once its rows have arrived. Only the first group's
     // scan and selection (one layer) and the last group's attention lie
     // outside the gathers; each group's scan and selection take less time
-    // than the gather of the group before it. The gather runs on
+    // than the gather of the group before it (a layer's scan and selection
+    // take about 25 us, its gather about 75 us, so a group may be three
+    // times the one before; every further group costs a cross-stream
+    // hand-over of about 12 us between two gathers). The gather runs on
     // kPipeGatherWgs workgroups, enough for the PCIe reads, so that the scans
     // beside it keep the other CUs. (Per-layer launches paid a cross-stream
     // wait of 10-20 us per layer, more than they hid; the gather on a full
@@ -846,7 +851,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     const hipEvent_t *ev_gat = ev + 1 + NS + n_layers;   // group at l0 gathered (side stream)
     const hipStream_t sg = (hipStream_t)side[0];
     auto staged_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, GatherLayers &GL, AttnLayers &AL) {
-        CL.flags = flags;
+        CL.flags = l0 == 0 ? nullptr : flags;      // the first scan clears the word instead
         GL.flags = flags;
         AL.flags = flags;
         for (int i = 0; i < nl; i++) {
@@ -880,7 +885,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     };
     int group_len[QSA_MAX_LAYERS];
     int n_groups = 0;
-    for (int l0 = 0, want = 1; l0 < n_layers; want *= 2) {
+    for (int l0 = 0, want = 1; l0 < n_layers; want *= 3) {
         const int rest = n_layers - l0;
         int nl = want < kMaxChainLayers ? want : kMaxChainLayers;
         nl = nl < rest ? nl : rest;
@@ -898,7 +903,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         staged_tables(l0, nl, CL, SL, GL, AL);
         e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B, batch->max_ctx,
                                       bs_stride, w.g, K, cfg->sink_blocks, cfg->tail_tokens, sc,
-                                      (hipEvent_t)layers[l0].score_events[0], (hipEvent_t)layers[l0].score_events[1]);
+                                      (hipEvent_t)layers[l0].score_events[0], (hipEvent_t)layers[l0].score_events[1],
+                                      l0 == 0 ? flags : nullptr);
         if (e == hipSuccess)
             e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
                                      cfg->sink_blocks, cfg->tail_tokens, sc);
