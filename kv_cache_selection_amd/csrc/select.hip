@@ -514,8 +514,8 @@ __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayer
                     }
                 }
             }
-        }
-        __syncthreads();
+            __syncthreads();
+        }                                           // (else: marked before the needy count's barrier)
         if (tid == 0 && n - 1 >= seg0 && n - 1 < seg1)
             sh_u[6] = (bm[(n - 1 - seg0) >> 5] >> ((n - 1 - seg0) & 31)) & 1u;
         // ordered compaction: thread t owns words [t*per, (t+1)*per)
