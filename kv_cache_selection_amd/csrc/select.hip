@@ -55,7 +55,6 @@ constexpr int kCoarse = 64;                        // coarse bins of a digit his
 constexpr int kPerCoarse = kDigitBins / kCoarse;   // 32 digits each
 static_assert(kMaxListChunks <= kThreads, "one selection thread per chunk");
 
-
 // Number of non-forced blocks to take, or -1 when every block fits.
 __device__ __forceinline__ int rest_to_take(int L, int n, int K, int sink_blocks, int tail_tokens, int *tail_first)
 {
@@ -63,20 +62,6 @@ __device__ __forceinline__ int rest_to_take(int L, int n, int K, int sink_blocks
         return -1;
     *tail_first = tail_first_block(L, tail_tokens, n);
     return K - forced_count(n, sink_blocks, *tail_first);   // host guarantees >= 0
-}
-
-// Index of the chunk whose [off[s], off[s+1]) range holds p (off ascending, off[0] = 0).
-__device__ __forceinline__ int slot_of(const uint32_t *off, int ns, uint32_t p)
-{
-    int lo = 0, hi = ns - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= p)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
 }
 
 // Wave 0 of a workgroup: the bin of a kDigitBins-bin histogram h where the
