@@ -149,7 +149,9 @@ qsa_status_t qsa_index_score(const qsa_config_t *cfg, const qsa_batch_t *batch, 
  *   sel_blocks i32 [B][K] ascending, -1 padded;  n_sel i32 [B];
  *   n_tok      i32 [B] tokens covered by the selection, or NULL.
  * Exact: the same selection as a full sort by (score desc, index asc); -0.0
- * and +0.0 compare equal. Needs qsa_workspace_size(cfg, B, max_ctx, 1, QSA_KV_DEVICE)
+ * and +0.0 compare equal, +-inf are ordinary values; NaN scores have no
+ * defined rank (the selection stays in bounds, its choice among them is
+ * unspecified). Needs qsa_workspace_size(cfg, B, max_ctx, 1, QSA_KV_DEVICE)
  * bytes of workspace (any content; 256-byte aligned). QSA_ERR_INVALID_ARGUMENT
  * if the forced blocks could exceed the budget. */
 qsa_status_t qsa_topk_blocks(const qsa_config_t *cfg, const qsa_batch_t *batch, const float *block_scores,

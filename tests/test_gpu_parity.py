@@ -272,6 +272,24 @@ def test_topk_exact_clustered_scores(gpu, max_len):
             _check_topk_exact(bs, lens, budget, sink=sink, tail=tail)
 
 
+@pytest.mark.parametrize("max_len", [40000, 262144 + 4 * 2048 + 1])
+def test_topk_exact_infinite_scores(gpu, max_len):
+    """Rows as multi-query scoring leaves them for an early query (-inf past
+    the visible blocks), +inf and -inf mixed in, and a row of -inf only: on
+    the list route, chunks of -inf alone give empty lists, the pool holds
+    fewer than r entries, and every incomplete chunk is re-read."""
+    rng = np.random.default_rng(11 + max_len)
+    lens = [max_len, max_len - 777, 4 * 512 + 3, 50001]
+    n_max = (max(lens) + 3) // 4
+    bs = rng.standard_normal((len(lens), n_max)).astype(np.float32)
+    bs[0, 300:] = -np.inf                                   # visible: the first 300 blocks
+    bs[1, rng.random(n_max) < 0.1] = np.inf
+    bs[1, rng.random(n_max) < 0.3] = -np.inf
+    bs[3, :] = -np.inf
+    for budget, sink, tail in ((2048, 1, 0), (2048, 0, 64), (64, 0, 0)):
+        _check_topk_exact(bs, lens, budget, sink=sink, tail=tail)
+
+
 def test_topk_exact_small_budget_many_candidates(gpu):
     rng = np.random.default_rng(6)
     lens = [60000, 123457]
