@@ -263,11 +263,13 @@ typedef struct {
  *     layer's index scoring). `compute` scores and selects the layers;
  *     side[0] gathers the selected rows over PCIe into their staging
  *     buffers as soon as they are selected, back to back;
- *     `compute` then attends each layer once its rows have arrived. The
+ *     `compute` attends the layers once the last rows have arrived. The
  *     layers go in groups of 1, 3, 9, ... layers (the last takes the rest),
  *     one launch per group and step, and the gather runs on a few dozen
  *     workgroups, enough for the PCIe reads, so that the scans beside it
- *     keep the other CUs. Further side streams are not used.
+ *     keep the other CUs. side[0] waits for each group's selection on the
+ *     event set's signal (a stream memory operation), `compute` for the last
+ *     gather on one of its events. Further side streams are not used.
  * The call leaves `compute` ordered after all of its work, so a sync on
  * `compute` covers the step. Results are bit-identical for every schedule
  * of a call (the attention's split size is chosen once per call, as for
@@ -293,11 +295,15 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                              size_t workspace_bytes, qsa_stream_t compute, const qsa_stream_t *side,
                              int32_t n_side, qsa_step_events_t *events);
 
-/* The HIP events that order the streams of qsa_decode_step's overlapped
- * schedules, created here (outside any hot path) on the current device, for
- * calls of up to max_layers layers and max_side side streams. Not itself
- * thread-safe: one set per host thread that issues overlapped steps.
- * QSA_ERR_HIP if HIP cannot create the events (nothing is then kept). */
+/* The HIP events and the signal that order the streams of qsa_decode_step's
+ * overlapped schedules, created here (outside any hot path) on the current
+ * device, for calls of up to max_layers layers and max_side side streams.
+ * The signal is 8 bytes of signal memory (hipExtMallocWithFlags with
+ * hipMallocSignalMemory), set to 0 here with a stream write on the null
+ * stream, which this call then synchronises; each pinned-host pipeline step
+ * writes it with values that only grow. Not itself thread-safe: one set per
+ * host thread that issues overlapped steps. QSA_ERR_HIP if HIP cannot create
+ * the events or the signal (nothing is then kept). */
 qsa_status_t qsa_step_events_create(int32_t max_layers, int32_t max_side, qsa_step_events_t **events);
 void qsa_step_events_destroy(qsa_step_events_t *events);
 

@@ -247,11 +247,15 @@ void *static_scratch(qsa_status_t *err)
 
 } // namespace
 
-// The caller's event set (qsa_step_events_create).
+// The caller's event set (qsa_step_events_create): HIP events, and one signal
+// (signal memory, written and waited on by stream memory operations) with the
+// last value written to it.
 struct qsa_step_events {
     int device;
     int max_layers, max_side;
     std::vector<hipEvent_t> ev;
+    uint64_t *signal = nullptr;
+    uint64_t epoch = 0;
 };
 
 extern "C" {
@@ -280,6 +284,17 @@ qsa_status_t qsa_step_events_create(int32_t max_layers, int32_t max_side, qsa_st
         }
         e->ev.push_back(h);
     }
+    // A fresh signal holds 1, so it is set to 0 before its first use; the
+    // values written later count up from there.
+    if (hipExtMallocWithFlags((void **)&e->signal, sizeof(uint64_t), hipMallocSignalMemory) != hipSuccess) {
+        e->signal = nullptr;
+        qsa_step_events_destroy(e);
+        return QSA_ERR_HIP;
+    }
+    if (hipStreamWriteValue64(nullptr, e->signal, 0, 0) != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess) {
+        qsa_step_events_destroy(e);
+        return QSA_ERR_HIP;
+    }
     *events = e;
     return QSA_OK;
 }
@@ -290,6 +305,8 @@ void qsa_step_events_destroy(qsa_step_events_t *events)
         return;
     for (hipEvent_t h : events->ev)
         (void)hipEventDestroy(h);
+    if (events->signal)
+        (void)hipFree(events->signal);
     delete events;
 }
 
@@ -835,20 +852,23 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     // compute stream scores and selects group after group (one launch each
     // per group); the side stream gathers each group's selected rows over
     // PCIe as soon as that group is selected, one launch per group, back to
-    // back, so that the PCIe reads hardly stop; the compute stream then
-    // attends each group once its rows have arrived. Only the first group's
-    // scan and selection (one layer) and the last group's attention lie
-    // outside the gathers; each group's scan and selection take less time
-    // than the gather of the group before it (a layer's scan and selection
-    // take about 25 us, its gather about 75 us, so a group may be three
-    // times the one before; every further group costs a cross-stream
-    // hand-over of about 12 us between two gathers). The gather runs on
-    // kPipeGatherWgs workgroups, enough for the PCIe reads, so that the scans
-    // beside it keep the other CUs. (Per-layer launches paid a cross-stream
-    // wait of 10-20 us per layer, more than they hid; the gather on a full
-    // grid starved the scans beside it of CUs.)
-    const hipEvent_t *ev_sel = ev + 1 + NS;              // group at l0 selected (compute stream)
-    const hipEvent_t *ev_gat = ev + 1 + NS + n_layers;   // group at l0 gathered (side stream)
+    // back, so that the PCIe reads hardly stop; once the last gather is done
+    // the compute stream attends all layers. Only the first group's scan and
+    // selection (one layer) and the attention lie outside the gathers; each
+    // group's scan and selection take less time than the gather of the group
+    // before it (a layer's scan and selection take about 25 us, its gather
+    // about 75 us, so a group may be three times the one before). The gather
+    // runs on kPipeGatherWgs workgroups, enough for the PCIe reads, so that
+    // the scans beside it keep the other CUs. (Per-layer launches paid a
+    // cross-stream wait of 10-20 us per layer, more than they hid; the gather
+    // on a full grid starved the scans beside it of CUs.)
+    // Hand-overs: the compute stream writes the set's signal after each
+    // group's selection and the side stream waits for that value (a wait
+    // that is reached first ends about 5 us after the write, an event about
+    // 10 us after its record). The side stream records no event between its
+    // gathers (a record after a kernel delays the stream's next kernel by
+    // 3-5 us), only after the last one, for which the compute stream waits on
+    // an event: a signal wait held that long sometimes ended 180 us late.
     const hipStream_t sg = (hipStream_t)side[0];
     auto staged_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, GatherLayers &GL, AttnLayers &AL) {
         CL.flags = l0 == 0 ? nullptr : flags;      // the first scan clears the word instead
@@ -908,29 +928,35 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         if (e == hipSuccess)
             e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
                                      cfg->sink_blocks, cfg->tail_tokens, sc);
-        if (e == hipSuccess)
-            e = hipEventRecord(ev_sel[l0], sc);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(sg, ev_sel[l0], 0);
+        // the side stream's wait is enqueued only once its value's write is
+        if (e == hipSuccess) {
+            const uint64_t value = events->epoch + 1;
+            e = hipStreamWriteValue64(sc, events->signal, value, 0);
+            if (e == hipSuccess) {
+                events->epoch = value;
+                e = hipStreamWaitValue64(sg, events->signal, value, hipStreamWaitValueGte, ~0ull);
+            }
+        }
         if (e == hipSuccess)
             e = launch_gather_layers(GL, nl, batch->ctx_len, B, batch->max_ctx, batch->pt_stride, batch->n_slots, K,
                                      cfg->budget_tokens, sg, kPipeGatherWgs);
-        if (e == hipSuccess)
-            e = hipEventRecord(ev_gat[l0], sg);
     }
-    // The compute stream waits for every gather before the call returns, so
-    // the side stream holds no work of this call afterwards.
-    for (int g = 0, l0 = 0; g < n_groups && e == hipSuccess; l0 += group_len[g++]) {
-        const int nl = group_len[g];
+    // The compute stream waits for the last gather (and with it every one
+    // before it on the side stream), so the side stream holds no work of this
+    // call afterwards; then it attends the layers, up to a group's worth of
+    // layers per launch.
+    if (e == hipSuccess)
+        e = hipEventRecord(ev[0], sg);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(sc, ev[0], 0);
+    for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
+        const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
         ScoreLayers CL = {};
         SelectLayers SL = {};
         GatherLayers GL = {};
         AttnLayers AL = {};
         staged_tables(l0, nl, CL, SL, GL, AL);
-        e = hipStreamWaitEvent(sc, ev_gat[l0], 0);
-        if (e == hipSuccess)
-            e = launch_attention_layers(false, AL, nl, 0, 0, B, 0, cfg->budget_tokens, cfg->sm_scale,
-                                        lw[l0].aw.tps, sc);
+        e = launch_attention_layers(false, AL, nl, 0, 0, B, 0, cfg->budget_tokens, cfg->sm_scale, lw[l0].aw.tps, sc);
     }
     return hip_status(e);
 }

@@ -466,6 +466,44 @@ def test_decode_step_deterministic_and_offload_bit_exact(gpu):
         assert np.array_equal(out1, out3), n_side
 
 
+def test_decode_step_offload_reuses_one_event_set(gpu):
+    """One event set and one side stream serve several pinned-host pipeline
+    calls in a row, as in a decode loop: the set's signal carries a larger
+    value at every hand-over. The queries change between the calls, so a
+    gather that started before its group's selection had been written would
+    copy the previous call's rows; every call must give the one-stream bits
+    of its own inputs."""
+    wl = S.WORKLOADS["batch8-short"]
+    dh = DeviceInputs(wl, gpu, layers=5, kv_host=True)
+    perm = torch.roll(torch.arange(dh.batch, device="cuda"), 1)
+    states = [(dh.q_idx.clone(), dh.q.clone()), (dh.q_idx[:, perm].clone(), dh.q[:, perm].clone())]
+    ref = []
+    for qi, q in states:
+        dh.q_idx.copy_(qi)
+        dh.q.copy_(q)
+        ref.append(_step(dh, n_side=0))
+    assert not np.array_equal(ref[0][0], ref[1][0])
+    cfg = _cfg(wl)
+    K = wl.budget // 4
+    L = dh.n_layers
+    ws, nws = _ws(cfg, dh.batch, dh.max_ctx, L, qsa.QSA_KV_HOST_PINNED)
+    side = [torch.cuda.Stream()]
+    ev = qsa.StepEvents(L, 1)
+    for i in (0, 1, 1, 0, 1, 0):
+        dh.q_idx.copy_(states[i][0])
+        dh.q.copy_(states[i][1])
+        sel = torch.full((L, dh.batch, K), -7, dtype=torch.int32, device="cuda")
+        ns = torch.zeros((L, dh.batch), dtype=torch.int32, device="cuda")
+        layers = [qsa.make_layer(dh.keys[l], dh.scales[l], dh.q_idx[l], dh.w_idx[l], dh.q[l], dh.pool[l],
+                                 dh.out[l], None, sel[l], ns[l]) for l in range(L)]
+        qsa.qsa_decode_step(cfg, _batch(dh), layers, qsa.QSA_KV_HOST_PINNED, ws, nws,
+                            torch.cuda.current_stream(), side, events=ev)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), ref[i][0]), i
+        assert np.array_equal(ns.cpu().numpy(), ref[i][1]), i
+        assert np.array_equal(dh.out.cpu().numpy(), ref[i][2]), i
+
+
 def test_decode_step_more_layers_than_one_group(gpu):
     """The overlapped schedules scan, select and attend up to 16 layers per
     launch; 18 layers take two groups (16 + 2), and every schedule, with the
