@@ -20,7 +20,10 @@ Prints one JSON line with the driver's fields plus:
   step_hbm      the whole step's algorithmic bytes (index scan + gathered
                 rows) over the step time, against the same HBM peak;
   cpu_baseline  the CPU oracle, single-threaded, on a sample of (layer,
-                sequence) units of the same workload, scaled to layer-steps/s.
+                sequence) units of the same workload, scaled to layer-steps/s;
+  cold_cache    (HBM pools) steps timed one by one, each after reading a
+                separate 512 MiB buffer, against the back-to-back steps: what
+                the steps gain from data left in the 256 MB Infinity Cache.
 
 The roofline's "traffic" comes from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 summarised in profiles/ (see --pmc-summary); it is reported only while the
@@ -50,6 +53,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 STEP_TARGET_FRAC = 0.70       # the whole step's index-scan + gather traffic, as a fraction of HBM peak
 DRIFT = 0.25                  # indexer-query noise of the drifting region
+COLD_FLUSH_BYTES = 512 << 20  # read before each step of the cold-cache region (Infinity Cache: 256 MB)
 DRIFT_VARIANTS = 8
 PCIE_PEAK_GBS = 64.0          # PCIe 5.0 x16, one direction
 SCORE_KERNEL = "index_score_kernel"
@@ -925,6 +929,30 @@ def main():
                             "attention queries; the variants are cycled, so consecutive steps select overlapping "
                             "but different blocks"}
 
+    # Timed region 1c (HBM workloads): each step timed alone after a read of
+    # COLD_FLUSH_BYTES of another buffer, twice the 256 MB Infinity Cache, so
+    # that nothing an earlier step read is left in it. Against region 1's
+    # per-step times this shows what the steps gain from that cache.
+    cold = None
+    if not di.kv_host:
+        flush = torch.ones(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        n_cold = min(args.steps, 20)
+        ev_c = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+        sink = torch.zeros((), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for i in range(n_cold):
+            sink += flush.sum()
+            ev_c[i][0].record(stream)
+            step(plain)
+            ev_c[i][1].record(stream)
+        torch.cuda.synchronize()
+        per_cold = [a.elapsed_time(b) for a, b in ev_c]
+        del flush
+        cold = {"step_ms": step_percentiles(per_cold), "flush_bytes": COLD_FLUSH_BYTES,
+                "median_over_warm": round(float(np.median(per_cold) / np.median(per_step)), 4),
+                "note": "each step timed alone after reading a separate buffer of flush_bytes (twice the "
+                        "Infinity Cache); median_over_warm compares with the back-to-back steps of step_ms"}
+
     # Timed region 2: the same steps with every kernel in order on one stream (each layer's
     # score -> select -> attention -> merge before the next layer starts).
     ms_serial = None
@@ -1066,6 +1094,8 @@ def main():
     }
     if drifting is not None:
         result["drifting"] = drifting
+    if cold is not None:
+        result["cold_cache"] = cold
     if di.kv_host:
         # every gathered row crosses PCIe once per step (with a hot cache: the misses only)
         pcie_bytes = int(ntok.sum()) * g.row_bytes if fetched is None else int(round(fetched)) * g.row_bytes
