@@ -99,24 +99,31 @@ inline int score_chunk_tokens(int batch, int max_ctx)
 // (their next blocks could still belong to the answer).
 constexpr int kListCap = 128;                  // entries per chunk list, at most
 constexpr int kMaxListChunks = 1024;           // chunks per sequence (one selection thread each)
+constexpr int kPoolSlots = 8192;               // list slots the selection holds in LDS (more spill)
 struct ListGeom {
     int chunk_blocks;    // blocks per chunk
     int n_chunks;        // chunks per sequence (row stride of the headers)
     int m;               // entries a list aims at
     int cap;             // entries a list may hold (row stride of the lists)
 };
-// m is about three times a chunk's share of the budget, at least 4: a chunk
-// whose share of the answer reaches m is rare unless the scores cluster.
-// cap = 2 m leaves room for the blocks that share the m-th block's bin; a
-// crowded bin cuts the list short instead.
+// m is about three times a chunk's share of the budget, and at least 8 where
+// every chunk's cap = 2 m slots still fit the selection's LDS pool (else at
+// least 4): a chunk whose share of the answer reaches m is then rare unless
+// the scores cluster. (With a share of one block, as at 1M tokens in 512
+// chunks, a floor of 4 left one to nine chunks per sequence and layer to be
+// re-read: the share is about Poisson, and five or more of 512 chunks hold at
+// least five of the answer's blocks on average.) cap = 2 m leaves room for
+// the blocks that share the m-th block's bin; a crowded bin cuts the list
+// short instead.
 inline ListGeom list_geom(int batch, int max_ctx, int budget_blocks)
 {
     ListGeom g;
     g.chunk_blocks = score_chunk_tokens(batch, max_ctx) / kBT;
     const int n_blk = (max_ctx + kBT - 1) / kBT;
     g.n_chunks = n_blk > 0 ? (n_blk + g.chunk_blocks - 1) / g.chunk_blocks : 1;
+    const int m_floor = (int64_t)g.n_chunks * 16 <= kPoolSlots ? 8 : 4;
     int m = (int)((3 * (int64_t)budget_blocks + g.n_chunks - 1) / g.n_chunks);
-    m = m < 4 ? 4 : (m > kListCap / 2 ? kListCap / 2 : m);
+    m = m < m_floor ? m_floor : (m > kListCap / 2 ? kListCap / 2 : m);
     g.m = m;
     g.cap = 2 * m;
     return g;

@@ -44,7 +44,7 @@ namespace qsa {
 namespace {
 
 constexpr int kThreads = 1024;                     // pool_select_kernel
-constexpr int kCandCap = 8192;                     // pool entries held in LDS (64 KB)
+constexpr int kCandCap = kPoolSlots;               // pool entries held in LDS (64 KB)
 constexpr int kLoadBatch = 4;                      // re-read loads a thread keeps in flight per round
 constexpr int kSegBlocks = 1 << 18;                // bitmap segment (32 KB of LDS)
 constexpr int kSegWords = kSegBlocks / 32;
