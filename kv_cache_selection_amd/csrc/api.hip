@@ -101,6 +101,10 @@ SelectWs select_ws(void *ws, const WsLayout &w, int l)
     s.flags = at<uint32_t>(ws, w.flags);
     s.row0 = nullptr;
     s.n_rows = 0;
+    s.keys = nullptr;
+    s.scales = nullptr;
+    s.q_idx = nullptr;
+    s.w_idx = nullptr;
     return s;
 }
 
@@ -645,6 +649,11 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         x.sw = select_ws(workspace, w, l);
         x.sw.row0 = batch->idx_row0;
         x.sw.n_rows = batch->n_idx_rows;
+        // the scans keep few block scores; the selection scores again what it re-reads
+        x.sw.keys = Ly.idx_keys;
+        x.sw.scales = Ly.idx_scales;
+        x.sw.q_idx = Ly.q_idx;
+        x.sw.w_idx = Ly.w_idx;
         x.aw = attn_ws(workspace, w, l);
         x.stage = offload ? at<void>(workspace, w.stage + w.per_stage * l) : nullptr;
         x.fetch = offload ? at<int2>(workspace, w.fetch + w.per_fetch * l) : nullptr;
@@ -662,7 +671,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
                                   batch->n_idx_rows, B, batch->max_ctx, nullptr, lw[l].bs, bs_stride, lw[l].sw.heads,
                                   lw[l].sw.lists, w.g, K, cfg->sink_blocks, cfg->tail_tokens,
                                   clear ? nullptr : flags, s, (hipEvent_t)Ly.score_events[0],
-                                  (hipEvent_t)Ly.score_events[1], clear);
+                                  (hipEvent_t)Ly.score_events[1], clear, true);
     };
     auto select = [&](int l, hipStream_t s) {
         return launch_select(lw[l].bs, bs_stride, batch->ctx_len, B, batch->max_ctx, lw[l].sw, w.g, K,
@@ -729,6 +738,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     // The per-layer pointer tables of layers l0 .. l0 + nl - 1 (HBM pools).
     auto hbm_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, AttnLayers &AL) {
         CL.flags = l0 == 0 ? nullptr : flags;      // the first scan clears the word instead
+        CL.drop_listed_bs = 1;
         AL.flags = flags;
         for (int i = 0; i < nl; i++) {
             const int l = l0 + i;
@@ -872,6 +882,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     const hipStream_t sg = (hipStream_t)side[0];
     auto staged_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, GatherLayers &GL, AttnLayers &AL) {
         CL.flags = l0 == 0 ? nullptr : flags;      // the first scan clears the word instead
+        CL.drop_listed_bs = 1;
         GL.flags = flags;
         AL.flags = flags;
         for (int i = 0; i < nl; i++) {

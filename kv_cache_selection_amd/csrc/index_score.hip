@@ -6,21 +6,11 @@
 // and for every C4 block j (article intro: 4 adjacent tokens form the unit
 // of selection) B_j = max of s_t over the block's valid tokens.
 //
-// Mapping on gfx950: a wave scores a tile of 64 tokens as 4 groups of 16.
-// For group g, lane l loads the 16 bytes at offset 16*(l>>4) of token
-// 16g + (l&15), so each of the wave's four 16-byte loads reads one contiguous
-// 1 KB piece of the tile (full cache lines, no lane stride). The e4m3 codes
-// are widened to bf16 in registers (exact: 4 significant bits fit bf16's 8)
-// and the 4-head x 64-dim dot products run on the matrix cores as
-// v_mfma_f32_16x16x32_bf16 (B = 32 dims x 16 tokens): the lane's first 8
-// bytes feed one MFMA and its last 8 the other, and the query operand A
-// follows the same permutation of the 64 dims. For group g the query heads
-// sit in rows 4g..4g+3 of A (zeros elsewhere), so all four groups accumulate
-// into one 16x16 tile whose row 4g+h, column j -- head h of token 16g+j --
-// the MFMA output layout places in lane 16g+j: one token per lane, no
-// shuffles. bf16 x bf16 products are exact in fp32; accumulation is fp32.
-// The VALU only widens codes and runs the ReLU/weight epilogue and the block
-// max, so the kernel stays bound by HBM, not by fp32 FMA throughput.
+// Mapping on gfx950: a wave scores a tile of 64 tokens on the matrix cores,
+// one token per lane (idx_tile_load / idx_tile_score, shared with the
+// selection kernel, which scores a chunk again when it must). The VALU only
+// widens codes and runs the ReLU/weight epilogue and the block max, so the
+// kernel stays bound by HBM, not by fp32 FMA throughput.
 //
 // One launch may scan several layers (grid z), their pointers in the kernel
 // arguments, so that the scan streams from one layer into the next.
@@ -31,7 +21,12 @@
 // excluded) and from it the chunk's candidate list: its best blocks, cut at a
 // bin boundary (build_chunk_list). The selection then starts from these
 // lists, so nothing needs to be counted across workgroups, and no global
-// histogram has to be cleared before the scan.
+// histogram has to be cleared before the scan. In the decode step
+// (drop_listed_bs) such a chunk stores its block scores only when its list
+// was cut short by a crowded bin: the 24 MB of block scores of a 12-layer
+// batch8-256k step took about 18 us of its scan (266 against 249 us), and the
+// selection reads a chunk's scores back only in the rare case that it must
+// re-read the chunk, scoring it again from the index otherwise.
 #include "qsa_internal.h"
 
 #include <hip/hip_ext.h>
@@ -60,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
                                                                int tail_tokens, uint32_t *clear_flags)
 {
     __shared__ uint32_t lhist[kLists ? kHistBins : 1];
-    __shared__ uint32_t lsh[4];                    // highest key bin; list threshold, fill and size
+    __shared__ uint32_t lsh[5];                    // highest key bin; list threshold, fill, size and keep
     // The chunk's block scores, written out at the end as contiguous rows
     // with non-temporal stores. Their 2 MB per layer are 1.5 % of the bytes,
     // but stored from the loop with ordinary stores they slowed the 12-layer
@@ -68,8 +63,6 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     __shared__ float lbs[kMaxChunkTokens / kBT];
     const uint8_t *__restrict__ keys = Ls.keys[blockIdx.z];
     const uint16_t *__restrict__ scales = Ls.scales[blockIdx.z];
-    const uint16_t *__restrict__ q_idx = Ls.q_idx[blockIdx.z];
-    const float *__restrict__ w_idx = Ls.w_idx[blockIdx.z];
     float *__restrict__ token_scores = Ls.token_scores[blockIdx.z];
     float *__restrict__ block_scores = Ls.block_scores[blockIdx.z];
 
@@ -111,23 +104,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     // Two-deep software pipeline: the keys of the wave's next 64 tokens are
     // requested before the current 64 are widened and multiplied. The first
     // tile is requested before anything else is set up.
-    u32x4 k[4], kn[4];
+    idx_u32x4 k[4], kn[4];
     uint16_t sc_bits = 0, sc_next = 0;
-    const int grp_tok = lane & 15;          // token within a group, for the loads
-    const int grp_off = 16 * (lane >> 4);   // byte offset within the token's 64
-    auto load_tile = [&](int tw, u32x4 *dst, uint16_t &sc) {
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int t = tw + 16 * g + grp_tok;
-            dst[g] = t < L ? __builtin_nontemporal_load(
-                                 reinterpret_cast<const u32x4 *>(kbase + (int64_t)t * kIdxD + grp_off))
-                           : u32x4{0u, 0u, 0u, 0u};
-        }
-        sc = (tw + lane < L) ? sbase[tw + lane] : (uint16_t)0;
-    };
     int tw = t_begin + wave * kWaveTok;
     if (tw < t_end)
-        load_tile(tw, k, sc_bits);
+        idx_tile_load(kbase, sbase, tw, L, lane, k, sc_bits);
 
     if (do_hist) {
         for (int i = tid; i < kHistBins; i += kThreads)
@@ -136,27 +117,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
             lsh[0] = 0;
     }
     uint32_t top = 0;                       // highest key bin of this lane's eligible blocks
-
-    // A operands: for group g, lane l (row l&15 of A) holds head (l&3) of the
-    // query when (l&15)>>2 == g, else zeros; dims follow the lane's bytes:
-    // qa[g][0] = dims 16(l>>4) + 0..7, qa[g][1] = dims 16(l>>4) + 8..15.
-    bf16x8 qa[4][2];
-    {
-        const u32x4 *qrow =
-            reinterpret_cast<const u32x4 *>(q_idx + ((int64_t)b * kIdxH + (lane & 3)) * kIdxD + 16 * (lane >> 4));
-        const u32x4 q0 = qrow[0], q1 = qrow[1];
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const bool mine = ((lane & 15) >> 2) == g;
-            qa[g][0] = __builtin_bit_cast(bf16x8, mine ? q0 : z);
-            qa[g][1] = __builtin_bit_cast(bf16x8, mine ? q1 : z);
-        }
-    }
-    float w[kIdxH];
-#pragma unroll
-    for (int h = 0; h < kIdxH; h++)
-        w[h] = w_idx[b * kIdxH + h];
+    IdxQuery Q;
+    idx_query(Ls.q_idx[blockIdx.z] + (int64_t)b * kIdxH * kIdxD, Ls.w_idx[blockIdx.z] + (int64_t)b * kIdxH, lane, Q);
 
     if (do_hist)
         __syncthreads();
@@ -164,25 +126,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     for (; tw < t_end; tw += kWgTok) {
         const int tn = tw + kWgTok;
         if (tn < t_end)
-            load_tile(tn, kn, sc_next);
+            idx_tile_load(kbase, sbase, tn, L, lane, kn, sc_next);
         const int t = tw + lane;
         const bool valid = t < L;
-
-        // Two independent accumulation chains (first / last 8 bytes of each lane).
-        f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[g][0], e4m3x8_to_bf16x8(k[g].x, k[g].y), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[g][1], e4m3x8_to_bf16x8(k[g].z, k[g].w), acc1, 0, 0, 0);
-        }
-        const f32x4 acc = acc0 + acc1;
-        // acc[h] = q_h . k_t for this lane's token t.
-        const float sigma = (float)__builtin_bit_cast(_Float16, sc_bits);
-        float s = 0.0f;
-        s += w[0] * fmaxf(sigma * acc[0], 0.0f);
-        s += w[1] * fmaxf(sigma * acc[1], 0.0f);
-        s += w[2] * fmaxf(sigma * acc[2], 0.0f);
-        s += w[3] * fmaxf(sigma * acc[3], 0.0f);
+        float s = idx_tile_score(k, sc_bits, Q);
         if (!valid)
             s = -INFINITY;
         if (kTokens && valid)
@@ -213,13 +160,16 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const ScoreLayers
     }
     __syncthreads();
     const int blk_end = min(blk_begin + chunk_tokens / kBT, n_blk);
-    for (int j = blk_begin + tid; j < blk_end; j += kThreads)
-        __builtin_nontemporal_store(lbs[j - blk_begin], bs_row + j);
+    bool store = true;
     if (do_hist) {
         const int64_t c = (int64_t)b * g.n_chunks + blockIdx.x;
-        build_chunk_list<kThreads>(lhist, lbs, blk_begin, blk_end, sink_blocks, tail_first, g.m, g.cap,
-                                   (int)lsh[0], lsh + 1, Ls.heads[blockIdx.z] + c, Ls.lists[blockIdx.z] + c * g.cap);
+        store = build_chunk_list<kThreads>(lhist, lbs, blk_begin, blk_end, sink_blocks, tail_first, g.m, g.cap,
+                                           (int)lsh[0], !Ls.drop_listed_bs, lsh + 1, Ls.heads[blockIdx.z] + c,
+                                           Ls.lists[blockIdx.z] + c * g.cap);
     }
+    if (store)
+        for (int j = blk_begin + tid; j < blk_end; j += kThreads)
+            __builtin_nontemporal_store(lbs[j - blk_begin], bs_row + j);
 }
 
 // Chunk lists of existing block scores (standalone selection call): the
@@ -232,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void list_build_kernel(const float *__res
 {
     __shared__ uint32_t lhist[kHistBins];
     __shared__ float lbs[kMaxChunkTokens / kBT];
-    __shared__ uint32_t lsh[4];
+    __shared__ uint32_t lsh[5];
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int L = clamp_ctx(ctx_len[b], max_ctx);
@@ -263,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void list_build_kernel(const float *__res
         atomicMax(&lsh[0], top);
     __syncthreads();
     const int64_t c = (int64_t)b * g.n_chunks + blockIdx.x;
-    build_chunk_list<kThreads>(lhist, lbs, j0, j1, sink_blocks, tail_first, g.m, g.cap, (int)lsh[0], lsh + 1,
-                               heads + c, lists + c * g.cap);
+    (void)build_chunk_list<kThreads>(lhist, lbs, j0, j1, sink_blocks, tail_first, g.m, g.cap, (int)lsh[0], true,
+                                     lsh + 1, heads + c, lists + c * g.cap);
 }
 
 __global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n)
@@ -369,7 +319,7 @@ hipError_t launch_index_score_layers(const ScoreLayers &L, int n_layers, const i
                               sink_blocks, tail_tokens, s, ev0, ev1, clear_flags);
     const ScoreLayersT<1> L1 = {{L.keys[0]},         {L.scales[0]},       {L.q_idx[0]}, {L.w_idx[0]},
                                 {L.token_scores[0]}, {L.block_scores[0]}, {L.heads[0]}, {L.lists[0]},
-                                L.flags};
+                                L.flags,             L.drop_listed_bs};
     return launch_score_n(L1, 1, ctx_len, row0, n_rows, batch, max_ctx, bs_stride, g, budget_blocks, sink_blocks,
                           tail_tokens, s, ev0, ev1, clear_flags);
 }
@@ -379,10 +329,11 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *heads, uint64_t *lists, const ListGeom &g, int budget_blocks,
                               int sink_blocks, int tail_tokens, uint32_t *flags, hipStream_t s, hipEvent_t ev0,
-                              hipEvent_t ev1, uint32_t *clear_flags)
+                              hipEvent_t ev1, uint32_t *clear_flags, bool drop_listed_bs)
 {
     ScoreLayers L = {};
     L.flags = flags;
+    L.drop_listed_bs = drop_listed_bs ? 1 : 0;
     L.keys[0] = keys;
     L.scales[0] = scales;
     L.q_idx[0] = q_idx;

@@ -134,7 +134,9 @@ constexpr int kOneMaxBlocks = 16384;
 
 // Header of a chunk list: entry count (bits 0-15); threshold bin (bits
 // 16-28): the list holds exactly the chunk's eligible blocks whose key bin is
-// at least this; bit 31: the list holds every eligible block of the chunk.
+// at least this; bit 30: the chunk's block scores were stored; bit 31: the
+// list holds every eligible block of the chunk.
+constexpr uint32_t kListScoresKept = 1u << 30;
 constexpr uint32_t kListComplete = 1u << 31;
 __device__ __forceinline__ uint32_t list_count(uint32_t h) { return h & 0xFFFFu; }
 __device__ __forceinline__ uint32_t list_bin(uint32_t h) { return (h >> 16) & 0x1FFFu; }
@@ -158,6 +160,14 @@ struct SelectWs {
     // the selection takes it as empty too. Null when there is no index.
     const int64_t *row0;
     int64_t n_rows;
+    // The layer's index and indexer query (qsa_decode_step, whose scan keeps
+    // the block scores of a list-route chunk only when its list was cut short
+    // by a crowded bin): a chunk to re-read whose scores were not kept is
+    // scored again from these. Null: every chunk's block scores are there.
+    const uint8_t *keys;
+    const uint16_t *scales;
+    const uint16_t *q_idx;
+    const float *w_idx;
 };
 
 // The length the selection works with: ctx_len clamped to [0, max_ctx], or 0
@@ -195,6 +205,10 @@ struct ScoreLayersT {
     uint32_t *heads[N];                   // chunk list headers, or null (no lists)
     uint64_t *lists[N];                   // chunk lists
     uint32_t *flags;                      // the call's flags word, or null
+    // 0: store every block score; 1 (qsa_decode_step): a chunk with a list
+    // stores its block scores only when the list was cut short by a crowded
+    // bin (the selection scores the other chunks it re-reads again)
+    int drop_listed_bs;
 };
 using ScoreLayers = ScoreLayersT<kMaxChainLayers>;
 
@@ -334,12 +348,15 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v)
 // thread places its eligible blocks at or above the list's threshold bin.
 // Writes the header and the entries (in no particular order), and 0 in the
 // list's unused slots, so that a reader can tell entries from empty slots by
-// their value (no block's composite is 0). `sh` is three words of LDS. NT >=
-// cap.
+// their value (no block's composite is 0). The header's kListScoresKept bit is
+// set when keep_all is, or when the list was cut short by a crowded bin; the
+// return value (the same for every thread) says whether it was, so that the
+// caller stores the chunk's block scores then. `sh` is four words of LDS.
+// NT >= cap.
 template <int NT>
-__device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int blk_begin, int blk_end, int el_begin,
-                                 int el_end, int m, int cap, int top_bin, uint32_t *sh, uint32_t *head_out,
-                                 uint64_t *list_out)
+__device__ bool build_chunk_list(const uint32_t *lhist, const float *lbs, int blk_begin, int blk_end, int el_begin,
+                                 int el_end, int m, int cap, int top_bin, bool keep_all, uint32_t *sh,
+                                 uint32_t *head_out, uint64_t *list_out)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -348,7 +365,7 @@ __device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int bl
     const uint32_t n_el = hi > lo ? (uint32_t)(hi - lo) : 0u;
     if (tid < 64) {
         uint32_t theta = 0, size = n_el;
-        bool complete = true;
+        bool complete = true, cut = false;
         if (n_el >= (uint32_t)m) {
             uint32_t carry = 0;
             for (int hb = top_bin; hb >= 0; hb -= 64) {        // uniform in the wave
@@ -375,6 +392,7 @@ __device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int bl
                         theta = (uint32_t)(hb - f + 1);
                         size = cum - in_bin;
                         complete = false;
+                        cut = true;
                     }
                     break;
                 }
@@ -384,16 +402,20 @@ __device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int bl
         if (size > (uint32_t)cap) {                             // never, with lhist consistent
             size = (uint32_t)cap;
             complete = false;
+            cut = true;
         }
+        const bool keep = keep_all || cut;
         if (tid == 0) {
             sh[0] = theta;
             sh[1] = 0;
             sh[2] = size;
-            *head_out = size | (theta << 16) | (complete ? kListComplete : 0u);
+            sh[3] = keep ? 1u : 0u;
+            *head_out = size | (theta << 16) | (complete ? kListComplete : 0u) | (keep ? kListScoresKept : 0u);
         }
     }
     __syncthreads();
     const uint32_t theta = sh[0];
+    const bool kept = sh[3] != 0u;
     if (tid >= (int)sh[2] && tid < cap)
         list_out[tid] = 0ull;
     for (int j0 = blk_begin; j0 < blk_end; j0 += NT) {
@@ -413,6 +435,7 @@ __device__ void build_chunk_list(const uint32_t *lhist, const float *lbs, int bl
         if (in && pos < (uint32_t)cap)
             list_out[pos] = composite(key, j);
     }
+    return kept;
 }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -428,6 +451,85 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1)
                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
     return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- the indexer's token score on the matrix cores --------------------------
+// s_t = sum over the 4 heads of w_h ReLU(sigma_t (q_h . k_t)) (digest,
+// mechanism section), for a tile of 64 tokens per wave. Every kernel that
+// scores index rows uses these three functions, so a token's score has the
+// same bits wherever it is computed (the scan, and the selection when it
+// scores a chunk again).
+//
+// A wave scores its tile as 4 groups of 16 tokens. For group g, lane l loads
+// the 16 bytes at offset 16 (l >> 4) of token 16 g + (l & 15), so each of the
+// wave's four 16-byte loads reads one contiguous 1 KB piece of the tile. The
+// e4m3 codes are widened to bf16 (exact) and the 4-head x 64-dim products run
+// as v_mfma_f32_16x16x32_bf16 (B = 32 dims x 16 tokens): the lane's first 8
+// bytes feed one MFMA chain and its last 8 the other, and the query operand A
+// follows the same permutation of the dims. For group g the query heads sit in
+// rows 4g..4g+3 of A (zeros elsewhere), so the four groups accumulate into
+// one 16x16 tile whose row 4g+h, column j (head h of token 16g+j) the MFMA
+// output layout places in lane 16g+j: each lane ends with its own token's 4
+// head products. bf16 x bf16 products are exact in fp32; accumulation is
+// fp32, and the epilogue's multiply-adds are explicit fused operations so
+// that no kernel rounds them differently.
+typedef __attribute__((ext_vector_type(4))) uint32_t idx_u32x4;
+typedef __attribute__((ext_vector_type(4))) float idx_f32x4;
+
+struct IdxQuery {
+    bf16x8 qa[4][2];      // A operands: group g, first / last 8 dims of the lane's 16
+    float w[kIdxH];       // head weights
+};
+
+// Sequence b's query operands: q_b = q_idx + b * 4 * 64 (bf16 bits), w_b = w_idx + b * 4.
+__device__ __forceinline__ void idx_query(const uint16_t *__restrict__ q_b, const float *__restrict__ w_b, int lane,
+                                          IdxQuery &Q)
+{
+    const idx_u32x4 *qrow = reinterpret_cast<const idx_u32x4 *>(q_b + (lane & 3) * kIdxD + 16 * (lane >> 4));
+    const idx_u32x4 q0 = qrow[0], q1 = qrow[1];
+    const idx_u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        const bool mine = ((lane & 15) >> 2) == g;
+        Q.qa[g][0] = __builtin_bit_cast(bf16x8, mine ? q0 : z);
+        Q.qa[g][1] = __builtin_bit_cast(bf16x8, mine ? q1 : z);
+    }
+#pragma unroll
+    for (int h = 0; h < kIdxH; h++)
+        Q.w[h] = w_b[h];
+}
+
+// The lane's pieces of the tile of tokens [tw, tw + 64) of a sequence whose
+// rows start at kb (codes) and sb (scales); tokens at or past L read nothing.
+__device__ __forceinline__ void idx_tile_load(const uint8_t *__restrict__ kb, const uint16_t *__restrict__ sb, int tw,
+                                              int L, int lane, idx_u32x4 *k, uint16_t &sc)
+{
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        const int t = tw + 16 * g + (lane & 15);
+        k[g] = t < L ? __builtin_nontemporal_load(
+                           reinterpret_cast<const idx_u32x4 *>(kb + (int64_t)t * kIdxD + 16 * (lane >> 4)))
+                     : idx_u32x4{0u, 0u, 0u, 0u};
+    }
+    sc = (tw + lane < L) ? sb[tw + lane] : (uint16_t)0;
+}
+
+// Score of token tw + lane of the tile (valid or not: the caller masks).
+__device__ __forceinline__ float idx_tile_score(const idx_u32x4 *k, uint16_t sc, const IdxQuery &Q)
+{
+    idx_f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q.qa[g][0], e4m3x8_to_bf16x8(k[g].x, k[g].y), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q.qa[g][1], e4m3x8_to_bf16x8(k[g].z, k[g].w), acc1, 0, 0, 0);
+    }
+    const idx_f32x4 acc = acc0 + acc1;      // acc[h] = q_h . k_t
+    const float sigma = (float)__builtin_bit_cast(_Float16, sc);
+    float s = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kIdxH; h++)
+        s = __builtin_fmaf(Q.w[h], fmaxf(sigma * acc[h], 0.0f), s);
+    return s;
 }
 
 // Kernel launchers (one translation unit each).
@@ -448,7 +550,8 @@ hipError_t launch_index_score(const uint8_t *keys, const uint16_t *scales, const
                               int batch, int max_ctx, float *token_scores, float *block_scores, int64_t bs_stride,
                               uint32_t *heads, uint64_t *lists, const ListGeom &g, int budget_blocks,
                               int sink_blocks, int tail_tokens, uint32_t *flags, hipStream_t s,
-                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, uint32_t *clear_flags = nullptr);
+                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, uint32_t *clear_flags = nullptr,
+                              bool drop_listed_bs = false);
 
 // Index scoring of layers 0 .. n_layers - 1 of L in one launch (grid z =
 // layer); token_scores and heads must be null for all layers or for none.

@@ -45,6 +45,7 @@ namespace {
 
 constexpr int kThreads = 1024;                     // pool_select_kernel
 constexpr int kCandCap = kPoolSlots;               // pool entries held in LDS (64 KB)
+constexpr int kTileBlocks = 64 / kBT;              // blocks of a 64-token scoring tile
 constexpr int kLoadBatch = 4;                      // re-read loads a thread keeps in flight per round
 constexpr int kSegBlocks = 1 << 18;                // bitmap segment (32 KB of LDS)
 constexpr int kSegWords = kSegBlocks / 32;
@@ -420,6 +421,27 @@ __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayer
             if (tid == 0)
                 sh_u[3] = E;
             __syncthreads();
+            // a block of a needy chunk joins the pool if it lies below the
+            // list's bin and reaches T_U (wave-wide: add, append position)
+            auto offer = [&](int j, float x, bool in) {
+                bool add = false;
+                uint64_t c = 0;
+                if (in) {
+                    const uint32_t key = order_key(x);
+                    c = composite(key, j);
+                    add = (key >> kHistShift) < list_bin(head[j / cb]) && (!bounded || c >= TU);
+                }
+                const uint64_t bal = __ballot(add);
+                uint32_t base = 0;
+                if (lane == 0 && bal)
+                    base = atomicAdd(&sh_u[3], (uint32_t)__popcll(bal));
+                base = __shfl(base, 0);
+                const uint32_t p = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+                if (add && p < (uint32_t)ws.spill_stride)
+                    put(p, c);
+            };
+            // a chunk's block scores are in memory unless the scan dropped them
+            auto kept = [&](int c) -> bool { return !ws.keys || (head[c] & kListScoresKept); };
             const float *row = block_scores + (int64_t)b * bs_stride;
             const uint32_t items = n_needy * (uint32_t)cb;
             for (uint32_t q0 = 0; q0 < items; q0 += kThreads * kLoadBatch) {
@@ -431,30 +453,43 @@ __global__ __launch_bounds__(kThreads) void pool_select_kernel(const SelectLayer
                     jj[e] = -1;
                     x[e] = 0.0f;
                     if (q < items) {
-                        const int j = (int)needy[q / cb] * cb + (int)(q % cb);
-                        if (j >= s_end && j < t_begin) {
+                        const int c = (int)needy[q / cb];
+                        const int j = c * cb + (int)(q % cb);
+                        if (j >= s_end && j < t_begin && kept(c)) {
                             jj[e] = j;
                             x[e] = row[j];
                         }
                     }
                 }
 #pragma unroll
-                for (int e = 0; e < kLoadBatch; e++) {
-                    bool add = false;
-                    uint64_t c = 0;
-                    if (jj[e] >= 0) {
-                        const uint32_t key = order_key(x[e]);
-                        c = composite(key, jj[e]);
-                        add = (key >> kHistShift) < list_bin(head[jj[e] / cb]) && (!bounded || c >= TU);
-                    }
-                    const uint64_t bal = __ballot(add);
-                    uint32_t base = 0;
-                    if (lane == 0 && bal)
-                        base = atomicAdd(&sh_u[3], (uint32_t)__popcll(bal));
-                    base = __shfl(base, 0);
-                    const uint32_t p = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-                    if (add && p < (uint32_t)ws.spill_stride)
-                        put(p, c);
+                for (int e = 0; e < kLoadBatch; e++)
+                    offer(jj[e], x[e], jj[e] >= 0);
+            }
+            if (ws.keys) {
+                // the needy chunks whose scores the scan dropped: score their
+                // tokens again, a 64-token tile per wave at a time, with the
+                // scan's own arithmetic (the same bits), and take each block's
+                // maximum over its valid tokens as the scan does
+                IdxQuery Q;
+                idx_query(ws.q_idx + (int64_t)b * kIdxH * kIdxD, ws.w_idx + (int64_t)b * kIdxH, lane, Q);
+                const uint8_t *kb = ws.keys + r0 * kIdxD;
+                const uint16_t *sb = ws.scales + r0;
+                const uint32_t tpc = (uint32_t)cb / kTileBlocks;   // tiles per chunk
+                for (uint32_t tile = (uint32_t)(tid >> 6); tile < n_needy * tpc; tile += kThreads / 64) {
+                    const int c = (int)needy[tile / tpc];
+                    if (kept(c))
+                        continue;                                   // uniform in the wave
+                    const int tw = (c * cb + (int)(tile % tpc) * kTileBlocks) * kBT;
+                    idx_u32x4 k[4];
+                    uint16_t sc;
+                    idx_tile_load(kb, sb, tw, L, lane, k, sc);
+                    float x = idx_tile_score(k, sc, Q);
+                    if (tw + lane >= L)
+                        x = -INFINITY;
+                    x = fmaxf(x, __shfl_xor(x, 1));
+                    x = fmaxf(x, __shfl_xor(x, 2));
+                    const int j = (tw + lane) >> 2;
+                    offer(j, x, (lane & 3) == 0 && j >= s_end && j < t_begin);
                 }
             }
             __syncthreads();

@@ -9,7 +9,7 @@ import qsa_synth as S
 from qsa_synth import fill
 from qsa_synth.device import DeviceInputs
 
-from qsa_testlib import (check_attention, check_scores, check_selection, oracle_attention_on, oracle_unit,
+from qsa_testlib import (Unit, check_attention, check_scores, check_selection, oracle_attention_on, oracle_unit,
                           score_scale, unit_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -464,6 +464,109 @@ def test_decode_step_deterministic_and_offload_bit_exact(gpu):
         sel3, ns3, out3 = _step(dh, n_side=n_side)
         assert np.array_equal(sel1, sel3), n_side
         assert np.array_equal(out1, out3), n_side
+
+
+def _list_geom(B, max_ctx, K):
+    """(blocks per scoring chunk, m, cap) of the chunk lists, the rule the
+    library applies (score chunk: 512 tokens, doubled while the call keeps
+    512 workgroups per layer, up to 8192; m about three times a chunk's share
+    of the budget, at least 8 while all lists fit 8192 slots, else 4)."""
+    chunk = 512
+    while chunk < 8192 and B * ((max_ctx + 2 * chunk - 1) // (2 * chunk)) >= 512:
+        chunk *= 2
+    cb = chunk // 4
+    n_chunks = ((max_ctx + 3) // 4 + cb - 1) // cb
+    floor = 8 if n_chunks * 16 <= 8192 else 4
+    m = min(max((3 * K + n_chunks - 1) // n_chunks, floor), 64)
+    return cb, m, 2 * m
+
+
+def test_decode_step_scores_re_read_chunks_again(gpu):
+    """In the decode step the scan keeps a chunk's block scores only when the
+    chunk's list was cut short by a crowded bin; a chunk that the selection
+    must re-read otherwise is scored again from the index. Here a run of 16
+    chunks per sequence holds keys along the query with scales that rise over
+    four octaves in every 512 tokens: each run chunk holds about 32 of the
+    answer's blocks, spread over some 32 bins, so its list (about m entries)
+    is not cut short, is wholly chosen, and the chunk is re-read and scored
+    again. The step's selection must equal the exact top-K of the block
+    scores that the standalone scoring call computes (the same arithmetic),
+    match the oracle's within near ties, and be the same with a side stream."""
+    from test_list_route_model import chunk_list, list_route, order_keys
+    rng = np.random.default_rng(17)
+    lens = np.array([100000, 70001], np.int64)
+    B = len(lens)
+    row0 = np.array([0, int(lens[0])], np.int64)
+    n = int(lens.sum())
+    budget, K = 2048, 512
+    keys = rng.integers(0, 256, size=(n, 64)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0x30
+    scales = np.float16(rng.uniform(0.001, 0.02, size=n))
+    v = rng.standard_normal((B, 64)).astype(np.float32)
+    q_idx = S.f32_to_bf16_bits(np.repeat(v[:, None, :], 4, axis=1))
+    w = rng.uniform(0.5, 1.0, (B, 4)).astype(np.float32)
+    run0 = (20000, 30720)                           # first token of each sequence's run (multiples of 512)
+    for b in range(B):
+        vb = S.bf16_bits_to_f32(q_idx[b, 0])
+        code = S.f32_to_e4m3_codes(vb / np.abs(vb).max() * 448.0)
+        t0 = int(row0[b]) + run0[b]
+        for c in range(16):
+            pos = np.arange(512)
+            keys[t0 + 512 * c:t0 + 512 * (c + 1)] = code
+            scales[t0 + 512 * c:t0 + 512 * (c + 1)] = np.float16(
+                1e-3 * np.exp2(4.0 * pos / 512 + 0.013 * c))
+    scales = scales.view(np.uint16)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    ctx, r0d = d(lens.astype(np.int32)), d(row0)
+    keys_d, scales_d = d(keys), d(scales.view(np.int16))
+    q_idx_d, w_d = d(q_idx.view(np.int16)), d(w)
+    # the GPU's own block scores, from the standalone scoring call
+    _, bs = _score(qsa.make_config(budget), B, int(lens.max()), ctx, r0d, keys_d, scales_d, q_idx_d, w_d, n)
+    cb, m, cap = _list_geom(B, int(lens.max()), K)
+    for b in range(B):                              # the construction does what it is for
+        nb = (int(lens[b]) + 3) // 4
+        _, n_needy = list_route(bs[b, :nb], K, 0, nb, cb, m, cap)
+        assert n_needy >= 8, (b, n_needy)
+        j0 = run0[b] // 4
+        kk = order_keys(bs[b, j0:j0 + cb])
+        theta, complete, comps = chunk_list(kk, np.arange(j0, j0 + cb), m, cap)
+        assert len(comps) >= m and not complete     # a full list, not cut short
+    # the decode step, on one stream and with a side stream
+    n_slots = n
+    pool = torch.randn((n_slots, 1024), dtype=torch.bfloat16, device=gpu).view(torch.int16)
+    pt = torch.from_numpy(np.stack([np.arange(int(lens.max())) + row0[b] for b in range(B)]).astype(np.int32))
+    pt = torch.where(pt < n, pt, torch.zeros_like(pt)).to(gpu)
+    q = torch.randn((B, 16, 256), dtype=torch.bfloat16, device=gpu).view(torch.int16)
+    cfg = qsa.make_config(budget)
+    bt = qsa.make_batch(B, int(lens.max()), ctx, r0d, pt, int(pt.shape[1]), n_slots, n)
+    ws, nws = _ws(cfg, B, int(lens.max()), 1, qsa.QSA_KV_DEVICE)
+    got = []
+    for n_side in (0, 1):
+        ws.fill_(0xAB)                              # no stale block scores to find
+        sel = torch.full((1, B, K), -7, dtype=torch.int32, device=gpu)
+        ns = torch.zeros((1, B), dtype=torch.int32, device=gpu)
+        out = torch.zeros((1, B, 16, 256), dtype=torch.float32, device=gpu)
+        lay = [qsa.make_layer(keys_d, scales_d, q_idx_d, w_d, q, pool, out[0], None, sel[0], ns[0])]
+        side = [torch.cuda.Stream() for _ in range(n_side)]
+        ev = qsa.StepEvents(1, n_side) if n_side else None
+        qsa.qsa_decode_step(cfg, bt, lay, qsa.QSA_KV_DEVICE, ws, nws, torch.cuda.current_stream(), side, events=ev)
+        torch.cuda.synchronize()
+        got.append((sel.cpu().numpy(), ns.cpu().numpy(), out.cpu().numpy()))
+    for a, b_ in zip(got[0], got[1]):
+        assert np.array_equal(a, b_)
+    sel, ns, _ = got[0]
+    for b in range(B):
+        L = int(lens[b])
+        nb = (L + 3) // 4
+        fm = oracle.forced_mask(L, 4, 0, 0)
+        exact = oracle.select_blocks(bs[b, :nb], K, fm).blocks      # exact top-K of the GPU's block scores
+        assert ns[0, b] == len(exact)
+        assert np.array_equal(sel[0, b, :ns[0, b]], exact), b
+        k, s = keys[row0[b]:row0[b] + L], scales[row0[b]:row0[b] + L]
+        ref_bs = oracle.block_scores(oracle.token_scores(k, s, q_idx[b], w[b]))
+        osel = oracle.select_blocks(ref_bs, K, fm)
+        check_selection(sel[0, b, :ns[0, b]], Unit(L, None, None, None, None, None, None, None, ref_bs, fm,
+                                                   osel.blocks, osel.kth_score, None))
 
 
 def test_decode_step_offload_reuses_one_event_set(gpu):
