@@ -485,88 +485,103 @@ def test_decode_step_scores_re_read_chunks_again(gpu):
     """In the decode step the scan keeps a chunk's block scores only when the
     chunk's list was cut short by a crowded bin; a chunk that the selection
     must re-read otherwise is scored again from the index. Here a run of 16
-    chunks per sequence holds keys along the query with scales that rise over
-    four octaves in every 512 tokens: each run chunk holds about 32 of the
-    answer's blocks, spread over some 32 bins, so its list (about m entries)
-    is not cut short, is wholly chosen, and the chunk is re-read and scored
-    again. The step's selection must equal the exact top-K of the block
-    scores that the standalone scoring call computes (the same arithmetic),
-    match the oracle's within near ties, and be the same with a side stream."""
+    chunks per sequence and layer holds keys along the query with scales that
+    rise over four octaves in every 512 tokens: each run chunk holds about 32
+    of the answer's blocks, spread over some 32 bins, so its list (about m
+    entries) is not cut short, is wholly chosen, and the chunk is re-read and
+    scored again. Two layers (runs in different places), a sink block and a
+    64-token tail; one stream (per-layer launches), a side stream (one launch
+    per kernel for both layers) and the pinned-host pipeline. Every schedule
+    must give the same bits, and each selection must equal the exact top-K of
+    the block scores that the standalone scoring call computes (the same
+    arithmetic) and match the oracle's within near ties."""
     from test_list_route_model import chunk_list, list_route, order_keys
     rng = np.random.default_rng(17)
     lens = np.array([100000, 70001], np.int64)
-    B = len(lens)
+    B, NL = len(lens), 2
     row0 = np.array([0, int(lens[0])], np.int64)
     n = int(lens.sum())
-    budget, K = 2048, 512
-    keys = rng.integers(0, 256, size=(n, 64)).astype(np.uint8)
-    keys[(keys & 0x7F) == 0x7F] = 0x30
-    scales = np.float16(rng.uniform(0.001, 0.02, size=n))
-    v = rng.standard_normal((B, 64)).astype(np.float32)
-    q_idx = S.f32_to_bf16_bits(np.repeat(v[:, None, :], 4, axis=1))
-    w = rng.uniform(0.5, 1.0, (B, 4)).astype(np.float32)
-    run0 = (20000, 30720)                           # first token of each sequence's run (multiples of 512)
-    for b in range(B):
-        vb = S.bf16_bits_to_f32(q_idx[b, 0])
-        code = S.f32_to_e4m3_codes(vb / np.abs(vb).max() * 448.0)
-        t0 = int(row0[b]) + run0[b]
-        for c in range(16):
-            pos = np.arange(512)
-            keys[t0 + 512 * c:t0 + 512 * (c + 1)] = code
-            scales[t0 + 512 * c:t0 + 512 * (c + 1)] = np.float16(
-                1e-3 * np.exp2(4.0 * pos / 512 + 0.013 * c))
-    scales = scales.view(np.uint16)
+    budget, K, sink, tail = 2048, 512, 1, 64
+    runs = {(0, 0): 20000, (0, 1): 30720, (1, 0): 61440, (1, 1): 4096}   # (layer, b): first token of the run
+    keys = np.empty((NL, n, 64), np.uint8)
+    scales = np.empty((NL, n), np.uint16)
+    q_idx = np.empty((NL, B, 4, 64), np.uint16)
+    w = rng.uniform(0.5, 1.0, (NL, B, 4)).astype(np.float32)
+    for l in range(NL):
+        kl = rng.integers(0, 256, size=(n, 64)).astype(np.uint8)
+        kl[(kl & 0x7F) == 0x7F] = 0x30
+        sl = np.float16(rng.uniform(0.001, 0.02, size=n))
+        v = rng.standard_normal((B, 64)).astype(np.float32)
+        q_idx[l] = S.f32_to_bf16_bits(np.repeat(v[:, None, :], 4, axis=1))
+        for b in range(B):
+            vb = S.bf16_bits_to_f32(q_idx[l, b, 0])
+            code = S.f32_to_e4m3_codes(vb / np.abs(vb).max() * 448.0)
+            t0 = int(row0[b]) + runs[(l, b)]
+            for c in range(16):
+                kl[t0 + 512 * c:t0 + 512 * (c + 1)] = code
+                sl[t0 + 512 * c:t0 + 512 * (c + 1)] = np.float16(
+                    1e-3 * np.exp2(4.0 * np.arange(512) / 512 + 0.013 * c))
+        keys[l], scales[l] = kl, sl.view(np.uint16)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    max_ctx = int(lens.max())
     ctx, r0d = d(lens.astype(np.int32)), d(row0)
     keys_d, scales_d = d(keys), d(scales.view(np.int16))
     q_idx_d, w_d = d(q_idx.view(np.int16)), d(w)
-    # the GPU's own block scores, from the standalone scoring call
-    _, bs = _score(qsa.make_config(budget), B, int(lens.max()), ctx, r0d, keys_d, scales_d, q_idx_d, w_d, n)
-    cb, m, cap = _list_geom(B, int(lens.max()), K)
-    for b in range(B):                              # the construction does what it is for
-        nb = (int(lens[b]) + 3) // 4
-        _, n_needy = list_route(bs[b, :nb], K, 0, nb, cb, m, cap)
-        assert n_needy >= 8, (b, n_needy)
-        j0 = run0[b] // 4
-        kk = order_keys(bs[b, j0:j0 + cb])
-        theta, complete, comps = chunk_list(kk, np.arange(j0, j0 + cb), m, cap)
-        assert len(comps) >= m and not complete     # a full list, not cut short
-    # the decode step, on one stream and with a side stream
+    cb, m, cap = _list_geom(B, max_ctx, K)
+    bs = []                                         # the GPU's own block scores, from the standalone call
+    for l in range(NL):
+        _, bl = _score(qsa.make_config(budget, sink, tail), B, max_ctx, ctx, r0d, keys_d[l], scales_d[l],
+                       q_idx_d[l], w_d[l], n)
+        bs.append(bl)
+        for b in range(B):                          # the construction does what it is for
+            nb = (int(lens[b]) + 3) // 4
+            tail_first = max(int(lens[b]) - tail, 0) // 4
+            _, n_needy = list_route(bl[b, :nb], K, sink, tail_first, cb, m, cap)
+            assert n_needy >= 8, (l, b, n_needy)
+            j0 = runs[(l, b)] // 4
+            theta, complete, comps = chunk_list(order_keys(bl[b, j0:j0 + cb]), np.arange(j0, j0 + cb), m, cap)
+            assert len(comps) >= m and not complete     # a full list, not cut short
     n_slots = n
-    pool = torch.randn((n_slots, 1024), dtype=torch.bfloat16, device=gpu).view(torch.int16)
-    pt = torch.from_numpy(np.stack([np.arange(int(lens.max())) + row0[b] for b in range(B)]).astype(np.int32))
-    pt = torch.where(pt < n, pt, torch.zeros_like(pt)).to(gpu)
-    q = torch.randn((B, 16, 256), dtype=torch.bfloat16, device=gpu).view(torch.int16)
-    cfg = qsa.make_config(budget)
-    bt = qsa.make_batch(B, int(lens.max()), ctx, r0d, pt, int(pt.shape[1]), n_slots, n)
-    ws, nws = _ws(cfg, B, int(lens.max()), 1, qsa.QSA_KV_DEVICE)
+    pool = torch.randn((NL, n_slots, 1024), dtype=torch.bfloat16, device=gpu).view(torch.int16)
+    pool_h = torch.empty((NL, n_slots, 1024), dtype=torch.int16, pin_memory=True)
+    pool_h.copy_(pool)
+    pt = np.stack([np.arange(max_ctx) + row0[b] for b in range(B)])
+    pt = d(np.where(pt < n, pt, 0).astype(np.int32))
+    q = torch.randn((NL, B, 16, 256), dtype=torch.bfloat16, device=gpu).view(torch.int16)
+    cfg = qsa.make_config(budget, sink, tail)
+    bt = qsa.make_batch(B, max_ctx, ctx, r0d, pt, int(pt.shape[1]), n_slots, n)
     got = []
-    for n_side in (0, 1):
+    for loc, n_side in ((qsa.QSA_KV_DEVICE, 0), (qsa.QSA_KV_DEVICE, 1), (qsa.QSA_KV_HOST_PINNED, 1)):
+        ws, nws = _ws(cfg, B, max_ctx, NL, loc)
         ws.fill_(0xAB)                              # no stale block scores to find
-        sel = torch.full((1, B, K), -7, dtype=torch.int32, device=gpu)
-        ns = torch.zeros((1, B), dtype=torch.int32, device=gpu)
-        out = torch.zeros((1, B, 16, 256), dtype=torch.float32, device=gpu)
-        lay = [qsa.make_layer(keys_d, scales_d, q_idx_d, w_d, q, pool, out[0], None, sel[0], ns[0])]
+        sel = torch.full((NL, B, K), -7, dtype=torch.int32, device=gpu)
+        ns = torch.zeros((NL, B), dtype=torch.int32, device=gpu)
+        out = torch.zeros((NL, B, 16, 256), dtype=torch.float32, device=gpu)
+        pl = pool if loc == qsa.QSA_KV_DEVICE else pool_h
+        lay = [qsa.make_layer(keys_d[l], scales_d[l], q_idx_d[l], w_d[l], q[l], pl[l], out[l], None, sel[l], ns[l])
+               for l in range(NL)]
         side = [torch.cuda.Stream() for _ in range(n_side)]
-        ev = qsa.StepEvents(1, n_side) if n_side else None
-        qsa.qsa_decode_step(cfg, bt, lay, qsa.QSA_KV_DEVICE, ws, nws, torch.cuda.current_stream(), side, events=ev)
+        ev = qsa.StepEvents(NL, n_side) if n_side else None
+        qsa.qsa_decode_step(cfg, bt, lay, loc, ws, nws, torch.cuda.current_stream(), side, events=ev)
         torch.cuda.synchronize()
         got.append((sel.cpu().numpy(), ns.cpu().numpy(), out.cpu().numpy()))
-    for a, b_ in zip(got[0], got[1]):
-        assert np.array_equal(a, b_)
+    for other in got[1:]:
+        for a, b_ in zip(got[0], other):
+            assert np.array_equal(a, b_)
     sel, ns, _ = got[0]
-    for b in range(B):
-        L = int(lens[b])
-        nb = (L + 3) // 4
-        fm = oracle.forced_mask(L, 4, 0, 0)
-        exact = oracle.select_blocks(bs[b, :nb], K, fm).blocks      # exact top-K of the GPU's block scores
-        assert ns[0, b] == len(exact)
-        assert np.array_equal(sel[0, b, :ns[0, b]], exact), b
-        k, s = keys[row0[b]:row0[b] + L], scales[row0[b]:row0[b] + L]
-        ref_bs = oracle.block_scores(oracle.token_scores(k, s, q_idx[b], w[b]))
-        osel = oracle.select_blocks(ref_bs, K, fm)
-        check_selection(sel[0, b, :ns[0, b]], Unit(L, None, None, None, None, None, None, None, ref_bs, fm,
-                                                   osel.blocks, osel.kth_score, None))
+    for l in range(NL):
+        for b in range(B):
+            L = int(lens[b])
+            nb = (L + 3) // 4
+            fm = oracle.forced_mask(L, 4, sink, tail)
+            exact = oracle.select_blocks(bs[l][b, :nb], K, fm).blocks   # exact top-K of the GPU's block scores
+            assert ns[l, b] == len(exact)
+            assert np.array_equal(sel[l, b, :ns[l, b]], exact), (l, b)
+            k, s = keys[l, row0[b]:row0[b] + L], scales[l, row0[b]:row0[b] + L]
+            ref_bs = oracle.block_scores(oracle.token_scores(k, s, q_idx[l, b], w[l, b]))
+            osel = oracle.select_blocks(ref_bs, K, fm)
+            check_selection(sel[l, b, :ns[l, b]], Unit(L, None, None, None, None, None, None, None, ref_bs, fm,
+                                                       osel.blocks, osel.kth_score, None))
 
 
 def test_decode_step_offload_reuses_one_event_set(gpu):
