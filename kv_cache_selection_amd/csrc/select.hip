@@ -22,7 +22,10 @@
 //    still hide a block of the answer: a chunk whose list is incomplete,
 //    whose every entry is at least T_U, and whose threshold lies above T_U.
 //    Their missing blocks at or above T_U join the pool, and the r-th largest
-//    of the pool is the exact threshold.
+//    of the pool is the exact threshold. A re-read chunk's block scores come
+//    from memory when they were stored (the standalone call; in the decode
+//    step, a chunk whose list was cut short by a crowded bin), and are
+//    otherwise computed again from the index with the scan's own arithmetic.
 //    Why this is exact: a block x of the answer missing from the pool sits in
 //    a chunk whose list entries all beat it (their bins are higher), so they
 //    are in the answer too, and so among the pool's best r (the pool is a
