@@ -307,10 +307,27 @@ def step_percentiles(ms):
             "max": round(float(a.max()), 4), "n": int(a.size)}
 
 
+def timed_region(run, n, stream):
+    """Runs `run()` n times back to back between two events, with nothing
+    recorded and no synchronisation inside the region: the mean per call in
+    ms."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def timed_steps(run, n, stream):
-    """Runs `run()` n times back to back with an event between consecutive
-    calls (no synchronisation inside the region): the mean and the per-call
-    times in ms."""
+    """The per-call times of n calls with an event between consecutive calls,
+    then the mean of n more calls timed as one region (timed_region). An
+    event recorded after a call delays the next one by 1.5-3 us, so the
+    first run gives the spread of the calls and the second their mean; the
+    first also carries the first calls after the warm-up, which run slower."""
     import torch
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     torch.cuda.synchronize()
@@ -320,7 +337,8 @@ def timed_steps(run, n, stream):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
-    return evs[0].elapsed_time(evs[n]) / n, per
+    mean = timed_region(run, n, stream)
+    return mean, per
 
 
 def copy_calibration():
