@@ -14,9 +14,14 @@ Prints one JSON line with the driver's fields plus:
                 duration, timed with HIP events taken by the launch itself.
                 Without a hot cache one launch scans all the layers (up to
                 16), so a launch's bytes are the layers' index bytes together;
-  one_stream_score  the same for the per-layer scoring launch of the
-                one-stream step (each launch has the GPU alone);
-  one_stream    the step time with every kernel in order on one stream;
+  one_stream_score  the same for the scoring launch of a one-layer call
+                (each launch has the GPU alone);
+  one_stream    the step time with no side stream (the same grouped launches
+                on one stream for HBM pools; groups of scan, selection,
+                gather and attention for pinned-host pools; layer by layer
+                with a hot cache);
+  per_layer_calls  one qsa_decode_step call per layer, as a model with
+                dependent layers runs it;
   step_hbm      the whole step's algorithmic bytes (index scan + gathered
                 rows) over the step time, against the same HBM peak;
   cpu_baseline  the CPU oracle, single-threaded, on a sample of (layer,
@@ -153,8 +158,8 @@ def stats_summary(path, workload, op="step", bench_args=""):
              "#   rocprofv3 --kernel-trace --stats -f csv -d OUT -o run -- python3 bench.py %s" % bench_args,
              "# summary: python3 bench.py --stats-summary OUT/run_kernel_stats.csv %s" % bench_args]
     if op == "step":
-        lines += ["# averages over every launch of the run: warm-up and the timed regions, overlapped steps (one",
-                  "# scoring launch over all layers, <..., 16>) and one-stream steps (one launch per layer, <..., 1>)"]
+        lines += ["# averages over every launch of the run: warm-up and the timed regions, whole steps (one",
+                  "# launch per kernel over a group of layers, <..., 16>) and one-layer calls (<..., 1>)"]
     lines += ["",
              "%8s %12s %10s %10s %10s %7s  %s" % ("calls", "total ms", "avg us", "min us", "max us", "%", "kernel")]
     with open(path, newline="") as f:
@@ -971,8 +976,8 @@ def main():
                 "note": "each step timed alone after reading a separate buffer of flush_bytes (twice the "
                         "Infinity Cache); median_over_warm compares with the back-to-back steps of step_ms"}
 
-    # Timed region 2: the same steps with every kernel in order on one stream (each layer's
-    # score -> select -> attention -> merge before the next layer starts).
+    # Timed region 2: the same steps with no side stream (everything in order
+    # on the compute stream).
     ms_serial = None
     if side:
         e0.record(stream)
@@ -1004,7 +1009,6 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms_per_layer_calls = e0.elapsed_time(e1) / args.steps
-        del ws1
 
     # Timed region 3: the headline schedule again, with HIP events around
     # the scoring launches. A launch that scans a group of layers takes the
@@ -1028,12 +1032,18 @@ def main():
     score_ms = float(np.mean(durs)) / n_launch             # per launch
     layers_per_launch = NL / n_launch
 
-    # Timed region 4: one-stream steps with events around every per-layer
-    # scoring launch (each scan alone, as a kernel-trace profile sees it).
+    # Timed region 4: every one-layer scoring launch timed alone, as a
+    # kernel-trace profile sees it: the one-layer calls of region 2b (the
+    # one-stream step with a hot cache, which runs layer by layer).
     durs1 = []
     timed1 = [layers(v, evs) for v in range(NV)]
     for _ in range(args.steps):
-        step(timed1, streams=False)
+        if hot:
+            step(timed1, streams=False)
+        else:
+            for ly in timed1[n_done[0] % NV]:
+                qsa.qsa_decode_step(cfg, bt, [ly], loc, ws1, nws1, stream, None)
+            n_done[0] += 1
         torch.cuda.synchronize()
         durs1.extend(hev.elapsed_ms(a, b) for (a, b) in evs)
     score1_ms = float(np.mean(durs1))
@@ -1084,7 +1094,7 @@ def main():
                      "bytes_per_launch": idx_bytes_launch,
                      "layers_per_launch": round(layers_per_launch, 3), "launches_per_step": n_launch,
                      "avg_launch_us": round(score_ms * 1e3, 2)},
-        # the per-layer scoring launch of the one-stream step, each launch alone
+        # the scoring launch of a one-layer call, each launch alone
         "one_stream_score": {"achieved": round(achieved1, 1), "unit": "GB/s",
                              "frac": round(achieved1 / HBM_PEAK_GBS, 4), "bytes_per_launch": idx_bytes_layer,
                              "avg_launch_us": round(score1_ms * 1e3, 2),

@@ -247,20 +247,24 @@ typedef struct {
  * area in the workspace, one buffer per layer (B x budget_tokens x 2048 B).
  * Streams: `side` holds n_side extra streams (all distinct from `compute`);
  * with n_side = 0 (side may then be NULL) every kernel runs in order on
- * `compute`. With side streams the layers overlap (this treats the layers
- * as independent, which they are within one call):
+ * `compute`. The layers of a call are independent, so kernels cover several
+ * layers at once:
  *   - HBM pools: the layers go in groups of up to 16; one launch scans the
  *     whole group's index, then one launch each of the selection and
- *     attention kernels covers the whole group, all on `compute`. With more
- *     than 16 layers, each group's selection and attention run on side[0]
- *     and overlap the next group's scan. Further side streams are not used;
+ *     attention kernels covers the whole group, all on `compute`, with or
+ *     without side streams. With more than 16 layers and a side stream, each
+ *     group's selection and attention run on side[0] and overlap the next
+ *     group's scan. Further side streams are not used;
  *   - host pools with a hot cache: layer l's whole chain (score, select,
  *     cache update, miss fetch, attend, merge) runs on stream
  *     l % (n_side + 1) of {compute, side[0], side[1], ...}, with at most two
- *     index scans at a time;
- *   - host pools without a hot cache: a pipeline over the layers (digest,
- *     efficiency section: the copy of a layer's rows overlaps the next
- *     layer's index scoring). `compute` scores and selects the layers;
+ *     index scans at a time (with n_side = 0, layer after layer);
+ *   - host pools without a hot cache and n_side = 0: groups of up to 16
+ *     layers, each scanned, selected, gathered and attended with one launch
+ *     per kernel;
+ *   - host pools without a hot cache, with a side stream: a pipeline over
+ *     the layers (digest, efficiency section: the copy of a layer's rows
+ *     overlaps the next layer's index scoring). `compute` scores and selects the layers;
  *     side[0] gathers the selected rows over PCIe into their staging
  *     buffers as soon as they are selected, back to back;
  *     `compute` attends the layers once the last rows have arrived. The

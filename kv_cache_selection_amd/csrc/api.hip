@@ -719,8 +719,9 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         flags_cleared = true;
     }
 
-    if (!two_streams) {
-        // One stream: every layer's kernels in order.
+    if (!two_streams && hot) {
+        // Hot cache, one stream: every layer's kernels in order (its cache
+        // update and miss fetch sit between its selection and attention).
         for (int l = 0; l < n_layers && e == hipSuccess; l++) {
             e = score(l, sc);
             if (e == hipSuccess)
@@ -777,10 +778,11 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         // the chains during the scans instead only takes CUs and bandwidth
         // from the scans, and every dependency between streams adds 6-13 us
         // before the waiting kernel starts. With one group everything runs
-        // on the compute stream. With several, the chains run on side 0, so a
-        // group's chain overlaps the next group's scan. The first layer's
-        // score events of a group time that group's scan.
-        const hipStream_t cs = n_layers > kMaxChainLayers ? (hipStream_t)side[0] : sc;
+        // on the compute stream, with or without side streams. With several
+        // and a side stream, the chains run on side 0, so a group's chain
+        // overlaps the next group's scan. The first layer's score events of a
+        // group time that group's scan.
+        const hipStream_t cs = two_streams && n_layers > kMaxChainLayers ? (hipStream_t)side[0] : sc;
         const int n_used = cs != sc ? 1 : 0;
         if (e == hipSuccess && n_used) {
             e = hipEventRecord(ev[0], sc);
@@ -857,7 +859,9 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         return hip_status(e);
     }
 
-    // Pools in pinned host memory, a side stream given: a pipeline over
+    // Pools in pinned host memory without a hot cache. With no side stream,
+    // groups of up to 16 layers one after another (below). With a side
+    // stream given: a pipeline over
     // groups of layers of sizes 1, 3, 9, ... (the last takes the rest). The
     // compute stream scores and selects group after group (one launch each
     // per group); the side stream gathers each group's selected rows over
@@ -879,7 +883,7 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
     // gathers (a record after a kernel delays the stream's next kernel by
     // 3-5 us), only after the last one, for which the compute stream waits on
     // an event: a signal wait held that long sometimes ended 180 us late.
-    const hipStream_t sg = (hipStream_t)side[0];
+    const hipStream_t sg = two_streams ? (hipStream_t)side[0] : sc;
     auto staged_tables = [&](int l0, int nl, ScoreLayers &CL, SelectLayers &SL, GatherLayers &GL, AttnLayers &AL) {
         CL.flags = l0 == 0 ? nullptr : flags;      // the first scan clears the word instead
         CL.drop_listed_bs = 1;
@@ -914,6 +918,33 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             AL.out[i] = Ly.out;
         }
     };
+    if (!two_streams) {
+        // One stream: groups of up to kMaxChainLayers layers, each scanned,
+        // selected, gathered (on the whole grid) and attended with one launch
+        // per kernel.
+        for (int l0 = 0; l0 < n_layers && e == hipSuccess; l0 += kMaxChainLayers) {
+            const int nl = n_layers - l0 < kMaxChainLayers ? n_layers - l0 : kMaxChainLayers;
+            ScoreLayers CL = {};
+            SelectLayers SL = {};
+            GatherLayers GL = {};
+            AttnLayers AL = {};
+            staged_tables(l0, nl, CL, SL, GL, AL);
+            e = launch_index_score_layers(CL, nl, batch->ctx_len, batch->idx_row0, batch->n_idx_rows, B,
+                                          batch->max_ctx, bs_stride, w.g, K, cfg->sink_blocks, cfg->tail_tokens, sc,
+                                          (hipEvent_t)layers[l0].score_events[0],
+                                          (hipEvent_t)layers[l0].score_events[1], l0 == 0 ? flags : nullptr);
+            if (e == hipSuccess)
+                e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
+                                         cfg->sink_blocks, cfg->tail_tokens, sc);
+            if (e == hipSuccess)
+                e = launch_gather_layers(GL, nl, batch->ctx_len, B, batch->max_ctx, batch->pt_stride,
+                                         batch->n_slots, K, cfg->budget_tokens, sc, 0);
+            if (e == hipSuccess)
+                e = launch_attention_layers(false, AL, nl, 0, 0, B, 0, cfg->budget_tokens, cfg->sm_scale,
+                                            lw[l0].aw.tps, sc);
+        }
+        return hip_status(e);
+    }
     int group_len[QSA_MAX_LAYERS];
     int n_groups = 0;
     for (int l0 = 0, want = 1; l0 < n_layers; want *= 3) {
