@@ -305,9 +305,11 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
  * The signal is 8 bytes of signal memory (hipExtMallocWithFlags with
  * hipMallocSignalMemory), set to 0 here with a stream write on the null
  * stream, which this call then synchronises; each pinned-host pipeline step
- * writes it with values that only grow. Not itself thread-safe: one set per
- * host thread that issues overlapped steps. QSA_ERR_HIP if HIP cannot create
- * the events or the signal (nothing is then kept). */
+ * writes it with values that only grow. Where signal memory cannot be
+ * allocated the set keeps none and the pipeline hands over with its events.
+ * Not itself thread-safe: one set per host thread that issues overlapped
+ * steps. QSA_ERR_HIP if HIP cannot create the events or set the signal
+ * (nothing is then kept). */
 qsa_status_t qsa_step_events_create(int32_t max_layers, int32_t max_side, qsa_step_events_t **events);
 void qsa_step_events_destroy(qsa_step_events_t *events);
 

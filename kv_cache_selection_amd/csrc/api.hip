@@ -289,13 +289,13 @@ qsa_status_t qsa_step_events_create(int32_t max_layers, int32_t max_side, qsa_st
         e->ev.push_back(h);
     }
     // A fresh signal holds 1, so it is set to 0 before its first use; the
-    // values written later count up from there.
+    // values written later count up from there. Where signal memory is not
+    // available the pipeline hands over with events instead.
     if (hipExtMallocWithFlags((void **)&e->signal, sizeof(uint64_t), hipMallocSignalMemory) != hipSuccess) {
+        (void)hipGetLastError();
         e->signal = nullptr;
-        qsa_step_events_destroy(e);
-        return QSA_ERR_HIP;
-    }
-    if (hipStreamWriteValue64(nullptr, e->signal, 0, 0) != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess) {
+    } else if (hipStreamWriteValue64(nullptr, e->signal, 0, 0) != hipSuccess ||
+               hipStreamSynchronize(nullptr) != hipSuccess) {
         qsa_step_events_destroy(e);
         return QSA_ERR_HIP;
     }
@@ -971,13 +971,17 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
             e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
                                      cfg->sink_blocks, cfg->tail_tokens, sc);
         // the side stream's wait is enqueued only once its value's write is
-        if (e == hipSuccess) {
+        if (e == hipSuccess && events->signal) {
             const uint64_t value = events->epoch + 1;
             e = hipStreamWriteValue64(sc, events->signal, value, 0);
             if (e == hipSuccess) {
                 events->epoch = value;
                 e = hipStreamWaitValue64(sg, events->signal, value, hipStreamWaitValueGte, ~0ull);
             }
+        } else if (e == hipSuccess) {
+            e = hipEventRecord(ev[1 + NS + l0], sc);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(sg, ev[1 + NS + l0], 0);
         }
         if (e == hipSuccess)
             e = launch_gather_layers(GL, nl, batch->ctx_len, B, batch->max_ctx, batch->pt_stride, batch->n_slots, K,
