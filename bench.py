@@ -203,7 +203,7 @@ def read_attn_traffic(workload):
 
 
 def h2d_copy_gbs(n_bytes=1 << 28, reps=10):
-    """The PCIe reference measured on the same box: a plain copy of a pinned
+    """The PCIe reference measured on the same machine: a plain copy of a pinned
     host buffer to the GPU (the DMA engines), GB/s over `reps` copies."""
     import torch
     src = torch.empty(n_bytes, dtype=torch.uint8, pin_memory=True)
@@ -445,7 +445,7 @@ def cpu_baseline(wl, hi, seconds):
                         "C oracle in fp64: %.3f s per unit, and a layer-step is %d units; input generation excluded"
                         % (len(units), wl.name, units[0][0], units[-1][0], sum(times), mean, wl.batch)}
 
-    # All host cores (at most 16, one GPU's share of the box): one thread per
+    # All host cores (at most 16, one GPU's share of the host): one thread per
     # core, each running the oracle on its own (layer, sequence) unit over and
     # over for about seconds / 2. The C oracle and the generator release the
     # GIL, so the threads run in parallel; inputs are generated before timing.

@@ -1,7 +1,7 @@
 // bench_stream.hip -- the streaming-read reference that bench.py measures
 // beside the decode step: how fast this GPU reads a large device buffer
 // front to back, so that the step's and the index scan's achieved GB/s can
-// be given as fractions of a ceiling measured on the same box, next to the
+// be given as fractions of a ceiling measured on the same machine, next to the
 // published HBM peak. Not part of libqsa.
 //
 // Workgroup w (256 threads) reads bytes [w * chunk, (w + 1) * chunk) of buf,
