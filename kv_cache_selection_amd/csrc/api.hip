@@ -970,7 +970,8 @@ qsa_status_t qsa_decode_step(const qsa_config_t *cfg, const qsa_batch_t *batch, 
         if (e == hipSuccess)
             e = launch_select_layers(SL, nl, bs_stride, batch->ctx_len, B, batch->max_ctx, w.g, K,
                                      cfg->sink_blocks, cfg->tail_tokens, sc);
-        // the side stream's wait is enqueued only once its value's write is
+        // the side stream's wait is enqueued only once the write of its value
+        // is, so it can never wait for a value that no write will bring
         if (e == hipSuccess && events->signal) {
             const uint64_t value = events->epoch + 1;
             e = hipStreamWriteValue64(sc, events->signal, value, 0);
