@@ -382,14 +382,13 @@ void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx, 
     }
 }
 
-constexpr int kMergeUnroll = 16;
-
 // One workgroup per (sequence, head) and layer (grid (B * kHq, layers));
 // thread d owns output dim d. Every thread reads the (uniform) split LSEs
-// itself and its column of partial outputs in the same batch, so the whole
-// merge is one round of loads: for each batch of splits, the running max is
-// raised and the sums rescaled.
-template <int N>
+// itself and its column of partial outputs in batches of kBatch splits (16
+// or 32, the launch takes the smaller one that covers n_split), so the whole
+// merge is one round of loads: for each batch, the running max is raised
+// and the sums rescaled.
+template <int N, int kBatch>
 __global__ __launch_bounds__(kDh) void merge_kernel(const AttnLayersT<N> Ls, int n_split)
 {
     const float *__restrict__ part_o = Ls.part_o[blockIdx.y];
@@ -400,17 +399,25 @@ __global__ __launch_bounds__(kDh) void merge_kernel(const AttnLayersT<N> Ls, int
     const float *lse = part_lse + (int64_t)bh * n_split;
     const float *col = part_o + (int64_t)bh * n_split * kDh + tid;
     float M = -INFINITY, acc = 0.0f, den = 0.0f;
-    for (int s0 = 0; s0 < n_split; s0 += kMergeUnroll) {
-        float ls[kMergeUnroll], x[kMergeUnroll];
+    for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+        float ls[kBatch], x[kBatch];
+        // unconditional loads of clamped splits (no branches between them,
+        // so all are in flight together), masked afterwards
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; u++) {
+        for (int u = 0; u < kBatch; u++) {
+            const int sc = min(s0 + u, n_split - 1);
+            ls[u] = lse[sc];
+            x[u] = col[(int64_t)sc * kDh];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
             const bool in = s0 + u < n_split;
-            ls[u] = in ? lse[s0 + u] : -INFINITY;
-            x[u] = in ? col[(int64_t)(s0 + u) * kDh] : 0.0f;
+            ls[u] = in ? ls[u] : -INFINITY;
+            x[u] = in ? x[u] : 0.0f;
         }
         float mb = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; u++)
+        for (int u = 0; u < kBatch; u++)
             mb = fmaxf(mb, ls[u]);
         if (mb == -INFINITY)
             continue;                       // uniform: every split of the batch is empty
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kDh) void merge_kernel(const AttnLayersT<N> Ls, int
         acc *= r;
         den *= r;
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; u++) {
+        for (int u = 0; u < kBatch; u++) {
             const float ws = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
             den += ws;
             // empty splits hold stale data: select, not multiply
@@ -457,8 +464,11 @@ static hipError_t launch_attention_n(bool paged, const AttnLayersT<N> &L, int n_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((merge_kernel<N>), dim3((unsigned)(batch * kHq), (unsigned)n_layers), dim3(kDh), 0, s, L,
-                       n_split);
+    const dim3 mgrid((unsigned)(batch * kHq), (unsigned)n_layers);
+    if (n_split <= 16)
+        hipLaunchKernelGGL((merge_kernel<N, 16>), mgrid, dim3(kDh), 0, s, L, n_split);
+    else
+        hipLaunchKernelGGL((merge_kernel<N, 32>), mgrid, dim3(kDh), 0, s, L, n_split);
     return hipGetLastError();
 }
 
