@@ -378,6 +378,26 @@ def test_sparse_decode_parity_and_closed_forms(gpu):
     assert np.abs(got[ntok > 0] + 0.75).max() <= 4 * np.spacing(np.float32(0.75))
 
 
+@pytest.mark.parametrize("budget", [640, 1500, 2600])
+def test_sparse_decode_split_counts(gpu, budget):
+    """Split counts that are not a multiple of the merge's batch of splits:
+    10, 24 and 41 splits of 64 tokens (or 5, 12 and 21 of 128). The merge
+    loads past the last split are clamped and masked, and 41 splits take a
+    second batch that continues the online rescale. Full, ragged and half
+    sequences against the oracle."""
+    rng = np.random.default_rng(budget)
+    cfg = qsa.make_config(budget)
+    B = 3
+    ntok = np.array([budget, budget - 3, budget // 2 + 1], np.int32)
+    kv = S.f32_to_bf16_bits(rng.standard_normal((B, budget, G.row_elems)).astype(np.float32))
+    q = S.f32_to_bf16_bits(rng.standard_normal((B, 16, 256)).astype(np.float32))
+    got = _decode(cfg, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(kv.view(np.int16)).cuda(),
+                  torch.from_numpy(ntok).cuda())
+    for b in range(B):
+        ref = oracle.attention(np.arange(ntok[b]), None, kv[b], q[b], 2, G.sm_scale)
+        check_attention(got[b], ref, "budget %d, sequence %d" % (budget, b))
+
+
 # ------------------------------------------------------------- whole step
 
 def _step(di, loc=None, n_side=2):
