@@ -385,9 +385,9 @@ void attn_split_kernel(const AttnLayersT<N> Ls, int64_t pt_stride, int max_ctx, 
 // One workgroup per (sequence, head) and layer (grid (B * kHq, layers));
 // thread d owns output dim d. Every thread reads the (uniform) split LSEs
 // itself and its column of partial outputs in batches of kBatch splits (16
-// or 32, the launch takes the smaller one that covers n_split), so the whole
-// merge is one round of loads: for each batch, the running max is raised
-// and the sums rescaled.
+// when the launch has at most 16 splits, else 32), so that up to 32 splits
+// take one round of loads: for each batch, the running max is raised and
+// the sums rescaled.
 template <int N, int kBatch>
 __global__ __launch_bounds__(kDh) void merge_kernel(const AttnLayersT<N> Ls, int n_split)
 {
